@@ -1,0 +1,266 @@
+/*
+ * CPU oracle for one routed-expert FP4 MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The GPU product
+ * shares no code with it: no kernel, header, table or helper.
+ *
+ * It is the plain definition, slow and obvious: double accumulation, one
+ * element at a time, a library sort for the router.  Sources (DeepSeek-V4.1-
+ * Flash pages):
+ *   - 10100.com page, section on the MoE expert-capacity bottleneck: 384
+ *     routed experts per layer, 6 active per token, each with w1/w2/w3 held as
+ *     FP4 E2M1 codes (two per byte) plus UE8M0 scales; shapes
+ *     w1/w3 [2304, 2560 B] + scale [2304, 160], w2 [5120, 1152 B] + scale
+ *     [5120, 72], i.e. one scale byte per 32 consecutive inputs of a row.
+ *   - ai-shiz.ru page, section "what the model is": hidden 5120, 384 routed
+ *     experts, the router takes 6 per token; one expert is three 5120 x 2304
+ *     matrices.
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - FFN is SwiGLU: y_e = W2 (silu(W1 x) * (W3 x)), silu(z) = z / (1 + e^-z);
+ *   - the hidden activation h is rounded once to bf16 (nearest, ties to even)
+ *     after silu(G)*U; G and U are not rounded;
+ *   - low nibble of a byte = even element; scale group = 32 consecutive inputs;
+ *   - E2M1 code c: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0;
+ *     exponent field 0 is subnormal (0.5 * mantissa);  UE8M0 byte e = 2^(e-127);
+ *   - routing: experts ranked by logit descending, ties to the lower index,
+ *     -0 equal to +0, NaN below every number; gates are a softmax over the k
+ *     selected logits; the output is the gate-weighted sum over the k experts
+ *     taken in rank order, applied after w2.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ORACLE_MUTANT plants one deliberate mistake (tests only: the mutation tests
+ * build a copy with -DORACLE_MUTANT=n and check that some pin catches it).
+ * The default, 0, is the oracle. */
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+#define MUT(n) (ORACLE_MUTANT == (n))
+
+/* ------------------------------------------------------------------ formats */
+
+/* E2M1 code -> value, from the bit fields of the format. */
+double oracle_e2m1(int code) {
+    int s = (code >> 3) & 1, E = (code >> 1) & 3, m = code & 1;
+    double mag = (E == 0) ? (MUT(11) ? 1.0 : 0.5) * m : ldexp(1.0 + 0.5 * m, E - 1);
+    return (s && !MUT(12)) ? -mag : mag;
+}
+
+/* UE8M0 byte -> scale 2^(e-127); 255 is NaN in the OCP MX format. */
+double oracle_ue8m0(int e) {
+    if (e == 255) return NAN;
+    return ldexp(1.0, e - (MUT(3) ? 126 : 127));
+}
+
+/* bf16 bit pattern -> value */
+double oracle_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round a double straight to bf16 (8 significant bits, round to nearest, ties
+ * to even; overflow to inf, NaN kept), return the bit pattern.  One rounding
+ * step: never through float, which would round twice. */
+uint16_t oracle_double_to_bf16(double v) {
+    float f;
+    uint32_t u;
+    if (isnan(v)) return 0x7FC0;
+    if (v == 0.0 || isinf(v)) {
+        f = (float)v;
+    } else {
+        int ex;
+        frexp(v, &ex);                    /* |v| = m * 2^ex, m in [0.5, 1) */
+        int qexp = ex - 8;                /* 8 significant bits */
+        if (qexp < -133) qexp = -133;     /* bf16 subnormal quantum 2^-133 */
+        double r = nearbyint(ldexp(v, -qexp)) ;  /* default mode: ties to even */
+        double q = ldexp(r, qexp);
+        if (fabs(q) >= ldexp(1.0, 128)) q = copysign(INFINITY, v);
+        f = (float)q;                     /* exact: q is a bf16 value */
+    }
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------ weights */
+
+/* Decoded weight element: row r, input column c of a [rows][cols/2] nibble
+ * tensor with a [rows][cols/32] scale tensor. */
+static inline double wval(const uint8_t *w, const uint8_t *s, int cols, int r, int c) {
+    uint8_t byte = w[(size_t)r * (cols / 2) + (c >> 1)];
+    int code = ((c & 1) != MUT(1)) ? (byte >> 4) : (byte & 0xF);
+    return oracle_e2m1(code) * oracle_ue8m0(s[(size_t)r * (cols / 32) + (MUT(4) ? 0 : (c >> 5))]);
+}
+
+/* ------------------------------------------------------------------ router */
+
+typedef struct { float v; int e; } okey;
+
+/* Total order of the router: larger logit first, then lower expert index.
+ * -0 and +0 compare equal; NaN ranks below everything. */
+static int key_cmp(const void *a, const void *b) {
+    const okey *x = (const okey *)a, *y = (const okey *)b;
+    int xn = isnan(x->v), yn = isnan(y->v);
+    if (xn != yn) return xn ? 1 : -1;
+    if (!xn) {
+        if (x->v > y->v) return -1;
+        if (x->v < y->v) return 1;
+    }
+    if (MUT(5)) return (x->e > y->e) ? -1 : (x->e < y->e);
+    return (x->e < y->e) ? -1 : (x->e > y->e);
+}
+
+/* Per token: the k best experts by the total order, and gates = softmax over
+ * those k logits (computed in double, stored as float). */
+void oracle_route(int T, int E, int k, const float *logits, int32_t *idx, float *gates) {
+    okey *keys = (okey *)malloc(sizeof(okey) * (size_t)E);
+    double *ex = (double *)malloc(sizeof(double) * (size_t)k);
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) { keys[e].v = logits[(size_t)t * E + e]; keys[e].e = e; }
+        qsort(keys, (size_t)E, sizeof(okey), key_cmp);
+        double l0 = keys[0].v, den = 0.0;
+        for (int j = 0; j < k; ++j) {
+            idx[(size_t)t * k + j] = keys[j].e;
+            ex[j] = exp((double)keys[j].v - l0);
+            den += ex[j];
+        }
+        if (MUT(6))
+            for (int j = k; j < E; ++j) den += exp((double)keys[j].v - l0);
+        for (int j = 0; j < k; ++j) gates[(size_t)t * k + j] = (float)(ex[j] / den);
+    }
+    free(ex);
+    free(keys);
+}
+
+/* Token permutation grouped by expert.  Pair p = t*k + j.  counts[e] = pairs
+ * routed to e; offsets = exclusive prefix sum (E+1 entries); sorted_pairs lists
+ * pair ids expert by expert, ascending p inside an expert; pair_slot is the
+ * inverse (slot of pair p in sorted_pairs). */
+void oracle_permute(int T, int E, int k, const int32_t *idx, int32_t *counts, int32_t *offsets,
+                    int32_t *sorted_pairs, int32_t *pair_slot) {
+    int P = T * k;
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int p = 0; p < P; ++p) counts[idx[p]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int s = 0;
+    for (int e = 0; e < E; ++e)
+        for (int p = 0; p < P; ++p)
+            if (idx[p] == e) { sorted_pairs[s] = p; pair_slot[p] = s; ++s; }
+}
+
+/* ------------------------------------------------------------------ expert FFN */
+
+typedef struct {
+    /* per-expert base pointers of the six tensors (NULL = not provided) */
+    const uint8_t **w1, **s1, **w3, **s3, **w2, **s2;
+} oracle_weights;
+
+/* One token through one expert.
+ *   G_n = sum_c x_c W1[n][c],  U_n = sum_c x_c W3[n][c]           (double)
+ *   h_n = bf16(silu(G_n) * U_n)                                    (one rounding)
+ *   Y_m = sum_n h_n W2[m][n]                                       (double)
+ * hpre (optional) receives silu(G)*U before rounding. */
+static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const uint8_t *s1,
+                       const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
+                       uint16_t *h, double *hpre, double *Y) {
+    double *hv = (double *)malloc(sizeof(double) * (size_t)I);
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < I; ++n) {
+        double G = 0.0, U = 0.0;
+        for (int c = 0; c < H - MUT(10); ++c) {
+            G += x[c] * wval(w1, s1, H, n, c);
+            U += x[c] * wval(w3, s3, H, n, c);
+        }
+        double a = MUT(2) ? U / (1.0 + exp(-U)) * G : G / (1.0 + exp(-G)) * U;
+        if (hpre) hpre[n] = a;
+        h[n] = oracle_double_to_bf16(a);
+        hv[n] = MUT(9) ? a : oracle_bf16_to_double(h[n]);
+    }
+    #pragma omp parallel for schedule(static)
+    for (int m = 0; m < H; ++m) {
+        double acc = 0.0;
+        for (int n = 0; n < I; ++n)
+            acc += hv[n] * (MUT(8) ? wval(w2, s2, H, n, m) : wval(w2, s2, I, m, n));
+        Y[m] = acc;
+    }
+    free(hv);
+}
+
+/* Forward of the layer for the tokens listed in `tok` (n_tok of them; NULL =
+ * all T in order).  Routing and permutation are computed for all T tokens.
+ *   x      [T][H] bf16 bits          logits [T][E] float
+ *   y      [n_tok][H] float           y[i] = sum_j g[t][j] * Y_(t,j), j ascending
+ *   h_out  optional [T*k][I] bf16 (pair order; only pairs of listed tokens set)
+ *   hpre   optional [T*k][I] double (same, before rounding)
+ *   idx, gates optional [T*k] outputs of the router
+ * Returns 0, or -1 if a selected expert's weights were not provided. */
+int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
+                   const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
+                   uint16_t *h_out, double *hpre, int32_t *idx_out, float *gates_out) {
+    int P = T * k;
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
+    float *g = (float *)malloc(sizeof(float) * (size_t)P);
+    oracle_route(T, E, k, logits, idx, g);
+    if (idx_out) memcpy(idx_out, idx, sizeof(int32_t) * (size_t)P);
+    if (gates_out) memcpy(gates_out, g, sizeof(float) * (size_t)P);
+    if (tok == NULL) n_tok = T;
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *Y = (double *)malloc(sizeof(double) * (size_t)H);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+    double *hp = (double *)malloc(sizeof(double) * (size_t)I);
+    int rc = 0;
+    for (int i = 0; i < n_tok && rc == 0; ++i) {
+        int t = tok ? tok[i] : i;
+        for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(x[(size_t)t * H + c]);
+        for (int m = 0; m < H; ++m) acc[m] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = idx[(size_t)t * k + j];
+            if (!W->w1[e] || !W->s1[e] || !W->w3[e] || !W->s3[e] || !W->w2[e] || !W->s2[e]) {
+                rc = -1;
+                break;
+            }
+            expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], h,
+                       hp, Y);
+            size_t p = (size_t)t * k + j;
+            if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
+            if (hpre) memcpy(hpre + p * I, hp, sizeof(double) * (size_t)I);
+            double gj = MUT(7) ? 1.0 : (double)g[p];
+            for (int m = 0; m < H; ++m) acc[m] += gj * Y[m];
+        }
+        for (int m = 0; m < H; ++m) y[(size_t)i * H + m] = (float)acc[m];
+    }
+    free(hp); free(h); free(acc); free(Y); free(xd); free(g); free(idx);
+    return rc;
+}
+
+/* Pre-normalisation of the layer stack: u = bf16(x / sqrt(mean(x^2) + eps)). */
+void oracle_prenorm(int T, int H, const float *x, double eps, uint16_t *u) {
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int m = 0; m < H; ++m) ss += (double)x[(size_t)t * H + m] * x[(size_t)t * H + m];
+        double r = sqrt(ss / H + eps);
+        for (int m = 0; m < H; ++m) u[(size_t)t * H + m] = oracle_double_to_bf16(x[(size_t)t * H + m] / r);
+    }
+}
+
+/* One layer of the residual stack: x <- x + moe(prenorm(x)), float storage.
+ * x [T][H] float is updated in place. */
+int oracle_stack_layer(int T, int H, int I, int E, int k, float *x, const float *logits,
+                       const oracle_weights *W) {
+    uint16_t *u = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
+    float *y = (float *)malloc(sizeof(float) * (size_t)T * H);
+    oracle_prenorm(T, H, x, 1e-6, u);
+    int rc = oracle_forward(T, H, I, E, k, u, logits, W, T, NULL, y, NULL, NULL, NULL, NULL);
+    if (rc == 0)
+        for (size_t i = 0; i < (size_t)T * H; ++i) x[i] = (float)((double)x[i] + (double)y[i]);
+    free(y);
+    free(u);
+    return rc;
+}

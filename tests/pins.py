@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle: checks against facts fixed outside the oracle itself.
+
+Each pin takes an `oracle.Oracle` and raises AssertionError when the oracle
+disagrees with what the pages, the format specification, a library routine or
+hand-computed closed forms fix.  tests/test_oracle.py runs them all on the real
+oracle; tests/test_oracle_mutants.py runs them on copies of the oracle with one
+planted mistake each and requires that every mistake is caught by some pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+
+import numpy as np
+
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            out[key] = [float(v) for v in vals]
+    return out
+
+
+def bf16_bits(v: float) -> int:
+    """bf16 bit pattern of a value that is exactly representable in bf16."""
+    u = struct.unpack("<I", struct.pack("<f", v))[0]
+    assert u & 0xFFFF == 0, v
+    return u >> 16
+
+
+def f32(v: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+# ------------------------------------------------------------------ helpers
+def const_expert(H, I, w1, w3, w2, s1=127, s3=127, s2=127):
+    """Expert whose every nibble of a tensor holds the same E2M1 code."""
+    def nib(code, rows, cols):
+        return np.full((rows, cols // 2), code | (code << 4), np.uint8)
+    return {"w1": nib(w1, I, H), "s1": np.full((I, H // 32), s1, np.uint8),
+            "w3": nib(w3, I, H), "s3": np.full((I, H // 32), s3, np.uint8),
+            "w2": nib(w2, H, I), "s2": np.full((H, I // 32), s2, np.uint8)}
+
+
+def random_expert(rng, H, I, lo=120, hi=124):
+    return {"w1": rng.integers(0, 256, (I, H // 2), dtype=np.uint8),
+            "s1": rng.integers(lo, hi + 1, (I, H // 32), dtype=np.uint8),
+            "w3": rng.integers(0, 256, (I, H // 2), dtype=np.uint8),
+            "s3": rng.integers(lo, hi + 1, (I, H // 32), dtype=np.uint8),
+            "w2": rng.integers(0, 256, (H, I // 2), dtype=np.uint8),
+            "s2": rng.integers(lo, hi + 1, (H, I // 32), dtype=np.uint8)}
+
+
+def set_nibble(w, r, c, code):
+    b = int(w[r, c // 2])
+    if c % 2:
+        b = (b & 0x0F) | (code << 4)
+    else:
+        b = (b & 0xF0) | code
+    w[r, c // 2] = b
+
+
+def rand_bf16(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ formats
+def pin_e2m1_table(o):
+    """16 codes against the OCP MX v1.0 E2M1 facts (tests/golden/mx_formats.txt)."""
+    g = read_golden("mx_formats.txt")
+    pos = g["e2m1_positive"]
+    for c in range(8):
+        assert o.e2m1(c) == pos[c], (c, o.e2m1(c))
+        neg = o.e2m1(c + 8)
+        assert neg == -pos[c] and math.copysign(1.0, neg) == -1.0, (c + 8, neg)
+    vals = [o.e2m1(c) for c in range(16)]
+    assert max(vals) == g["e2m1_max_normal"][0]
+    assert min(v for v in vals if v >= 1.0) == g["e2m1_min_normal"][0]
+    sub = [v for v in vals if 0 < v < 1.0]
+    assert max(sub) == g["e2m1_max_subnormal"][0] and min(sub) == g["e2m1_min_subnormal"][0]
+
+
+def pin_ue8m0(o):
+    """All 256 scale bytes against torch's float8_e8m0fnu decode (a library routine)."""
+    import torch
+    g = read_golden("mx_formats.txt")
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64)
+    for e in range(256):
+        v = o.ue8m0(e)
+        r = float(ref[e])
+        if e == int(g["e8m0_nan"][0]):
+            assert math.isnan(v) and math.isnan(r)
+        else:
+            assert v == r, (e, v, r)
+    assert o.ue8m0(int(g["e8m0_bias"][0])) == 1.0
+
+
+def pin_bf16_rounding(o):
+    """double -> bf16 against the exact rational rounding of brute.to_bf16_bits."""
+    rng = np.random.default_rng(7)
+    vals = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 1.0 + 2.0 ** -8 + 2.0 ** -40,
+            2.0 ** -130, 2.0 ** -133 * 1.5, 2.0 ** -134, 3.3961e38, 3.4e38, -3.4e38, 1e-45,
+            0.0, -0.0, 255.5, 256.5, 71.99955]
+    vals += list(rng.standard_normal(300) * 10.0 ** rng.integers(-20, 20, 300))
+    for v in vals:
+        a, b = o.to_bf16(v), brute.to_bf16_bits(v)
+        assert a == b, (v, hex(a), hex(b))
+    assert o.to_bf16(float("inf")) == 0x7F80 and o.to_bf16(float("-inf")) == 0xFF80
+    assert (o.to_bf16(float("nan")) & 0x7F80) == 0x7F80 and (o.to_bf16(float("nan")) & 0x7F)
+
+
+# ------------------------------------------------------------------ router
+def pin_router_vs_sort(o):
+    """Top-k = first k of numpy's stable argsort of -logits; gates = scipy softmax."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(11)
+    T, E, k = 64, 37, 5
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[:, 3] = lg[:, 20]          # exact ties
+    lg[::3, 7] = -0.0
+    lg[::3, 2] = 0.0              # -0 vs +0 tie
+    lg[5, :] = lg[5, 0]           # a fully tied row
+    idx, g = o.route(lg, k)
+    ref = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    assert np.array_equal(idx, ref)
+    sel = np.take_along_axis(lg.astype(np.float64), ref, axis=1)
+    assert np.max(np.abs(g - softmax(sel, axis=1))) < 1e-6
+    assert np.max(np.abs(g.astype(np.float64).sum(1) - 1.0)) < 1e-6
+
+
+def pin_router_special(o):
+    E = 12
+    idx, g = o.route(np.full((2, E), 0.75, np.float32), 4)      # all equal
+    assert np.array_equal(idx, np.tile(np.arange(4), (2, 1))) and np.all(g == f32(0.25))
+    lg = np.random.default_rng(3).standard_normal((5, E)).astype(np.float32)
+    idx, g = o.route(lg, 1)                                     # k = 1
+    assert np.array_equal(idx[:, 0], np.argmax(lg, axis=1)) and np.all(g == 1.0)
+    idx, g = o.route(lg, E)                                     # k = E: full order
+    assert np.array_equal(idx, np.argsort(-lg, axis=1, kind="stable"))
+    z = np.zeros((1, E), np.float32)
+    z[0, 0] = -0.0
+    z[0, 1] = -1.0
+    idx, _ = o.route(z, 3)                                      # -0 ties +0
+    assert list(idx[0]) == [0, 2, 3]
+    n = np.zeros((1, E), np.float32)
+    n[0, 0] = np.nan
+    n[0, 5] = -np.inf
+    idx, _ = o.route(n, E)                                      # NaN ranks last
+    assert idx[0, -1] == 0 and idx[0, -2] == 5
+
+
+# ------------------------------------------------------------------ permutation
+def pin_permute(o):
+    """Invariants, plus equality with numpy's stable argsort of the expert ids."""
+    rng = np.random.default_rng(5)
+    for T, E, k in ((1, 384, 6), (33, 16, 2), (257, 40, 6), (2, 8, 8)):
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        idx, _ = o.route(lg, k)
+        counts, offsets, sp, slot = o.permute(idx, E)
+        flat = idx.ravel()
+        assert np.array_equal(counts, np.bincount(flat, minlength=E))
+        assert counts.sum() == T * k and offsets[0] == 0 and offsets[-1] == T * k
+        assert np.all(np.diff(offsets) == counts)
+        assert np.array_equal(np.sort(sp), np.arange(T * k))
+        assert np.array_equal(slot[sp], np.arange(T * k))
+        assert np.array_equal(sp, np.argsort(flat, kind="stable"))
+        for e in range(E):
+            seg = sp[offsets[e]:offsets[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg // k) > 0)
+        assert np.array_equal(np.bincount(sp // k, minlength=T), np.full(T, k))
+
+
+# ------------------------------------------------------------------ one-hot probes
+def pin_probe_w1(o, H=256, I=128, cases=None):
+    """A single nonzero w1 nibble fixes G exactly: G[n0] = x[c0]*E2M1(code)*2^(sc-127).
+
+    w3 is all 1.0, so U[n] = sum(x); x has two nonzeros in the byte holding c0, so a
+    swapped nibble order, a wrong row/column orientation, a wrong scale index or a
+    dropped column all change hpre = silu(G)*U."""
+    cases = cases or [(0, 0, 7, 124), (0, 1, 15, 120), (I - 1, H - 1, 1, 130),
+                      (I // 2 + 3, 37, 9, 126), (5, 32 * 3 + 17, 6, 121), (I - 2, 32, 3, 140)]
+    e2m1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for n0, c0, code, sc in cases:
+        ex = const_expert(H, I, 0, 2, 0)
+        set_nibble(ex["w1"], n0, c0, code)
+        ex["s1"][n0, c0 // 32] = sc
+        x = np.zeros((1, H), np.uint16)
+        a, b = 1.5, -0.625
+        x[0, c0] = bf16_bits(a)
+        x[0, c0 ^ 1] = bf16_bits(b)
+        out = o.forward(H, I, 1, 1, x, np.zeros((1, 1), np.float32), {0: ex}, want_h=True)
+        val = (-1 if code & 8 else 1) * e2m1[code & 7] * 2.0 ** (sc - 127)
+        G = a * val
+        U = a + b
+        want = G / (1.0 + math.exp(-G)) * U
+        hp = out["hpre"][0]
+        assert abs(hp[n0] - want) <= 1e-14 * abs(want), (n0, c0, hp[n0], want)
+        others = np.delete(hp, n0)
+        assert np.all(others == 0.0), (n0, c0)
+
+
+def pin_probe_w2(o, H=256, I=128, cases=None):
+    """A single nonzero w2 nibble at (m0, n0) makes y nonzero only at row m0."""
+    cases = cases or [(0, 0, 7, 124), (H - 1, I - 1, 13, 125), (3, 33, 5, 127), (H // 2, 1, 2, 131)]
+    e2m1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for m0, n0, code, sc in cases:
+        ex = const_expert(H, I, 2, 2, 0)
+        set_nibble(ex["w2"], m0, n0, code)
+        ex["s2"][m0, n0 // 32] = sc
+        x = np.zeros((1, H), np.uint16)
+        a = 1.25
+        x[0, 0] = bf16_bits(a)
+        out = o.forward(H, I, 1, 1, x, np.zeros((1, 1), np.float32), {0: ex}, want_h=True)
+        h0 = brute.bf16_value(brute.to_bf16_bits(a / (1.0 + math.exp(-a)) * a))
+        assert np.all(out["h"][0] == brute.to_bf16_bits(h0))
+        val = (-1 if code & 8 else 1) * e2m1[code & 7] * 2.0 ** (sc - 127)
+        y = out["y"][0]
+        assert y[m0] == f32(h0 * val), (m0, n0, y[m0], h0 * val)
+        assert np.all(np.delete(y, m0) == 0.0), (m0, n0)
+
+
+# ------------------------------------------------------------------ closed forms
+def pin_closed_form_swiglu(o):
+    """Constant-weight experts whose output can be done by hand.
+
+    H = 64, I = 32, x = 3/16 everywhere, two experts, k = 2, logits (0.3, -0.2):
+      expert 0: W1 = 1, W3 = 1/2, W2 = 1/4  -> G = 12, U = 6,  silu(G)U = 71.99955 -> h = 72
+      expert 1: W1 = 1/2, W3 = -1, W2 = 2   -> G = 6,  U = -12, silu(G)U = -71.8218 -> h = -72
+      Y0 = 32*72/4 = 576, Y1 = -32*72*2 = -4608,  y = g0*Y0 + g1*Y1."""
+    H, I = 64, 32
+    e0 = const_expert(H, I, 2, 1, 2, s2=125)       # 1.0, 0.5, 1.0*2^-2
+    e1 = const_expert(H, I, 1, 10, 4)              # 0.5, -1.0, 2.0
+    x = np.full((1, H), bf16_bits(0.1875), np.uint16)
+    lg = np.array([[0.3, -0.2]], np.float32)
+    out = o.forward(H, I, 2, 2, x, lg, {0: e0, 1: e1}, want_h=True)
+    l0, l1 = float(lg[0, 0]), float(lg[0, 1])
+    g0 = f32(1.0 / (1.0 + math.exp(l1 - l0)))
+    g1 = f32(math.exp(l1 - l0) / (1.0 + math.exp(l1 - l0)))
+    assert list(out["idx"][0]) == [0, 1] and out["gates"][0, 0] == g0 and out["gates"][0, 1] == g1
+    assert np.all(out["h"][0] == bf16_bits(72.0)) and np.all(out["h"][1] == bf16_bits(-72.0))
+    want = f32(g0 * 576.0 + g1 * -4608.0)
+    assert np.all(out["y"][0] == want), (out["y"][0][:4], want)
+    # k = 1 keeps only expert 0, gate exactly 1
+    out1 = o.forward(H, I, 2, 1, x, lg, {0: e0, 1: e1})
+    assert np.all(out1["y"][0] == 576.0)
+
+
+def pin_prenorm(o):
+    """x = (3, -4, 3, -4, ...): mean(x^2) = 12.5, u = bf16(x / sqrt(12.5 + 1e-6))."""
+    H = 64
+    x = np.tile(np.array([3.0, -4.0], np.float32), (2, H // 2))
+    x[1] *= -2.0
+    u = o.prenorm(x)
+    r0 = math.sqrt(12.5 + 1e-6)
+    r1 = math.sqrt(50.0 + 1e-6)
+    assert u[0, 0] == brute.to_bf16_bits(3.0 / r0) and u[0, 1] == brute.to_bf16_bits(-4.0 / r0)
+    assert u[1, 0] == brute.to_bf16_bits(-6.0 / r1) and u[1, 1] == brute.to_bf16_bits(8.0 / r1)
+
+
+# ------------------------------------------------------------------ independent implementations
+def pin_brute(o):
+    """Bit-equal with the scalar pure-Python version on a tiny random layer."""
+    rng = np.random.default_rng(21)
+    H, I, E, k, T = 64, 32, 5, 2, 3
+    experts = {e: random_expert(rng, H, I) for e in range(E)}
+    x = rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    out = o.forward(H, I, E, k, x, lg, experts, want_h=True)
+    ys, idx, g, hs = brute.forward(H, I, k, x, lg, experts)
+    assert np.array_equal(out["idx"], np.array(idx))
+    assert np.array_equal(out["gates"], np.array(g, np.float32))
+    for p, h in hs.items():
+        assert np.array_equal(out["h"][p], np.array(h, np.uint16)), p
+    assert np.array_equal(out["y"], np.array(ys, np.float32))
+
+
+def _dequant(w, s):
+    """numpy dequantisation: table lookup + ldexp (for the matmul pin)."""
+    g = read_golden("mx_formats.txt")["e2m1_positive"]
+    table = np.array(g + [-v for v in g])
+    lo = w & 0x0F
+    hi = w >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(w.shape[0], -1)
+    sc = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=1)
+    return table[codes] * sc
+
+
+def pin_numpy_matmul(o):
+    """Against numpy float64 dequantisation + matmul (library GEMM) at a mid shape."""
+    rng = np.random.default_rng(33)
+    H, I, E, k, T = 256, 96, 7, 3, 5
+    experts = {e: random_expert(rng, H, I) for e in range(E)}
+    x = rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    out = o.forward(H, I, E, k, x, lg, experts, want_h=True)
+    xd = bf16_to_f64(x)
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            e = int(out["idx"][t, j])
+            W1 = _dequant(experts[e]["w1"], experts[e]["s1"])
+            W3 = _dequant(experts[e]["w3"], experts[e]["s3"])
+            W2 = _dequant(experts[e]["w2"], experts[e]["s2"])
+            G = W1 @ xd[t]
+            U = W3 @ xd[t]
+            hp = G / (1.0 + np.exp(-G)) * U
+            p = t * k + j
+            assert np.allclose(out["hpre"][p], hp, rtol=1e-12, atol=1e-12 * np.abs(hp).max())
+            Y = W2 @ bf16_to_f64(out["h"][p])
+            acc += float(out["gates"][t, j]) * Y
+        assert np.allclose(out["y"][t], acc.astype(np.float32), rtol=1e-6, atol=1e-6 * np.abs(acc).max())
+
+
+ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pin_router_special,
+            pin_permute, pin_probe_w1, pin_probe_w2, pin_closed_form_swiglu, pin_prenorm,
+            pin_brute, pin_numpy_matmul]

@@ -1,0 +1,29 @@
+"""Every planted mistake in the oracle must be caught by at least one pin.
+
+Each mutant is oracle.c compiled with -DORACLE_MUTANT=n (one deliberate error:
+swapped nibble order, silu on the wrong projection, scale bias off by one, one
+scale for the whole row, ties to the higher index, gates normalised over all
+experts, no gate in the combine, w2 read transposed, h left unrounded, last input
+column dropped, wrong subnormal, sign bit ignored)."""
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {1: "nibble order", 2: "silu on w3", 3: "scale bias 126", 4: "one scale per row",
+           5: "ties to higher index", 6: "softmax over all experts", 7: "no gate",
+           8: "w2 transposed", 9: "h not rounded", 10: "last column dropped",
+           11: "subnormal = 1.0", 12: "sign ignored"}
+
+
+@pytest.mark.parametrize("n", sorted(MUTANTS), ids=lambda n: MUTANTS[n].replace(" ", "_"))
+def test_mutant_is_caught(n, tmp_path):
+    so = oracle.build(str(tmp_path / f"liboracle_mut{n}.so"), mutant=n)
+    o = oracle.Oracle(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {n} ({MUTANTS[n]}) passes every pin"
