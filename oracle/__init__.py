@@ -64,13 +64,18 @@ class Oracle:
         lib.oracle_forward.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
                                       _f32p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                      ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_prenorm.restype = None
         lib.oracle_prenorm.argtypes = [ctypes.c_int, ctypes.c_int, _f32p, ctypes.c_double,
                                        ctypes.c_void_p]
         lib.oracle_stack_layer.restype = ctypes.c_int
         lib.oracle_stack_layer.argtypes = [ctypes.c_int] * 5 + [_f32p, _f32p, ctypes.POINTER(_OW)]
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
         self.lib = lib
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
 
     # ---------------------------------------------------------------- formats
     def e2m1(self, code: int) -> float:
@@ -121,7 +126,7 @@ class Oracle:
                 want_h: bool = False):
         """y for the listed tokens (default all).  `experts` maps expert id -> its six
         byte tensors; only experts the router selects for the listed tokens are needed.
-        Returns dict(y, idx, gates[, h, hpre])."""
+        Returns dict(y, idx, gates[, h, hpre, hbound])."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         logits = np.ascontiguousarray(logits, dtype=np.float32)
         T = x_bits.shape[0]
@@ -133,18 +138,19 @@ class Oracle:
         g = np.empty((T, k), np.float32)
         h = np.zeros((T * k, I), np.uint16) if want_h else None
         hpre = np.zeros((T * k, I), np.float64) if want_h else None
+        hbound = np.zeros((T * k, I), np.float64) if want_h else None
         ow, keep = self._weights(experts, E)
         rc = self.lib.oracle_forward(
             T, H, I, E, k, x_bits.ctypes.data, logits, ctypes.byref(ow), n_tok,
             None if tok is None else tok.ctypes.data, y,
             None if h is None else h.ctypes.data, None if hpre is None else hpre.ctypes.data,
-            idx.ctypes.data, g.ctypes.data)
+            None if hbound is None else hbound.ctypes.data, idx.ctypes.data, g.ctypes.data)
         del keep
         if rc != 0:
             raise KeyError("the router selected an expert whose weights were not given")
         out = {"y": y, "idx": idx, "gates": g}
         if want_h:
-            out["h"], out["hpre"] = h, hpre
+            out["h"], out["hpre"], out["hbound"] = h, hpre, hbound
         return out
 
     def prenorm(self, x: np.ndarray, eps: float = 1e-6) -> np.ndarray:

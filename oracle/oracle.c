@@ -32,6 +32,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ORACLE_MUTANT plants one deliberate mistake (tests only: the mutation tests
  * build a copy with -DORACLE_MUTANT=n and check that some pin catches it).
@@ -161,33 +164,80 @@ typedef struct {
     const uint8_t **w1, **s1, **w3, **s3, **w2, **s2;
 } oracle_weights;
 
+/* Row r of a matrix with `cols` inputs per row, decoded to doubles:
+ * out[c] = E2M1(nibble c of row r) * 2^(scale of group c/32 - 127).
+ * Same values as wval(), one scale decode per group of 32. */
+static void decode_row(const uint8_t *w, const uint8_t *s, int cols, int r, double *out) {
+    double table[16];
+    for (int c = 0; c < 16; ++c) table[c] = oracle_e2m1(c);
+    for (int g = 0; g < cols / 32; ++g) {
+        double sc = oracle_ue8m0(s[(size_t)r * (cols / 32) + (MUT(4) ? 0 : g)]);
+        for (int c = 32 * g; c < 32 * g + 32; ++c) {
+            uint8_t byte = w[(size_t)r * (cols / 2) + (c >> 1)];
+            int code = ((c & 1) != MUT(1)) ? (byte >> 4) : (byte & 0xF);
+            out[c] = table[code] * sc;
+        }
+    }
+}
+
 /* One token through one expert.
  *   G_n = sum_c x_c W1[n][c],  U_n = sum_c x_c W3[n][c]           (double)
  *   h_n = bf16(silu(G_n) * U_n)                                    (one rounding)
  *   Y_m = sum_n h_n W2[m][n]                                       (double)
- * hpre (optional) receives silu(G)*U before rounding. */
+ * Sums run over ascending c (resp. n).  hpre (optional) receives silu(G)*U
+ * before rounding.  hbound (optional) receives a first-order bound on how far
+ * an fp32 evaluation of silu(G)*U can stray from it when G and U are sums of
+ * H fp32 products accumulated in any order (Higham's gamma_H times the sum of
+ * absolute products), plus 8 fp32 ulps for the epilogue. */
 static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const uint8_t *s1,
                        const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
-                       uint16_t *h, double *hpre, double *Y) {
+                       uint16_t *h, double *hpre, double *hbound, double *Y) {
+    const double u32 = ldexp(1.0, -24);
+    const double gam = H * u32 / (1.0 - H * u32);
     double *hv = (double *)malloc(sizeof(double) * (size_t)I);
-    #pragma omp parallel for schedule(static)
-    for (int n = 0; n < I; ++n) {
-        double G = 0.0, U = 0.0;
-        for (int c = 0; c < H - MUT(10); ++c) {
-            G += x[c] * wval(w1, s1, H, n, c);
-            U += x[c] * wval(w3, s3, H, n, c);
+    #pragma omp parallel
+    {
+        double *r1 = (double *)malloc(sizeof(double) * (size_t)H);
+        double *r3 = (double *)malloc(sizeof(double) * (size_t)H);
+        #pragma omp for schedule(static)
+        for (int n = 0; n < I; ++n) {
+            decode_row(w1, s1, H, n, r1);
+            decode_row(w3, s3, H, n, r3);
+            double G = 0.0, U = 0.0, Ga = 0.0, Ua = 0.0;
+            for (int c = 0; c < H - MUT(10); ++c) {
+                G += x[c] * r1[c];
+                U += x[c] * r3[c];
+                Ga += fabs(x[c] * r1[c]);
+                Ua += fabs(x[c] * r3[c]);
+            }
+            double a = MUT(2) ? U / (1.0 + exp(-U)) * G : G / (1.0 + exp(-G)) * U;
+            if (hpre) hpre[n] = a;
+            if (hbound) {
+                double sg = 1.0 / (1.0 + exp(-G));
+                double dsilu = sg * (1.0 + G * (1.0 - sg));
+                hbound[n] = fabs(dsilu * U) * gam * Ga + fabs(G * sg) * gam * Ua + 8.0 * u32 * fabs(a);
+            }
+            h[n] = oracle_double_to_bf16(a);
+            hv[n] = MUT(9) ? a : oracle_bf16_to_double(h[n]);
         }
-        double a = MUT(2) ? U / (1.0 + exp(-U)) * G : G / (1.0 + exp(-G)) * U;
-        if (hpre) hpre[n] = a;
-        h[n] = oracle_double_to_bf16(a);
-        hv[n] = MUT(9) ? a : oracle_bf16_to_double(h[n]);
+        free(r3);
+        free(r1);
     }
-    #pragma omp parallel for schedule(static)
-    for (int m = 0; m < H; ++m) {
-        double acc = 0.0;
-        for (int n = 0; n < I; ++n)
-            acc += hv[n] * (MUT(8) ? wval(w2, s2, H, n, m) : wval(w2, s2, I, m, n));
-        Y[m] = acc;
+    #pragma omp parallel
+    {
+        double *r2 = (double *)malloc(sizeof(double) * (size_t)I);
+        #pragma omp for schedule(static)
+        for (int m = 0; m < H; ++m) {
+            double acc = 0.0;
+            if (MUT(8)) {
+                for (int n = 0; n < I; ++n) acc += hv[n] * wval(w2, s2, H, n, m);
+            } else {
+                decode_row(w2, s2, I, m, r2);
+                for (int n = 0; n < I; ++n) acc += hv[n] * r2[n];
+            }
+            Y[m] = acc;
+        }
+        free(r2);
     }
     free(hv);
 }
@@ -198,11 +248,13 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
  *   y      [n_tok][H] float           y[i] = sum_j g[t][j] * Y_(t,j), j ascending
  *   h_out  optional [T*k][I] bf16 (pair order; only pairs of listed tokens set)
  *   hpre   optional [T*k][I] double (same, before rounding)
+ *   hbound optional [T*k][I] double (fp32 evaluation bound of hpre, see expert_ffn)
  *   idx, gates optional [T*k] outputs of the router
  * Returns 0, or -1 if a selected expert's weights were not provided. */
 int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
                    const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
-                   uint16_t *h_out, double *hpre, int32_t *idx_out, float *gates_out) {
+                   uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
+                   float *gates_out) {
     int P = T * k;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     float *g = (float *)malloc(sizeof(float) * (size_t)P);
@@ -215,6 +267,7 @@ int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const f
     double *acc = (double *)malloc(sizeof(double) * (size_t)H);
     uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
     double *hp = (double *)malloc(sizeof(double) * (size_t)I);
+    double *hb = (double *)malloc(sizeof(double) * (size_t)I);
     int rc = 0;
     for (int i = 0; i < n_tok && rc == 0; ++i) {
         int t = tok ? tok[i] : i;
@@ -227,16 +280,17 @@ int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const f
                 break;
             }
             expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], h,
-                       hp, Y);
+                       hp, hbound ? hb : NULL, Y);
             size_t p = (size_t)t * k + j;
             if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
             if (hpre) memcpy(hpre + p * I, hp, sizeof(double) * (size_t)I);
+            if (hbound) memcpy(hbound + p * I, hb, sizeof(double) * (size_t)I);
             double gj = MUT(7) ? 1.0 : (double)g[p];
             for (int m = 0; m < H; ++m) acc[m] += gj * Y[m];
         }
         for (int m = 0; m < H; ++m) y[(size_t)i * H + m] = (float)acc[m];
     }
-    free(hp); free(h); free(acc); free(Y); free(xd); free(g); free(idx);
+    free(hb); free(hp); free(h); free(acc); free(Y); free(xd); free(g); free(idx);
     return rc;
 }
 
@@ -257,10 +311,19 @@ int oracle_stack_layer(int T, int H, int I, int E, int k, float *x, const float 
     uint16_t *u = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
     float *y = (float *)malloc(sizeof(float) * (size_t)T * H);
     oracle_prenorm(T, H, x, 1e-6, u);
-    int rc = oracle_forward(T, H, I, E, k, u, logits, W, T, NULL, y, NULL, NULL, NULL, NULL);
+    int rc = oracle_forward(T, H, I, E, k, u, logits, W, T, NULL, y, NULL, NULL, NULL, NULL, NULL);
     if (rc == 0)
         for (size_t i = 0; i < (size_t)T * H; ++i) x[i] = (float)((double)x[i] + (double)y[i]);
     free(y);
     free(u);
     return rc;
+}
+
+/* Threads the oracle's parallel loops use. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
