@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed-expert FP4 MoE layer on one MI355X.
+
+Workload (timed steps): decode, T = 1 token per step, 384 experts resident in
+HBM (7.22 GB of FP4 E2M1 codes + UE8M0 scales, 18,800,640 bytes per expert),
+top-6 routing, H = 5120, I = 2304.  Each step is one whole layer call -- router,
+permutation, w1/w3 GEMV with SiLU gating, w2 GEMV with the gate-weighted
+combine -- on a fresh token (x ~ N(0,1) in bf16, logits ~ N(0,1) plus a
+per-expert Zipf(1.1) bias).  Inputs are resident in HBM before timing starts.
+
+Also measured, in the same JSON line: the 2048-token prefill chunk (TFLOP/s),
+per-kernel HIP-event durations (roofline of the dominant decode kernel), a
+cold-cache decode figure (L2/MALL flushed between steps), and the CPU oracle
+timed on a bounded sample of the same decode workload.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 MoE layer: decode µs/token (HBM GB/s) & 2048-tok prefill TFLOP/s"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+SPIN_CYCLES = 200_000_000       # head start for the host to enqueue profiled steps
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(H, I):
+    return 2 * (I * H // 2 + I * H // 32) + (H * I // 2 + H * I // 32)
+
+
+def topk_sets(logits, k):
+    return np.argsort(-logits, axis=1, kind="stable")[:, :k]
+
+
+def decode_bytes(wl, idx):
+    """Algorithmic HBM bytes of one decode step, per kernel."""
+    H, I, T, k = wl.H, wl.I, wl.T, wl.k
+    D = len(np.unique(idx))
+    P = T * k
+    b13 = D * 2 * (I * H // 2 + I * H // 32) + T * H * 2 + P * I * 2
+    b2 = D * (H * I // 2 + H * I // 32) + P * I * 2 + T * H * 4
+    broute = T * wl.E * 4 + P * 4 * 4
+    return {"route": broute, "w13": b13, "w2": b2, "D": D}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode figure")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X and this build has "
+              "no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import mxfp4_routed_expert_router_amd as moe
+    from synth.configs import DECODE as wl, PREFILL as pf
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device: {torch.cuda.get_device_name(dev)}")
+
+    # ---------------------------------------------------------------- set-up
+    t0 = time.time()
+    w = moe.ExpertWeights.from_dict(synth.layer_device(wl, layer=0, device=dev))
+    torch.cuda.synchronize()
+    log(f"weights: {wl.E} experts x {expert_bytes(wl.H, wl.I)} B generated in HBM "
+        f"in {time.time() - t0:.1f} s")
+    n_tok = max(args.steps, 1)
+    n_gen = min(wl.steps, n_tok + args.warmup)
+    xs = np.stack([synth.gen_x(wl, s)[0] for s in range(n_gen)])
+    lgs = np.stack([synth.gen_logits(wl, s)[0] for s in range(n_gen)])
+    x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+    lg_d = torch.from_numpy(lgs).to(dev)
+    y_d = torch.empty((n_gen, wl.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_fp4_workspace_size(1, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8,
+                     device=dev)
+    idx_all = topk_sets(lgs, wl.k)
+
+    def step(i, events=None):
+        j = i % n_gen
+        xi, li, yi = x_d[j:j + 1], lg_d[j:j + 1], y_d[j:j + 1]
+        if events is None:
+            moe.moe_fp4_forward(xi, li, w, wl.k, y=yi, workspace=ws)
+        else:
+            moe.moe_fp4_forward_profiled(xi, li, w, wl.k, events, y=yi, workspace=ws)
+
+    # ---------------------------------------------------------------- decode, timed
+    # The steps are captured once into HIP graphs and replayed: a serving loop
+    # issues a layer call this way, and it keeps the host's per-call launch
+    # overhead (Python + ctypes, tens of microseconds) out of the GPU timeline.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g_plain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_plain):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    g_plain.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g_plain.replay()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    # Kernel durations: HIP events recorded between the layer's kernels on its
+    # stream.  The steps are enqueued behind a spin kernel so that they are all
+    # queued before the first one runs and execute back to back, as in the graph.
+    evs = [moe.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    tp0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[4]) / args.steps
+    stage = np.array([e.stage_ms() for e in evs])  # [steps, 4]: route, w13, w2, combine
+    k_ms = {"route": float(stage[:, 0].mean()), "w13": float(stage[:, 1].mean()),
+            "w2": float(stage[:, 2].mean())}
+    by = [decode_bytes(wl, idx_all[(args.warmup + i) % n_gen][None]) for i in range(args.steps)]
+    k_bytes = {n: float(np.mean([b[n] for b in by])) for n in ("route", "w13", "w2")}
+    step_bytes = k_bytes["route"] + k_bytes["w13"] + k_bytes["w2"]
+    us_tok = ms_per_step * 1e3 / wl.T
+    dom = max(("w13", "w2"), key=lambda n: k_ms[n])
+    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+    log(f"decode: {us_tok:.2f} us/token graph replay ({step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s "
+        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us between stage events); kernels route "
+        f"{k_ms['route'] * 1e3:.2f} us, w1/w3 {k_ms['w13'] * 1e3:.2f} us, "
+        f"w2+combine {k_ms['w2'] * 1e3:.2f} us")
+    eager_t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
+    log(f"decode eager (one Python call per step): {us_eager:.2f} us/token")
+
+    # ---------------------------------------------------------------- decode, cold caches
+    # A read-only flush (summing a 1 GiB buffer) between steps evicts the
+    # experts from L2 and the MALL without leaving dirty lines whose write-back
+    # would compete with the timed step.
+    cold = None
+    if not args.no_cold:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        n_cold = min(64, args.steps)
+        evc = [moe.StageEvents() for _ in range(n_cold)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        sinks = []
+        for i in range(n_cold):
+            sinks.append(flush.sum())
+            step(args.warmup + i, evc[i])
+        torch.cuda.synchronize()
+        st = np.array([e.stage_ms() for e in evc])
+        tot = st[:, :3].sum(1)
+        cold = {"us_per_token": float(tot.mean() * 1e3),
+                "w13_us": float(st[:, 1].mean() * 1e3), "w2_us": float(st[:, 2].mean() * 1e3),
+                "w13_GBps": float(k_bytes["w13"] / (st[:, 1].mean() * 1e-3) / 1e9),
+                "w2_GBps": float(k_bytes["w2"] / (st[:, 2].mean() * 1e-3) / 1e9),
+                "steps": n_cold, "note": "1 GiB read between steps, outside the events"}
+        del flush, sinks
+        log(f"decode cold: {cold['us_per_token']:.2f} us/token (kernel sum), w1/w3 "
+            f"{cold['w13_GBps']:.0f} GB/s, w2 {cold['w2_GBps']:.0f} GB/s")
+
+    # ---------------------------------------------------------------- prefill chunk
+    xp = torch.from_numpy(synth.gen_x(pf, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+    lp_np = synth.gen_logits(pf, 0)
+    lp = torch.from_numpy(lp_np).to(dev)
+    yp = torch.empty((pf.T, pf.H), dtype=torch.float32, device=dev)
+    wsp = torch.empty(moe.moe_fp4_workspace_size(pf.T, pf.H, pf.I, pf.E, pf.k), dtype=torch.uint8,
+                      device=dev)
+    for _ in range(2):
+        moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, workspace=wsp)
+    torch.cuda.synchronize()
+    evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
+    tp0 = time.perf_counter()
+    for i in range(args.prefill_reps):
+        moe.moe_fp4_forward_profiled(xp, lp, w, pf.k, evp[i], y=yp, workspace=wsp)
+    torch.cuda.synchronize()
+    tp1 = time.perf_counter()
+    pst = np.array([e.stage_ms() for e in evp])
+    p_ms = (tp1 - tp0) * 1e3 / args.prefill_reps
+    pairs = pf.T * pf.k
+    flops = pairs * (2 * 2 * pf.H * pf.I + 2 * pf.I * pf.H)
+    Dp = len(np.unique(topk_sets(lp_np, pf.k)))
+    p_bytes = Dp * expert_bytes(pf.H, pf.I) + pf.T * pf.H * 2 + pf.T * pf.H * 4
+    prefill = {
+        "workload": "prefill chunk T=2048, E=384, top-6, H=5120, I=2304, Zipf(0.3) logit bias",
+        "ms_per_chunk": p_ms, "tflops": flops / (p_ms * 1e-3) / 1e12, "gflop": flops / 1e9,
+        "distinct_experts": Dp, "weight_GB": Dp * expert_bytes(pf.H, pf.I) / 1e9,
+        "hbm_frac": p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "mfma_bf16_frac": flops / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "kernel_ms": {"route": float(pst[:, 0].mean()), "gemm13": float(pst[:, 1].mean()),
+                      "gemm2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
+    }
+    prefill["roofline_frac"] = max(prefill["hbm_frac"], prefill["mfma_bf16_frac"])
+    log(f"prefill: {p_ms:.3f} ms/chunk, {prefill['tflops']:.1f} TFLOP/s, HBM frac "
+        f"{prefill['hbm_frac']:.2f}, kernels {prefill['kernel_ms']}")
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        o = oracle.get()
+        spent, n, i = 0.0, 0, 0
+        while spent < args.cpu_seconds and n < n_gen:
+            ids = np.unique(idx_all[i])
+            experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in ids}
+            tc = time.perf_counter()
+            o.forward(wl.H, wl.I, wl.E, wl.k, xs[i:i + 1], lgs[i:i + 1], experts)
+            spent += time.perf_counter() - tc
+            n += 1
+            i += 1
+        cpu = {"value": spent / n * 1e6, "unit": "us/token", "cores": o.threads(), "kind": "oracle",
+               "sample": f"{n} decode tokens of the same workload (T=1, 6 of 384 experts, full "
+                         f"H=5120, I=2304), one oracle call each; weight generation excluded"}
+        log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads ({n} tokens)")
+
+    res = {
+        "metric": METRIC,
+        "value": round(us_tok, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode T=1, E=384 resident (7.22 GB FP4 E2M1 + UE8M0), top-6, "
+                               "H=5120, I=2304, Zipf(1.1) logit bias, 256 distinct tokens",
+                   "T": wl.T, "E": wl.E, "k": wl.k, "H": wl.H, "I": wl.I},
+        "tokens_per_s": 1e3 / ms_per_step * wl.T,
+        "hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": {"w13": "gemv13_kernel", "w2": "gemv2_combine_kernel"}[dom],
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": k_bytes[dom], "avg_us": k_ms[dom] * 1e3},
+        "kernels_us": {n: round(v * 1e3, 3) for n, v in k_ms.items()},
+        "timing": "value: HIP graph of all steps, replayed once (wall clock); kernel durations: "
+                  "HIP events recorded between the layer's kernels on its stream, steps queued "
+                  "back to back",
+        "us_per_token_with_events": ms_per_step_prof * 1e3 / wl.T,
+        "us_per_token_eager": us_eager,
+        "cold": cold,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

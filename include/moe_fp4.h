@@ -1,0 +1,164 @@
+/*
+ * moe_fp4 -- one routed-expert FP4 mixture-of-experts layer on MI355X (gfx950).
+ *
+ * The layer is the DeepSeek-V4.1-Flash routed-expert block as the 10100.com
+ * page describes it (section on the MoE expert-capacity bottleneck): each token
+ * picks k of E routed experts (6 of 384 in the model), and each picked expert is
+ * an FFN with three matrices w1, w3 (I x H) and w2 (H x I) stored as FP4 E2M1
+ * codes, two per byte, with one UE8M0 scale byte per 32 consecutive inputs of a
+ * row: w1/w3 [2304, 2560 B] + [2304, 160], w2 [5120, 1152 B] + [5120, 72],
+ * 18,800,640 bytes per expert.  The ai-shiz.ru page (section on the model) gives
+ * hidden 5120 and the 6-of-384 routing.
+ *
+ * Computation (readings of what the pages leave open):
+ *   route    idx[t][0..k) = the k largest logits of token t, larger first, ties to
+ *            the lower expert index, -0 equal to +0, NaN below every number;
+ *            gates[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k chosen.
+ *   expert   G = W1 x, U = W3 x, h = bf16_rne(silu(G) * U), Y = W2 h, with
+ *            W[r][c] = E2M1(nibble) * 2^(scale - 127), the low nibble of a byte
+ *            holding the even input.
+ *   combine  y[t] = sum_j gates[t][j] * Y_(t, idx[t][j]), j ascending, fp32.
+ * Accumulation is fp32 on MFMA; h is rounded to bf16 once, after silu(G)*U.
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, frees nothing and keeps no state between calls.
+ *   - A call validates its arguments on the host before any HIP call, enqueues
+ *     its kernels on `stream` and returns without synchronising.  Faults in the
+ *     kernels surface at the caller's next synchronisation.
+ *   - Inputs are read-only.  Calls that share a workspace must not overlap.
+ *   - Return value: MOE_FP4_OK or one of the error codes below; nothing is
+ *     enqueued when a call returns an error found during validation.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes */
+#define MOE_FP4_OK            0
+#define MOE_FP4_EINVAL        1  /* null pointer, non-positive or inconsistent size */
+#define MOE_FP4_EUNSUPPORTED  2  /* sizes outside the supported range (see below)  */
+#define MOE_FP4_EALIGN        3  /* a pointer or stride breaks its alignment rule   */
+#define MOE_FP4_EWORKSPACE    4  /* workspace missing or smaller than required      */
+#define MOE_FP4_EHIP          5  /* a kernel launch failed (hipGetLastError)        */
+
+/* ---- forward modes */
+#define MOE_FP4_MODE_AUTO     0  /* DECODE when T <= 32, else PREFILL                */
+#define MOE_FP4_MODE_DECODE   1  /* split-K GEMV path; requires T <= 32              */
+#define MOE_FP4_MODE_PREFILL  2  /* grouped-GEMM path; any T                         */
+
+/* ---- forward flags */
+#define MOE_FP4_ACCUMULATE    1  /* y += layer output (default: y = layer output)    */
+
+/* Supported range: 1 <= T <= 65536, 1 <= E <= 1024, 1 <= k <= min(E, 16),
+ * H and I multiples of 32 with 32 <= H, I <= 16384. */
+typedef struct {
+  int32_t T;  /* tokens in the call                  */
+  int32_t H;  /* hidden size (input of w1/w3)        */
+  int32_t I;  /* intermediate size (input of w2)     */
+  int32_t E;  /* routed experts in the weight tensors */
+  int32_t k;  /* experts per token                   */
+} moe_fp4_dims;
+
+/* Expert weights in the checkpoint layout, all uint8:
+ *   w1, w3  per expert [I][H/2] E2M1 code pairs (low nibble = even input column)
+ *   s1, s3  per expert [I][H/32] UE8M0 scales (scale g covers inputs 32g..32g+31)
+ *   w2      per expert [H][I/2]
+ *   s2      per expert [H][I/32]
+ * expert_stride[i] is the byte distance between consecutive experts of tensor
+ * i (order w1, s1, w3, s3, w2, s2); 0 means dense stacking (the per-expert size).
+ * Nibble tensors (w1, w3, w2) need 16-byte aligned bases and strides; scale
+ * tensors have no alignment rule.  Supported scale bytes are 2..252. */
+typedef struct {
+  const uint8_t *w1, *s1, *w3, *s3, *w2, *s2;
+  int64_t expert_stride[6];
+} moe_fp4_weights;
+
+/* Routing result, all device arrays written by moe_fp4_route:
+ *   topk_idx      [T][k] expert ids in rank order
+ *   gates         [T][k] fp32 gates in rank order
+ *   counts        [E]    pairs routed to each expert
+ *   offsets       [E+1]  exclusive prefix sum of counts (offsets[E] = T*k)
+ *   sorted_pairs  [T*k]  pair ids p = t*k + j grouped by expert (ascending expert),
+ *                        ascending p within an expert
+ *   pair_slot     [T*k]  inverse permutation: sorted_pairs[pair_slot[p]] == p */
+typedef struct {
+  int32_t *topk_idx;
+  float *gates;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *sorted_pairs;
+  int32_t *pair_slot;
+} moe_fp4_route_out;
+
+/* Bytes of workspace moe_fp4_forward needs for these dims and mode.
+ * Errors: EINVAL (null), EUNSUPPORTED (dims out of range or mode unknown). */
+int moe_fp4_workspace_size(const moe_fp4_dims *dims, int mode, size_t *bytes);
+
+/* Router and token permutation (top-k + softmax over the chosen logits, then a
+ * histogram, scan and stable scatter of the T*k pairs grouped by expert).
+ *   logits  [T][E] fp32, row-major, 4-byte aligned.
+ * Results are bit-exact functions of the logits (no atomics-order dependence).
+ * Errors: EINVAL (a null pointer), EUNSUPPORTED (dims), EHIP. */
+int moe_fp4_route(const moe_fp4_dims *dims, const float *logits, moe_fp4_route_out *out,
+                  hipStream_t stream);
+
+/* Whole layer: route, experts, combine.
+ *   x       [T][H] bf16 bit patterns, 16-byte aligned
+ *   logits  [T][E] fp32
+ *   w       expert weights (see moe_fp4_weights)
+ *   y       [T][H] fp32, 16-byte aligned; overwritten, or added to with
+ *           MOE_FP4_ACCUMULATE
+ *   ws      device workspace of at least moe_fp4_workspace_size(dims, mode)
+ *           bytes, 256-byte aligned; its contents need no initialisation
+ * Errors: EINVAL, EUNSUPPORTED (dims, unknown mode or flag, DECODE with T > 32),
+ * EALIGN, EWORKSPACE, EHIP. */
+int moe_fp4_forward(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                    const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* As moe_fp4_forward, and also writes the intermediates:
+ *   h_out      [T*k][I] bf16 bits in pair order (row p = t*k + j), or NULL
+ *   route_out  routing result as moe_fp4_route writes it, or NULL */
+int moe_fp4_forward_debug(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                          const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
+                          size_t ws_bytes, hipStream_t stream, uint16_t *h_out,
+                          moe_fp4_route_out *route_out);
+
+/* As moe_fp4_forward, and records HIP events on `stream` at the stage
+ * boundaries, for timing each kernel of the layer on the stream it runs on:
+ *   events[0] before routing            events[1] after routing
+ *   events[2] after the w1/w3 stage     events[3] after the w2 stage
+ *   events[4] after the combine (PREFILL; in DECODE the combine is fused into
+ *             the w2 stage and events[4] is recorded right after events[3]).
+ * `events` holds n_events >= 5 events created by the caller.
+ * Errors: as moe_fp4_forward, and EINVAL for null events or n_events < 5. */
+int moe_fp4_forward_profiled(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                             const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
+                             size_t ws_bytes, hipStream_t stream, hipEvent_t *events,
+                             int n_events);
+
+/* Pre-normalisation for a residual stack of layers:
+ *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
+ *   x [T][H] fp32, u [T][H] bf16 bits.
+ * Errors: EINVAL, EUNSUPPORTED (H not a multiple of 32 or above 16384), EHIP. */
+int moe_fp4_prenorm_bf16(const float *x, uint16_t *u, int32_t T, int32_t H, float eps,
+                         hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *moe_fp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

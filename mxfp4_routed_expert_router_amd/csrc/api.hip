@@ -1,0 +1,227 @@
+// C-ABI of the moe_fp4 library: argument validation, workspace layout and
+// dispatch to the route / decode / prefill kernels.  Every check runs on the
+// host before the first HIP call, so a rejected call enqueues nothing.
+#include "../../include/moe_fp4.h"
+
+#include <new>
+
+#include "kernels.h"
+
+using namespace moe_fp4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool dims_ok(const moe_fp4_dims& d) {
+  return d.T >= 1 && d.T <= 65535 && d.E >= 1 && d.E <= kMaxExperts && d.k >= 1 && d.k <= d.E &&
+         d.k <= kMaxK && d.H >= 32 && d.H <= 16384 && d.H % 32 == 0 && d.I >= 32 &&
+         d.I <= 16384 && d.I % 32 == 0;
+}
+
+// Mode that a call actually runs, or -1 if the dims do not allow it.
+int resolve_mode(const moe_fp4_dims& d, int mode) {
+  const bool decode_ok = decode_fits(d.T, d.H, d.I, d.k);
+  switch (mode) {
+    case MOE_FP4_MODE_AUTO: return decode_ok ? MOE_FP4_MODE_DECODE : MOE_FP4_MODE_PREFILL;
+    case MOE_FP4_MODE_DECODE: return decode_ok ? MOE_FP4_MODE_DECODE : -1;
+    case MOE_FP4_MODE_PREFILL: return MOE_FP4_MODE_PREFILL;
+    default: return -1;
+  }
+}
+
+// Workspace sections, each 256-byte aligned.
+struct WsLayout {
+  size_t idx, gates, counts, offsets, sorted, slot, dinfo, meta, h, ypair, total;
+};
+
+WsLayout layout(const moe_fp4_dims& d, int rmode) {
+  const size_t P = (size_t)d.T * d.k;
+  WsLayout L{};
+  size_t o = 0;
+  L.idx = o;      o = align_up(o + P * 4);
+  L.gates = o;    o = align_up(o + P * 4);
+  L.counts = o;   o = align_up(o + (size_t)d.E * 4);
+  L.offsets = o;  o = align_up(o + (size_t)(d.E + 1) * 4);
+  L.sorted = o;   o = align_up(o + P * 4);
+  L.slot = o;     o = align_up(o + P * 4);
+  L.dinfo = o;    o = align_up(o + (size_t)d.E * 16);
+  L.meta = o;     o = align_up(o + 64);
+  L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
+  L.ypair = o;
+  if (rmode == MOE_FP4_MODE_PREFILL) o = align_up(o + P * (size_t)d.H * 4);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                 const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
+                 size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
+                 moe_fp4_route_out* route_out, const hipEvent_t* events) {
+  if (!dims || !x || !logits || !w || !y || !ws) return MOE_FP4_EINVAL;
+  if (!w->w1 || !w->s1 || !w->w3 || !w->s3 || !w->w2 || !w->s2) return MOE_FP4_EINVAL;
+  if (route_out && (!route_out->topk_idx || !route_out->gates || !route_out->counts ||
+                    !route_out->offsets || !route_out->sorted_pairs || !route_out->pair_slot))
+    return MOE_FP4_EINVAL;
+  for (int i = 0; i < 6; ++i)
+    if (w->expert_stride[i] < 0) return MOE_FP4_EINVAL;
+  const moe_fp4_dims d = *dims;
+  if (d.T < 1 || d.H < 1 || d.I < 1 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_FP4_EINVAL;
+  if (!dims_ok(d)) return MOE_FP4_EUNSUPPORTED;
+  if (flags & ~MOE_FP4_ACCUMULATE) return MOE_FP4_EUNSUPPORTED;
+  const int rmode = resolve_mode(d, mode);
+  if (rmode < 0) return MOE_FP4_EUNSUPPORTED;
+
+  // per-expert tensor sizes in bytes, in the order w1, s1, w3, s3, w2, s2
+  const int64_t per[6] = {(int64_t)d.I * d.H / 2, (int64_t)d.I * d.H / 32,
+                          (int64_t)d.I * d.H / 2, (int64_t)d.I * d.H / 32,
+                          (int64_t)d.H * d.I / 2, (int64_t)d.H * d.I / 32};
+  int64_t stride[6];
+  for (int i = 0; i < 6; ++i) stride[i] = w->expert_stride[i] ? w->expert_stride[i] : per[i];
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(w->w1, 16) ||
+      !aligned(w->w3, 16) || !aligned(w->w2, 16) || stride[0] % 16 || stride[2] % 16 ||
+      stride[4] % 16 || (h_out && !aligned(h_out, 4)))
+    return MOE_FP4_EALIGN;
+  const WsLayout L = layout(d, rmode);
+  if (ws_bytes < L.total) return MOE_FP4_EWORKSPACE;
+
+  RouteArgs r{};
+  r.logits = logits;
+  r.T = d.T; r.E = d.E; r.k = d.k;
+  r.idx = at<int32_t>(ws, L.idx);
+  r.gates = at<float>(ws, L.gates);
+  r.counts = at<int32_t>(ws, L.counts);
+  r.offsets = at<int32_t>(ws, L.offsets);
+  r.sorted_pairs = at<int32_t>(ws, L.sorted);
+  r.pair_slot = at<int32_t>(ws, L.slot);
+  r.dinfo = at<int32_t>(ws, L.dinfo);
+  r.meta = at<int32_t>(ws, L.meta);
+  // A one-token decode ranks the logits inside its first expert kernel.
+  const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.E);
+  if (events) (void)hipEventRecord(events[0], stream);
+  if (!fused && launch_route(r, stream) != hipSuccess) return MOE_FP4_EHIP;
+  if (events) (void)hipEventRecord(events[1], stream);
+
+  LayerArgs a{};
+  a.T = d.T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
+  a.x = x;
+  a.w1 = w->w1; a.s1 = w->s1; a.w3 = w->w3; a.s3 = w->s3; a.w2 = w->w2; a.s2 = w->s2;
+  for (int i = 0; i < 6; ++i) a.stride[i] = stride[i];
+  a.counts = r.counts; a.offsets = r.offsets; a.sorted_pairs = r.sorted_pairs;
+  a.pair_slot = r.pair_slot; a.dinfo = r.dinfo; a.meta = r.meta; a.gates = r.gates;
+  a.h = at<uint16_t>(ws, L.h);
+  a.ypair = rmode == MOE_FP4_MODE_PREFILL ? at<float>(ws, L.ypair) : nullptr;
+  a.y = y;
+  a.accumulate = (flags & MOE_FP4_ACCUMULATE) ? 1 : 0;
+  a.stage_events = events ? events + 2 : nullptr;
+  a.fused_route = fused ? 1 : 0;
+  a.route = r;
+  a.logits = logits;
+  const hipError_t err = rmode == MOE_FP4_MODE_DECODE ? launch_decode(a, stream)
+                                                      : launch_prefill(a, stream);
+  if (err != hipSuccess) return MOE_FP4_EHIP;
+
+  if (h_out && launch_unsort_h(a, h_out, stream) != hipSuccess) return MOE_FP4_EHIP;
+  if (route_out) {
+    const size_t P = (size_t)d.T * d.k;
+    const struct { void* dst; const void* src; size_t n; } cp[6] = {
+        {route_out->topk_idx, r.idx, P * 4},       {route_out->gates, r.gates, P * 4},
+        {route_out->counts, r.counts, (size_t)d.E * 4},
+        {route_out->offsets, r.offsets, (size_t)(d.E + 1) * 4},
+        {route_out->sorted_pairs, r.sorted_pairs, P * 4},
+        {route_out->pair_slot, r.pair_slot, P * 4}};
+    for (const auto& c : cp)
+      if (hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return MOE_FP4_EHIP;
+  }
+  return MOE_FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_fp4_workspace_size(const moe_fp4_dims* dims, int mode, size_t* bytes) {
+  if (!dims || !bytes) return MOE_FP4_EINVAL;
+  if (!dims_ok(*dims)) return MOE_FP4_EUNSUPPORTED;
+  const int rmode = resolve_mode(*dims, mode);
+  if (rmode < 0) return MOE_FP4_EUNSUPPORTED;
+  *bytes = layout(*dims, rmode).total;
+  return MOE_FP4_OK;
+}
+
+int moe_fp4_route(const moe_fp4_dims* dims, const float* logits, moe_fp4_route_out* out,
+                  hipStream_t stream) {
+  if (!dims || !logits || !out || !out->topk_idx || !out->gates || !out->counts ||
+      !out->offsets || !out->sorted_pairs || !out->pair_slot)
+    return MOE_FP4_EINVAL;
+  const moe_fp4_dims d = *dims;
+  if (d.T < 1 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_FP4_EINVAL;
+  if (d.T > 65535 || d.E > kMaxExperts || d.k > kMaxK) return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(logits, 4)) return MOE_FP4_EALIGN;
+  // The per-distinct-expert records are internal to the forward path; with null
+  // pointers the permutation skips it.
+  RouteArgs r{};
+  r.logits = logits;
+  r.T = d.T; r.E = d.E; r.k = d.k;
+  r.idx = out->topk_idx; r.gates = out->gates; r.counts = out->counts; r.offsets = out->offsets;
+  r.sorted_pairs = out->sorted_pairs; r.pair_slot = out->pair_slot;
+  r.dinfo = nullptr; r.meta = nullptr;
+  return launch_route(r, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
+}
+
+int moe_fp4_forward(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                    const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, nullptr, nullptr,
+                      nullptr);
+}
+
+int moe_fp4_forward_profiled(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                             const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
+                             size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
+                             int n_events) {
+  if (!events || n_events < 5) return MOE_FP4_EINVAL;
+  for (int i = 0; i < 5; ++i)
+    if (!events[i]) return MOE_FP4_EINVAL;
+  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, nullptr, nullptr,
+                      events);
+}
+
+int moe_fp4_forward_debug(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                          const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
+                          size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
+                          moe_fp4_route_out* route_out) {
+  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, h_out, route_out,
+                      nullptr);
+}
+
+int moe_fp4_prenorm_bf16(const float* x, uint16_t* u, int32_t T, int32_t H, float eps,
+                         hipStream_t stream) {
+  if (!x || !u || T < 1 || H < 1) return MOE_FP4_EINVAL;
+  if (H % 32 || H > 16384) return MOE_FP4_EUNSUPPORTED;
+  return launch_prenorm(x, u, T, H, eps, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
+}
+
+const char* moe_fp4_status_string(int status) {
+  switch (status) {
+    case MOE_FP4_OK: return "ok";
+    case MOE_FP4_EINVAL: return "invalid argument (null pointer or inconsistent size)";
+    case MOE_FP4_EUNSUPPORTED: return "unsupported sizes, mode or flags";
+    case MOE_FP4_EALIGN: return "misaligned pointer or stride";
+    case MOE_FP4_EWORKSPACE: return "workspace missing or too small";
+    case MOE_FP4_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_fp4 {
+
+constexpr int kMaxExperts = 1024;      // router / permutation LDS tables
+constexpr int kMaxK = 16;
+constexpr int kSmallRouteTokens = 64;  // one-launch route for small batches
+constexpr int kSmallRoutePairs = 1024;
+constexpr int kDecodeMaxTokens = 16;   // decode GEMV: one 16-token MFMA tile per expert
+constexpr size_t kDecodeLds = 65536;   // LDS budget of each decode kernel (x / h rows staged whole)
+
+struct RouteArgs {
+  const float* logits;
+  int T, E, k;
+  int32_t *idx, *counts, *offsets, *sorted_pairs, *pair_slot, *dinfo, *meta;  // dinfo: per distinct expert {id, first sorted slot, pairs, 0}
+  float* gates;
+};
+
+// Weights and routing state shared by the expert kernels.
+struct LayerArgs {
+  int T, H, I, E, k;
+  const uint16_t* x;
+  const uint8_t *w1, *s1, *w3, *s3, *w2, *s2;
+  int64_t stride[6];  // resolved byte strides between experts
+  const int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *dinfo, *meta;  // dinfo: per distinct expert {id, first sorted slot, pairs, 0}
+  const float* gates;
+  uint16_t* h;   // [T*k][I] bf16, rows in sorted (by-expert) order
+  float* ypair;  // [T*k][H] fp32 gate-scaled expert outputs, sorted order (prefill only)
+  float* y;      // [T][H]
+  int accumulate;
+  const hipEvent_t* stage_events;  // optional: recorded after each expert-stage kernel
+  // one-token decode: the first expert kernel ranks the logits itself and
+  // publishes the routing result (no separate routing launch)
+  int fused_route;
+  RouteArgs route;
+  const float* logits;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+bool decode_fits(int T, int H, int I, int k);  // shapes the decode kernels take
+bool decode_fuses_route(int T, int H, int E);  // decode computes the routing in its first kernel
+hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);
+hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);
+
+}  // namespace moe_fp4

@@ -1,0 +1,254 @@
+// Router (top-k + softmax over the chosen logits) and token permutation grouped
+// by expert (histogram, exclusive scan, stable scatter).
+//
+// What is computed follows the 10100.com page's description of the layer (each
+// token picks 6 of the 384 routed experts of a layer) with the readings stated
+// in include/moe_fp4.h: larger logit first, ties to the lower expert index, -0
+// equal to +0, NaN last; gates are a softmax over the k chosen logits.  Every
+// output is a deterministic function of the logits: the ranking is exact integer
+// comparison and the scatter orders pairs by (expert, pair id) without relying on
+// the order in which atomics land.
+#include "device_common.h"
+#include "kernels.h"
+#include "topk.h"
+
+namespace moe_fp4 {
+namespace {
+
+template <int VPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ gates) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // whole waves leave together
+  wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, idx + (size_t)t * k, gates + (size_t)t * k);
+}
+
+// Inclusive scan across a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+template <int NTH>
+struct PermSmem {
+  static constexpr int kWaves = NTH / kWave;
+  int cnt[kMaxExperts];
+  int base[kMaxExperts];
+  uint8_t wcnt[kWaves][kMaxExperts];
+  int wsum[2 * kWave + 1];
+};
+
+// Exclusive scan of kMaxExperts values; thread t owns entries
+// t*PER .. t*PER+PER-1 in `vals`, which it gets back as exclusive prefixes.
+template <int NTH>
+__device__ void block_excl_scan_e(int (&vals)[kMaxExperts / NTH], int* s_wsum, int* total) {
+  constexpr int PER = kMaxExperts / NTH, NW = NTH / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) mine += vals[q];
+  const int inc = wave_incl_scan(mine, lane);
+  if (lane == kWave - 1) s_wsum[w] = inc;
+  lds_barrier();
+  if (w == 0) {
+    const int x = lane < NW ? s_wsum[lane] : 0;
+    const int xi = wave_incl_scan(x, lane);
+    if (lane < NW) s_wsum[kWave + lane] = xi - x;
+    if (lane == NW - 1) s_wsum[2 * kWave] = xi;
+  }
+  lds_barrier();
+  int run = inc - mine + s_wsum[kWave + w];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int v = vals[q];
+    vals[q] = run;
+    run += v;
+  }
+  *total = s_wsum[2 * kWave];
+  lds_barrier();
+}
+
+// Histogram, scan and stable scatter of the P pairs of `idx` (LDS or global)
+// by one NTH-thread block.  Pairs are taken in chunks of NTH in pair order;
+// inside a chunk a pair's position is base[e] + (pairs of e in earlier waves of
+// the chunk) + (pairs of e in earlier lanes of its wave), so the result is the
+// stable order whatever the timing of the LDS atomics in the histogram.
+template <int NTH>
+__device__ void block_permute(const int32_t* idx, int P, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* dinfo,
+                              int32_t* meta, PermSmem<NTH>& sm) {
+  constexpr int NW = NTH / kWave, PER = kMaxExperts / NTH;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  for (int e = tid; e < kMaxExperts; e += NTH) {
+    sm.cnt[e] = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) sm.wcnt[q][e] = 0;
+  }
+  lds_barrier();
+  for (int p = tid; p < P; p += NTH) atomicAdd(&sm.cnt[idx[p]], 1);
+  lds_barrier();
+  // offsets, and the ascending list of experts that received pairs
+  int c[PER], f[PER], cc[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    cc[q] = c[q] = sm.cnt[tid * PER + q];
+    f[q] = c[q] > 0 ? 1 : 0;
+  }
+  int total = 0, nd = 0;
+  block_excl_scan_e<NTH>(c, sm.wsum, &total);
+  block_excl_scan_e<NTH>(f, sm.wsum, &nd);
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = tid * PER + q;
+    if (e < E) {
+      counts[e] = cc[q];
+      offsets[e] = c[q];
+      sm.base[e] = c[q];
+      if (cc[q] > 0 && dinfo) {
+        dinfo[4 * f[q] + 0] = e;
+        dinfo[4 * f[q] + 1] = c[q];
+        dinfo[4 * f[q] + 2] = cc[q];
+        dinfo[4 * f[q] + 3] = 0;
+      }
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    if (meta) meta[0] = nd;
+  }
+  // records past the last distinct expert (up to the grid the expert kernels
+  // launch, min(P, E)) say "no expert"
+  if (dinfo)
+    for (int x = nd + tid; x < (P < E ? P : E); x += NTH) dinfo[4 * x] = -1;
+  lds_barrier();
+  for (int c0 = 0; c0 < P; c0 += NTH) {
+    const int p = c0 + tid;
+    const bool valid = p < P;
+    const int e = valid ? idx[p] : -1;
+    // lanes of this wave holding the same expert
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) sm.wcnt[w][e] = (uint8_t)__popcll(peers);
+    lds_barrier();
+    if (valid) {
+      int pos = sm.base[e] + rank;
+      for (int q = 0; q < w; ++q) pos += sm.wcnt[q][e];
+      sorted_pairs[pos] = p;
+      pair_slot[p] = pos;
+    }
+    lds_barrier();
+    if (c0 + NTH < P) {  // advance the per-expert bases for the next chunk
+      for (int x = tid; x < E; x += NTH) {
+        int add = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+          add += sm.wcnt[q][x];
+          sm.wcnt[q][x] = 0;
+        }
+        sm.base[x] += add;
+      }
+      lds_barrier();
+    }
+  }
+}
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermLdsPairs = 16384;  // expert ids staged in LDS up to this many pairs
+
+__global__ void __launch_bounds__(kPermThreads)
+permute_kernel(const int32_t* __restrict__ idx, int P, int E, int32_t* counts, int32_t* offsets,
+               int32_t* sorted_pairs, int32_t* pair_slot, int32_t* dinfo, int32_t* meta) {
+  __shared__ PermSmem<kPermThreads> sm;
+  __shared__ int32_t s_idx[kPermLdsPairs];
+  const int32_t* src = idx;
+  if (P <= kPermLdsPairs) {
+    for (int p = threadIdx.x; p < P; p += kPermThreads) s_idx[p] = idx[p];
+    lds_barrier();
+    src = s_idx;
+  }
+  block_permute<kPermThreads>(src, P, E, counts, offsets, sorted_pairs, pair_slot, dinfo, meta,
+                              sm);
+}
+
+// Small batches: top-k and permutation in one launch of 256 threads.  The four
+// waves take the tokens in turn; the chosen ids go through LDS.
+constexpr int kSmallThreads = 256;
+
+template <int VPL>
+__global__ void __launch_bounds__(kSmallThreads)
+route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* idx,
+                   float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                   int32_t* pair_slot, int32_t* dinfo, int32_t* meta) {
+  __shared__ PermSmem<kSmallThreads> sm;
+  __shared__ int32_t s_idx[kSmallRoutePairs];
+  __shared__ float s_g[kSmallRoutePairs];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  for (int t = w; t < T; t += kSmallThreads / kWave)
+    wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, s_idx + t * k, s_g + t * k);
+  lds_barrier();
+  const int P = T * k;
+  for (int p = threadIdx.x; p < P; p += kSmallThreads) {
+    idx[p] = s_idx[p];
+    gates[p] = s_g[p];
+  }
+  block_permute<kSmallThreads>(s_idx, P, E, counts, offsets, sorted_pairs, pair_slot, dinfo,
+                               meta, sm);
+}
+
+int vpl_for(int E) {
+  const int v = (E + kWave - 1) / kWave;
+  return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 6 ? 6 : v <= 8 ? 8 : 16;
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  const int P = a.T * a.k;
+  const int vpl = vpl_for(a.E);
+  if (a.T <= kSmallRouteTokens && P <= kSmallRoutePairs) {
+#define MOE_ROUTE_SMALL(V)                                                                       \
+  hipLaunchKernelGGL(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, a.logits,  \
+                     a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets, a.sorted_pairs,        \
+                     a.pair_slot, a.dinfo, a.meta)
+    switch (vpl) {
+      case 1: MOE_ROUTE_SMALL(1); break;
+      case 2: MOE_ROUTE_SMALL(2); break;
+      case 4: MOE_ROUTE_SMALL(4); break;
+      case 6: MOE_ROUTE_SMALL(6); break;
+      case 8: MOE_ROUTE_SMALL(8); break;
+      default: MOE_ROUTE_SMALL(16); break;
+    }
+#undef MOE_ROUTE_SMALL
+  } else {
+    const int wpb = 4;
+    const dim3 grid((a.T + wpb - 1) / wpb), block(wpb * kWave);
+#define MOE_TOPK(V) \
+  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, stream, a.logits, a.T, a.E, a.k, a.idx, a.gates)
+    switch (vpl) {
+      case 1: MOE_TOPK(1); break;
+      case 2: MOE_TOPK(2); break;
+      case 4: MOE_TOPK(4); break;
+      case 6: MOE_TOPK(6); break;
+      case 8: MOE_TOPK(8); break;
+      default: MOE_TOPK(16); break;
+    }
+#undef MOE_TOPK
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, a.idx, P, a.E,
+                       a.counts, a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe_fp4

@@ -1,0 +1,72 @@
+// Router top-k shared by the routing kernels and the fused one-token decode
+// kernel: one wave ranks one token's E logits (larger first, ties to the lower
+// expert index, -0 equal to +0, NaN last) and forms the softmax over the k
+// chosen logits.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe_fp4 {
+
+// Monotone map of a float onto uint32: larger float -> larger key; -0 maps to
+// the key of +0; NaN maps to 1, below the key of -inf (0x007FFFFF).  Key 0
+// marks a slot that is empty or already chosen.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (v != v) return 1u;
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// One wave ranks the E logits of one token and writes its k best experts and
+// their gates.  Lane l holds experts l, l+64, ...  Each round takes the
+// wave-wide maximum key (DPP), and among lanes holding it the lowest expert id,
+// then clears that entry.  Requires k <= E and all 64 lanes active.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, int lane,
+                          int32_t* __restrict__ idx_out, float* __restrict__ g_out) {
+  uint32_t keys[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    keys[i] = (e < E) ? order_key(lrow[e]) : 0u;
+  }
+  int my_e = 0;
+  float my_v = 0.f, v0 = 0.f, s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = 0;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (keys[i] > bk) { bk = keys[i]; bi = i; }  // strict: lower slot (lower id) wins ties
+    const uint32_t m = wave_max_u32(bk);
+    const uint64_t tied = __ballot(bk == m);
+    uint32_t e_win;
+    if (__popcll(tied) == 1) {
+      e_win = (uint32_t)__builtin_amdgcn_readlane(lane + kWave * bi,
+                                                  (int)(__ffsll((long long)tied) - 1));
+    } else {
+      e_win = wave_min_u32(bk == m ? (uint32_t)(lane + kWave * bi) : 0xFFFFFFFFu);
+    }
+    if ((int)(e_win & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (i == (int)(e_win >> 6)) keys[i] = 0u;
+    }
+    const float v = key_value(m);
+    if (j == 0) v0 = v;
+    s += expf(v - v0);  // softmax denominator, summed in rank order
+    if (j == lane) { my_e = (int)e_win; my_v = v; }
+  }
+  if (lane < k) {
+    idx_out[lane] = my_e;
+    g_out[lane] = expf(my_v - v0) / s;
+  }
+}
+
+}  // namespace moe_fp4

@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status codes
+before any HIP call.  The fake device addresses below are never dereferenced:
+every call here is built to fail validation, which happens on the host first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mxfp4_routed_expert_router_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_fp4_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
+              "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib._lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.status_string(s) and lib.status_string(s) != "unknown status"
+    assert lib.status_string(99) == "unknown status"
+
+
+def test_header_compiles_as_c(tmp_path):
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "moe_fp4.h"\nint main(void){moe_fp4_dims d={1,32,32,1,1};'
+                   'size_t b;return moe_fp4_workspace_size(&d,0,&b);}\n')
+    r = subprocess.run(["gcc", "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", "-c", str(src), "-o", str(tmp_path / "use.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+# --------------------------------------------------------------------------- validation
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def _weights(lib, **over):
+    w = lib.Weights()
+    for i, n in enumerate(lib.TENSORS):
+        setattr(w, n, over.get(n, FAKE + (i << 30)))
+    for i, s in enumerate(over.get("strides", (0,) * 6)):
+        w.expert_stride[i] = s
+    return w
+
+
+def _fwd(lib, dims=(4, 256, 128, 16, 2), x=FAKE, logits=FAKE, w=None, y=FAKE, mode=0, flags=0,
+         ws=FAKE, ws_bytes=None):
+    d = lib.Dims(*dims)
+    if w is None:
+        w = _weights(lib)
+    if ws_bytes is None:
+        n = ctypes.c_size_t()
+        rc = lib._lib.moe_fp4_workspace_size(ctypes.byref(d), mode, ctypes.byref(n))
+        ws_bytes = n.value if rc == 0 else 1 << 40
+    return lib._lib.moe_fp4_forward(ctypes.byref(d), x, logits, ctypes.byref(w), y, mode, flags, ws,
+                                    ws_bytes, None)
+
+
+def test_workspace_size(lib):
+    assert lib.moe_fp4_workspace_size(1, 5120, 2304, 384, 6) > 6 * 2304 * 2
+    pre = lib.moe_fp4_workspace_size(2048, 5120, 2304, 384, 6)
+    assert pre >= 12288 * 5120 * 4 + 12288 * 2304 * 2
+    assert lib.moe_fp4_workspace_size(8, 256, 128, 16, 2, lib.MODE_PREFILL) > \
+        lib.moe_fp4_workspace_size(8, 256, 128, 16, 2, lib.MODE_DECODE)
+    with pytest.raises(lib.MoeFp4Error) as e:
+        lib.moe_fp4_workspace_size(33, 256, 128, 16, 2, lib.MODE_DECODE)
+    assert e.value.status == lib.EUNSUPPORTED
+    n = ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(None, 0, ctypes.byref(n)) == lib.EINVAL
+
+
+def test_workspace_is_the_only_failure(lib):
+    # every other argument valid: the call stops at the workspace check
+    assert _fwd(lib, ws_bytes=0) == lib.EWORKSPACE
+    assert _fwd(lib, ws=0) == lib.EINVAL
+
+
+@pytest.mark.parametrize("field", ["x", "logits", "y"])
+def test_null_pointers(lib, field):
+    assert _fwd(lib, ws_bytes=0, **{field: 0}) == lib.EINVAL
+
+
+@pytest.mark.parametrize("name", ["w1", "s1", "w3", "s3", "w2", "s2"])
+def test_null_weights(lib, name):
+    assert _fwd(lib, ws_bytes=0, w=_weights(lib, **{name: 0})) == lib.EINVAL
+
+
+def test_null_dims(lib):
+    w = _weights(lib)
+    assert lib._lib.moe_fp4_forward(None, FAKE, FAKE, ctypes.byref(w), FAKE, 0, 0, FAKE, 0, None) \
+        == lib.EINVAL
+    assert lib._lib.moe_fp4_forward(ctypes.byref(lib.Dims(1, 32, 32, 1, 1)), FAKE, FAKE, None, FAKE,
+                                    0, 0, FAKE, 0, None) == lib.EINVAL
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((0, 256, 128, 16, 2), "EINVAL"),          # no tokens
+    ((4, 256, 128, 16, 0), "EINVAL"),          # k = 0
+    ((4, 256, 128, 2, 3), "EINVAL"),           # k > E
+    ((4, 250, 128, 16, 2), "EUNSUPPORTED"),    # H not a multiple of 32
+    ((4, 256, 100, 16, 2), "EUNSUPPORTED"),    # I not a multiple of 32
+    ((4, 256, 128, 2048, 2), "EUNSUPPORTED"),  # E > 1024
+    ((4, 256, 128, 64, 17), "EUNSUPPORTED"),   # k > 16
+    ((70000, 256, 128, 16, 2), "EUNSUPPORTED"),
+    ((4, 32768, 128, 16, 2), "EUNSUPPORTED"),
+])
+def test_bad_dims(lib, dims, code):
+    assert _fwd(lib, dims=dims, ws_bytes=0) == getattr(lib, code)
+
+
+def test_bad_mode_and_flags(lib):
+    assert _fwd(lib, mode=7, ws_bytes=0) == lib.EUNSUPPORTED
+    assert _fwd(lib, flags=2, ws_bytes=0) == lib.EUNSUPPORTED
+    assert _fwd(lib, dims=(33, 256, 128, 16, 2), mode=lib.MODE_DECODE, ws_bytes=0) == lib.EUNSUPPORTED
+    assert _fwd(lib, dims=(32, 256, 128, 16, 8), mode=lib.MODE_DECODE, ws_bytes=0) == lib.EUNSUPPORTED
+
+
+def test_negative_stride(lib):
+    assert _fwd(lib, w=_weights(lib, strides=(0, 0, 0, 0, -16, 0)), ws_bytes=0) == lib.EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(x=FAKE + 8), dict(y=FAKE + 4), dict(ws=FAKE + 64)])
+def test_misaligned(lib, kw):
+    assert _fwd(lib, ws_bytes=0, **kw) == lib.EALIGN
+
+
+@pytest.mark.parametrize("over", [dict(w1=FAKE + 8), dict(w3=FAKE + 1), dict(w2=FAKE + 4),
+                                  dict(strides=(65544, 0, 0, 0, 0, 0)),
+                                  dict(strides=(0, 0, 0, 0, 16392, 0))])
+def test_misaligned_weights(lib, over):
+    assert _fwd(lib, w=_weights(lib, **over), ws_bytes=0) == lib.EALIGN
+
+
+def test_scale_tensors_need_no_alignment(lib):
+    w = _weights(lib, s1=FAKE + 1, s3=FAKE + 3, s2=FAKE + 5, strides=(0, 7, 0, 9, 0, 11))
+    assert _fwd(lib, w=w, ws_bytes=0) == lib.EWORKSPACE
+
+
+def test_route_validation(lib):
+    r = lib.RouteOut()
+    for n in ("topk_idx", "gates", "counts", "offsets", "sorted_pairs", "pair_slot"):
+        setattr(r, n, FAKE)
+    f = lib._lib.moe_fp4_route
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), None, ctypes.byref(r), None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 20)), FAKE, ctypes.byref(r), None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 2000, 2)), FAKE, ctypes.byref(r), None) == lib.EUNSUPPORTED
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), FAKE + 2, ctypes.byref(r), None) == lib.EALIGN
+    r.gates = 0
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), FAKE, ctypes.byref(r), None) == lib.EINVAL
+
+
+def test_prenorm_validation(lib):
+    f = lib._lib.moe_fp4_prenorm_bf16
+    assert f(None, FAKE, 1, 64, 1e-6, None) == lib.EINVAL
+    assert f(FAKE, FAKE, 0, 64, 1e-6, None) == lib.EINVAL
+    assert f(FAKE, FAKE, 1, 48, 1e-6, None) == lib.EUNSUPPORTED

@@ -1,0 +1,280 @@
+"""GPU parity at small shapes: the HIP path against the CPU oracle, element by
+element, through the C-ABI.  Shapes span several tiles and ragged tails."""
+import numpy as np
+import pytest
+
+import pins
+from gpu_common import check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_routed_expert_router_amd as m
+    return m
+
+
+def _route_ref(orc, lg, k, E):
+    idx, g = orc.route(lg, k)
+    return idx, g, orc.permute(idx, E)
+
+
+def _gpu_route(moe, lg, k):
+    import torch
+    r = moe.moe_fp4_route(torch.from_numpy(np.ascontiguousarray(lg)).cuda(), k)
+    torch.cuda.synchronize()
+    return r
+
+
+# --------------------------------------------------------------------------- router
+ROUTE_CASES = [  # (T, E, k, seed)
+    (1, 1, 1, 0), (1, 384, 6, 1), (8, 16, 2, 2), (6, 384, 6, 3), (32, 384, 6, 4), (64, 384, 6, 5),
+    (65, 384, 6, 6), (2048, 384, 6, 7), (3, 1024, 16, 8), (100, 1024, 16, 9), (5, 16, 16, 10),
+    (3000, 7, 7, 11), (200, 138, 6, 12), (171, 64, 1, 13),
+]
+
+
+@pytest.mark.parametrize("T,E,k,seed", ROUTE_CASES)
+def test_route_random(moe, orc, T, E, k, seed):
+    say(f"route T={T} E={E} k={k}")
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx, g, perm = _route_ref(orc, lg, k, E)
+    check_route(_gpu_route(moe, lg, k), idx, g, perm, f"T={T} E={E} k={k}")
+
+
+def test_route_ties_zero_nan(moe, orc):
+    say("route ties / -0 / NaN / inf")
+    rng = np.random.default_rng(42)
+    T, E, k = 40, 100, 8
+    lg = np.round(rng.standard_normal((T, E)), 1).astype(np.float32)  # many exact ties
+    lg[0, :] = 0.5
+    lg[1, ::2] = -0.0
+    lg[1, 1::2] = 0.0
+    lg[2, 5] = np.nan
+    lg[2, 7] = np.inf
+    lg[2, 9] = -np.inf
+    lg[3, :] = np.nan
+    lg[4, :50] = -np.inf
+    idx, g, perm = _route_ref(orc, lg, k, E)
+    r = _gpu_route(moe, lg, k)
+    assert np.array_equal(r.topk_idx.cpu().numpy(), idx)
+    for name, ref in zip(("counts", "offsets", "sorted_pairs", "pair_slot"), perm):
+        assert np.array_equal(getattr(r, name).cpu().numpy(), ref), name
+    ok = np.isfinite(lg).all(axis=1) | (np.arange(T) > 4)
+    gg = r.gates.cpu().numpy()
+    assert np.max(np.abs(gg[ok] - g[ok])) <= 1e-6
+
+
+def test_route_repeatable(moe):
+    say("route twice, bitwise")
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((2048, 384)).astype(np.float32)
+    a, b = _gpu_route(moe, lg, 6), _gpu_route(moe, lg, 6)
+    for n in ("topk_idx", "gates", "counts", "offsets", "sorted_pairs", "pair_slot"):
+        assert np.array_equal(getattr(a, n).cpu().numpy(), getattr(b, n).cpu().numpy()), n
+
+
+# --------------------------------------------------------------------------- forward
+def decode_supported(moe, T, H, I, E, k):
+    try:
+        moe.moe_fp4_workspace_size(T, H, I, E, k, moe.MODE_DECODE)
+        return True
+    except moe.MoeFp4Error:
+        return False
+
+
+def _forward_case(moe, orc, T, H, I, E, k, seed, mode, scale_lo=120, scale_hi=124, accumulate=False):
+    import torch
+    rng = np.random.default_rng(seed)
+    experts = {e: pins.random_expert(rng, H, I, scale_lo, scale_hi) for e in range(E)}
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True)
+    dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
+    w = dev_weights(dense)
+    y0 = None
+    if accumulate:
+        y0 = rng.standard_normal((T, H)).astype(np.float32)
+        y_in = torch.from_numpy(y0).cuda()
+    else:
+        y_in = None
+    y, h, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k, y=y_in,
+                                            mode=mode, accumulate=accumulate)
+    torch.cuda.synchronize()
+    what = f"T={T} H={H} I={I} E={E} k={k} mode={mode}"
+    check_route(route, ref["idx"], ref["gates"], orc.permute(ref["idx"], E), what)
+    check_h(host_bits(h), ref["h"], ref["hpre"], ref["hbound"], what)
+    want = ref["y"] if y0 is None else (y0.astype(np.float64) + ref["y"]).astype(np.float32)
+    check_y(y.cpu().numpy(), want, what)
+
+
+FORWARD_CASES = [  # (T, H, I, E, k)
+    (8, 256, 128, 16, 2),     # the tiny workload's shape
+    (5, 352, 96, 7, 3),       # ragged: 11 input groups, 3 intermediate groups
+    (1, 32, 32, 1, 1),        # minimum
+    (3, 64, 32, 4, 4),        # k = E
+    (16, 512, 256, 24, 6),
+    (17, 224, 160, 9, 4),     # two decode token tiles
+    (32, 256, 192, 6, 6),     # every expert takes all 32 tokens
+    (16, 256, 128, 20, 2),    # a full 16-token decode tile
+]
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["decode", "prefill"])
+@pytest.mark.parametrize("T,H,I,E,k", FORWARD_CASES)
+def test_forward_small(moe, orc, T, H, I, E, k, mode):
+    if mode == 1 and not decode_supported(moe, T, H, I, E, k):
+        pytest.skip("shape outside the decode path's range")
+    say(f"forward T={T} H={H} I={I} E={E} k={k} mode={mode}")
+    _forward_case(moe, orc, T, H, I, E, k, seed=T * 7 + H + I, mode=mode)
+
+
+@pytest.mark.parametrize("T", [40, 130, 300])
+def test_forward_prefill_many_tokens(moe, orc, T):
+    say(f"forward prefill T={T}: experts with more than 64 tokens (several passes)")
+    _forward_case(moe, orc, T, 128, 96, 3, 2, seed=T, mode=2)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_forward_accumulate(moe, orc, mode):
+    say(f"forward accumulate mode={mode}")
+    _forward_case(moe, orc, 4, 256, 128, 8, 2, seed=5, mode=mode, accumulate=True)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_forward_scale_extremes(moe, orc, mode):
+    say(f"forward with scale bytes over the supported range, mode={mode}")
+    _forward_case(moe, orc, 3, 128, 64, 4, 2, seed=9, mode=mode, scale_lo=100, scale_hi=140)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_probes(moe, orc, mode):
+    """One-hot weights: pins nibble order, orientation and scale indexing on the GPU."""
+    import torch
+    H, I = 256, 128
+    for n0, c0, code, sc in [(0, 1, 7, 124), (I - 1, H - 1, 13, 120), (37, 64 + 33, 5, 130)]:
+        say(f"probe w1 n0={n0} c0={c0} mode={mode}")
+        ex = pins.const_expert(H, I, 0, 2, 2)
+        pins.set_nibble(ex["w1"], n0, c0, code)
+        ex["s1"][n0, c0 // 32] = sc
+        x = np.zeros((1, H), np.uint16)
+        x[0, c0] = pins.bf16_bits(1.5)
+        x[0, c0 ^ 1] = pins.bf16_bits(-0.625)
+        lg = np.zeros((1, 1), np.float32)
+        ref = orc.forward(H, I, 1, 1, x, lg, {0: ex}, want_h=True)
+        w = dev_weights({n: a[None] for n, a in ex.items()})
+        y, h, _ = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, 1, mode=mode)
+        torch.cuda.synchronize()
+        check_h(host_bits(h), ref["h"], ref["hpre"], ref["hbound"], "probe w1")
+        check_y(y.cpu().numpy(), ref["y"], "probe w1")
+    for m0, n0, code, sc in [(0, 0, 7, 124), (H - 1, I - 1, 13, 125), (3, 33, 5, 127)]:
+        say(f"probe w2 m0={m0} n0={n0} mode={mode}")
+        ex = pins.const_expert(H, I, 2, 2, 0)
+        pins.set_nibble(ex["w2"], m0, n0, code)
+        ex["s2"][m0, n0 // 32] = sc
+        x = np.zeros((1, H), np.uint16)
+        x[0, 0] = pins.bf16_bits(1.25)
+        lg = np.zeros((1, 1), np.float32)
+        ref = orc.forward(H, I, 1, 1, x, lg, {0: ex}, want_h=True)
+        w = dev_weights({n: a[None] for n, a in ex.items()})
+        y, h, _ = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, 1, mode=mode)
+        torch.cuda.synchronize()
+        yy = y.cpu().numpy()
+        assert np.array_equal(host_bits(h), ref["h"])
+        assert np.array_equal(yy, ref["y"]), (np.nonzero(yy)[1], np.nonzero(ref["y"])[1])
+
+
+def test_decode_and_prefill_agree(moe):
+    """Both paths on one input: routing identical, outputs within fp32 reordering."""
+    import torch
+    rng = np.random.default_rng(77)
+    T, H, I, E, k = 12, 512, 256, 20, 4
+    dense = {n: np.stack([pins.random_expert(rng, H, I)[n] for _ in range(E)])
+             for n in ("w1", "s1", "w3", "s3", "w2", "s2")}
+    w = dev_weights(dense)
+    x = dev_bits(pins.rand_bf16(rng, (T, H)))
+    lg = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).cuda()
+    y1 = moe.moe_fp4_forward(x, lg, w, k, mode=1)
+    y2 = moe.moe_fp4_forward(x, lg, w, k, mode=2)
+    torch.cuda.synchronize()
+    check_y(y1.cpu().numpy(), y2.cpu().numpy(), "decode vs prefill")
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_forward_repeatable(moe, mode):
+    """Same call twice gives bitwise the same y (no atomics-order dependence)."""
+    import torch
+    rng = np.random.default_rng(8)
+    T, H, I, E, k = 8, 256, 128, 16, 2
+    dense = {n: np.stack([pins.random_expert(rng, H, I)[n] for _ in range(E)])
+             for n in ("w1", "s1", "w3", "s3", "w2", "s2")}
+    w = dev_weights(dense)
+    x = dev_bits(pins.rand_bf16(rng, (T, H)))
+    lg = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).cuda()
+    a = moe.moe_fp4_forward(x, lg, w, k, mode=mode).cpu().numpy()
+    b = moe.moe_fp4_forward(x, lg, w, k, mode=mode).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_expert_blob_layout(moe, orc):
+    """Experts stored as one blob each (the six tensors back to back) via strides."""
+    import torch
+    rng = np.random.default_rng(19)
+    T, H, I, E, k = 4, 256, 128, 5, 2
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    sizes = [experts[0][n].size for n in names]
+    blob = sum(sizes) + 16 * 6
+    offs = []
+    o = 0
+    for s in sizes:
+        offs.append(o)
+        o += (s + 15) // 16 * 16
+    buf = np.zeros((E, (blob + 255) // 256 * 256), np.uint8)
+    for e in range(E):
+        for n, off, s in zip(names, offs, sizes):
+            buf[e, off:off + s] = experts[e][n].ravel()
+    dbuf = torch.from_numpy(buf).cuda()
+    stride = buf.shape[1]
+    views = {n: dbuf.view(-1)[off:] for n, off in zip(names, offs)}
+    w = moe.ExpertWeights(strides=(stride,) * 6, I=I, **views)
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ref = orc.forward(H, I, E, k, x, lg, experts)
+    y = moe.moe_fp4_forward(dev_bits(x), torch.from_numpy(lg).cuda(), w, k)
+    torch.cuda.synchronize()
+    check_y(y.cpu().numpy(), ref["y"], "blob layout")
+
+
+def test_prenorm(moe, orc):
+    import torch
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((6, 5120)) * 300).astype(np.float32)
+    u = moe.moe_fp4_prenorm_bf16(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    got = host_bits(u)
+    ref = orc.prenorm(x)
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= 1e-3 * diff.size
+
+
+def test_device_generator_matches_host(moe):
+    """The device weight generator writes the same bytes as the host generator."""
+    import torch
+    import synth
+    from synth.configs import TINY, DECODE
+    dev = synth.layer_device(TINY, layer=2)
+    host = synth.layer_host(TINY, layer=2)
+    for n in host:
+        assert np.array_equal(dev[n].cpu().numpy(), host[n]), n
+    dev = synth.layer_device(DECODE, layer=0, n_experts=3)
+    torch.cuda.synchronize()
+    for e in range(3):
+        h = synth.expert_host(DECODE, 0, e)
+        for n in h:
+            assert np.array_equal(dev[n][e].cpu().numpy(), h[n]), (e, n)
