@@ -18,7 +18,9 @@
  *            W[r][c] = E2M1(nibble) * 2^(scale - 127), the low nibble of a byte
  *            holding the even input.
  *   combine  y[t] = sum_j gates[t][j] * Y_(t, idx[t][j]), j ascending, fp32.
- * Accumulation is fp32 on MFMA; h is rounded to bf16 once, after silu(G)*U.
+ * Products of bf16 activations and decoded weights are exact in fp32 and are
+ * summed in fp32 (MFMA or v_dot2c_f32_bf16); h is rounded to bf16 once, after
+ * silu(G)*U.
  *
  * Conventions for every call:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -52,9 +54,14 @@ extern "C" {
 #define MOE_FP4_EHIP          5  /* a kernel launch failed (hipGetLastError)        */
 
 /* ---- forward modes */
-#define MOE_FP4_MODE_AUTO     0  /* DECODE when T <= 32, else PREFILL                */
-#define MOE_FP4_MODE_DECODE   1  /* split-K GEMV path; requires T <= 32              */
+#define MOE_FP4_MODE_AUTO     0  /* DECODE where it supports the dims, else PREFILL  */
+#define MOE_FP4_MODE_DECODE   1  /* GEMV path for a few tokens (see below)           */
 #define MOE_FP4_MODE_PREFILL  2  /* grouped-GEMM path; any T                         */
+/* DECODE supports T <= 16 (T <= 2 on row-contiguous dot kernels, more on MFMA
+ * kernels) as far as the T activation rows and the T*k h rows it stages in LDS
+ * fit 64 KiB; at H = 5120, I = 2304, k = 6 that is T <= 4.  I <= 3072 beyond
+ * two tokens.  moe_fp4_workspace_size(dims, MOE_FP4_MODE_DECODE, ...) returns
+ * MOE_FP4_EUNSUPPORTED outside that range. */
 
 /* ---- forward flags */
 #define MOE_FP4_ACCUMULATE    1  /* y += layer output (default: y = layer output)    */
@@ -120,7 +127,7 @@ int moe_fp4_route(const moe_fp4_dims *dims, const float *logits, moe_fp4_route_o
  *           MOE_FP4_ACCUMULATE
  *   ws      device workspace of at least moe_fp4_workspace_size(dims, mode)
  *           bytes, 256-byte aligned; its contents need no initialisation
- * Errors: EINVAL, EUNSUPPORTED (dims, unknown mode or flag, DECODE with T > 32),
+ * Errors: EINVAL, EUNSUPPORTED (dims, unknown mode or flag, DECODE outside its range),
  * EALIGN, EWORKSPACE, EHIP. */
 int moe_fp4_forward(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
                     const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,

@@ -34,7 +34,7 @@ int resolve_mode(const moe_fp4_dims& d, int mode) {
 
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
-  size_t idx, gates, counts, offsets, sorted, slot, dinfo, meta, h, ypair, total;
+  size_t idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h, ypair, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
@@ -47,6 +47,8 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   L.offsets = o;  o = align_up(o + (size_t)(d.E + 1) * 4);
   L.sorted = o;   o = align_up(o + P * 4);
   L.slot = o;     o = align_up(o + P * 4);
+  L.slot_gate = o; o = align_up(o + P * 4);
+  L.slot_tok = o; o = align_up(o + P * 4);
   L.dinfo = o;    o = align_up(o + (size_t)d.E * 16);
   L.meta = o;     o = align_up(o + 64);
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
@@ -105,8 +107,10 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   r.pair_slot = at<int32_t>(ws, L.slot);
   r.dinfo = at<int32_t>(ws, L.dinfo);
   r.meta = at<int32_t>(ws, L.meta);
+  r.slot_gate = at<float>(ws, L.slot_gate);
+  r.slot_tok = at<int32_t>(ws, L.slot_tok);
   // A one-token decode ranks the logits inside its first expert kernel.
-  const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.E);
+  const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.I, d.E, d.k);
   if (events) (void)hipEventRecord(events[0], stream);
   if (!fused && launch_route(r, stream) != hipSuccess) return MOE_FP4_EHIP;
   if (events) (void)hipEventRecord(events[1], stream);
@@ -118,6 +122,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   for (int i = 0; i < 6; ++i) a.stride[i] = stride[i];
   a.counts = r.counts; a.offsets = r.offsets; a.sorted_pairs = r.sorted_pairs;
   a.pair_slot = r.pair_slot; a.dinfo = r.dinfo; a.meta = r.meta; a.gates = r.gates;
+  a.slot_gate = r.slot_gate; a.slot_tok = r.slot_tok;
   a.h = at<uint16_t>(ws, L.h);
   a.ypair = rmode == MOE_FP4_MODE_PREFILL ? at<float>(ws, L.ypair) : nullptr;
   a.y = y;
@@ -175,7 +180,7 @@ int moe_fp4_route(const moe_fp4_dims* dims, const float* logits, moe_fp4_route_o
   r.T = d.T; r.E = d.E; r.k = d.k;
   r.idx = out->topk_idx; r.gates = out->gates; r.counts = out->counts; r.offsets = out->offsets;
   r.sorted_pairs = out->sorted_pairs; r.pair_slot = out->pair_slot;
-  r.dinfo = nullptr; r.meta = nullptr;
+  r.dinfo = nullptr; r.meta = nullptr; r.slot_gate = nullptr; r.slot_tok = nullptr;
   return launch_route(r, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
 }
 

@@ -22,6 +22,10 @@
 // Three to sixteen tokens (the MFMA kernels): the token rows become the 16
 // columns of a 16x16x32 bf16 MFMA whose other operand is 16 weight rows decoded
 // in registers; waves split the inputs (split-K) and meet in LDS.
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "topk.h"
@@ -34,11 +38,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kBPW = 5;  // MFMA path: weight blocks (4 scale groups each) per wave in one batch
 constexpr int kEB = 6;   // MFMA path: experts whose w2 loads are in flight together
 constexpr int kB2 = 3;   // MFMA path: w2 blocks per wave and expert (I <= 8 * 3 * 128)
-constexpr int kDJ13 = 5;  // dot path: load instructions per wave and batch, w1/w3
-constexpr int kDJ2 = 14;  // dot path: load instructions per wave and batch, w2
-constexpr int kDX = 4;    // dot path: activation chunks per thread loaded ahead of the weights
-constexpr int kDotMaxPairs = 32;   // dot path: token-expert pairs of a step (T <= 2, k <= 16)
-constexpr int kFusedVPL = 8;       // fused routing: logits per lane (E <= 512)
+constexpr int kFusedVPL = 8;  // one-token routing inside the w1/w3 kernel: logits per lane (E <= 512)
 
 __host__ __device__ constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -256,58 +256,77 @@ __global__ void __launch_bounds__(kThreads) gemv2_combine_kernel(LayerArgs a) {
   }
 }
 
-// =========================================================================== dot path
-// Activation rows in LDS for the dot kernels: each 32-input group (64 bytes)
-// takes an 80-byte slot.  Lane l reads group l, so lane addresses step by 20
-// dwords and a wave's 16-byte reads fall on every bank group evenly instead
-// of a quarter of them (a 64-byte step).
-constexpr int kGS = 40;  // bf16 per group slot
-__host__ __device__ constexpr int grp_row(int K) { return (K / 32) * kGS; }  // bf16 per row
-__device__ __forceinline__ int grp_chunk(int c) { return (c >> 2) * kGS + (c & 3) * 8; }
+// =========================================================================== one-token path
+// Lane l of a wave owns the 32-input groups g = l + 64 i (i < NXG) of the rows
+// it reads, and keeps the activations of those groups in registers for the
+// whole kernel: the weights are the only stream, and the inner loop is the FP4
+// decode (v_cvt_scalef32_pk_bf16_fp4) and the dot products (v_dot2c_f32_bf16,
+// bf16 products exact in fp32), with no LDS traffic and no per-chunk indexing.
 
-size_t lds13_dot_bytes(int T, int H) { return align256((size_t)T * grp_row(H) * 2); }
-size_t lds2_dot_bytes(int P, int I) {
-  return align256((size_t)P * grp_row(I) * 2) + (size_t)4 * kDotMaxPairs * 4;
+constexpr int kOneMaxXG = 4;      // x groups per lane: H <= 64 * 32 * 4
+constexpr int kOneMaxPL = 2;      // (slot, group) pairs per lane in the w2 kernel
+constexpr int kOneRowsMax = 64;   // w2 rows per workgroup
+constexpr int kOneDP = 8;         // w2 rows in flight per wave
+
+int one_xg(int H) { return (H / 32 + kWave - 1) / kWave; }
+int one_pl(int I, int k) {
+  const int pw = (k * (I / 32) + kWaves - 1) / kWaves;
+  return (pw + kWave - 1) / kWave;
+}
+bool one_token_fits(int H, int I, int k) {
+  return one_xg(H) <= kOneMaxXG && one_pl(I, k) <= kOneMaxPL;
 }
 
-// One token: rank the logits (every workgroup does, redundantly) and take
-// this workgroup's expert, the d-th smallest id among the k chosen (each
-// chosen expert holds exactly one pair, so its sorted slot is d).  Workgroup
-// (0, 0) publishes the routing result for the later kernels.
-__device__ DInfo fused_route(const LayerArgs& a, int d, int* s_e, float* s_g, int* s_sorted,
-                             int* s_rank) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Routing of the token in LDS: the k chosen experts by ascending id (slot d),
+// with their gates.
+struct OneTables {
+  int de[kMaxK];
+  float gate[kMaxK];
+};
+
+// Rank the logits in wave 0 (every workgroup does, redundantly).  Each chosen
+// expert holds exactly one pair, so the expert of rank j sits in sorted slot
+// (number of chosen ids below it).  Workgroup 0 publishes the routing result.
+__device__ void route_one(const LayerArgs& a, OneTables& tb) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int k = a.k, E = a.E;
   if (tid < kWave) {
-    wave_topk<kFusedVPL>(a.logits, E, k, lane, s_e, s_g);
-    // rank of each chosen id among the chosen (they are distinct)
-    const int my_e = lane < k ? s_e[lane] : 0x7FFFFFFF;
+    int my_e;
+    float my_g;
+    wave_topk_regs<kFusedVPL>(a.logits, E, k, lane, my_e, my_g);
+    const int key = lane < k ? my_e : 0x7FFFFFFF;
     int rank = 0;
-    for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(my_e, i) < my_e ? 1 : 0;
+    for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(key, i) < key ? 1 : 0;
     if (lane < k) {
-      s_sorted[rank] = my_e;
-      s_rank[lane] = rank;
+      tb.de[rank] = my_e;
+      tb.gate[rank] = my_g;
+      if (blockIdx.x == 0) {
+        const RouteArgs& r = a.route;
+        r.idx[lane] = my_e;
+        r.gates[lane] = my_g;
+        r.sorted_pairs[rank] = lane;
+        r.pair_slot[lane] = rank;
+        r.slot_gate[rank] = my_g;
+        r.slot_tok[rank] = 0;
+        r.dinfo[4 * rank + 0] = my_e;
+        r.dinfo[4 * rank + 1] = rank;
+        r.dinfo[4 * rank + 2] = 1;
+        r.dinfo[4 * rank + 3] = 0;
+      }
     }
   }
   lds_barrier();
-  const int e = s_sorted[d];
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  if (blockIdx.x == 0) {
     const RouteArgs& r = a.route;
-    if (tid < k) {
-      const int rank = s_rank[tid];
-      r.idx[tid] = s_e[tid];
-      r.gates[tid] = s_g[tid];
-      r.sorted_pairs[rank] = tid;
-      r.pair_slot[tid] = rank;
-      r.dinfo[4 * rank + 0] = s_e[tid];
-      r.dinfo[4 * rank + 1] = rank;
-      r.dinfo[4 * rank + 2] = 1;
-      r.dinfo[4 * rank + 3] = 0;
-    }
     for (int x = tid; x < E; x += kThreads) {
       int below = 0;
-      while (below < k && s_sorted[below] < x) ++below;
-      r.counts[x] = (below < k && s_sorted[below] == x) ? 1 : 0;
+      while (below < k && tb.de[below] < x) ++below;
+      r.counts[x] = (below < k && tb.de[below] == x) ? 1 : 0;
       r.offsets[x] = below;
     }
     if (tid == 0) {
@@ -315,311 +334,294 @@ __device__ DInfo fused_route(const LayerArgs& a, int d, int* s_e, float* s_g, in
       r.meta[0] = k;
     }
   }
-  return DInfo{e, d, 1};
 }
 
-template <int NT>
-__global__ void __launch_bounds__(kThreads) gemv13_dot_kernel(LayerArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_e[kMaxK], s_sorted[kMaxK], s_rank[kMaxK];
-  __shared__ float s_g[kMaxK];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int H = a.H, CPR = H / 32, C2 = 2 * CPR, XS = grp_row(H), C8 = H / 8;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+// G and U for every (chosen expert, row) unit.  The grid is persistent (what
+// is resident at once); wave w of the grid takes units w, w + W, w + 2W, ...
+// and keeps the next unit's loads in flight while it computes the current one.
+// A unit is one row of w1 and the same row of w3: NXG load instructions each
+// (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
+template <int NXG>
+__global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
+  __shared__ OneTables tb;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = uniform(tid / kWave);
+  const int H = a.H, I = a.I, CPR = H / 32;
 
-  DInfo di;
-  if (NT == 1 && a.fused_route) {
-    // the token is row 0: its x loads need no routing and go out first
-    u32x4 xr[kDX];
+  // this lane's x groups (clamped to the last group past the row end; their
+  // values are zeroed below, so the duplicate chunk adds exactly nothing)
+  int gc[NXG];
+  u32x4 xr[NXG][4];
 #pragma unroll
-    for (int q = 0; q < kDX; ++q) {
-      const int i = tid + q * kThreads;
-      xr[q] = ld16(a.x + (size_t)(i < C8 ? i : 0) * 8);
-    }
-    di = fused_route(a, blockIdx.y, s_e, s_g, s_sorted, s_rank);
+  for (int i = 0; i < NXG; ++i) {
+    const int g = lane + kWave * i;
+    gc[i] = g < CPR ? g : CPR - 1;
 #pragma unroll
-    for (int q = 0; q < kDX; ++q) {
-      const int i = tid + q * kThreads;
-      if (i < C8) st16(xs + grp_chunk(i), xr[q]);
-    }
-    for (int i = tid + kDX * kThreads; i < C8; i += kThreads)
-      st16(xs + grp_chunk(i), ld16(a.x + (size_t)i * 8));
+    for (int q = 0; q < 4; ++q) xr[i][q] = ld16(a.x + (size_t)gc[i] * 32 + 8 * q);
+  }
+  if (a.fused_route) {
+    route_one(a, tb);
   } else {
-    di = load_dinfo(a.dinfo, blockIdx.y);
-    if (di.e < 0) return;
+    if (tid < a.k) {
+      tb.de[tid] = a.dinfo[4 * tid];
+      tb.gate[tid] = a.slot_gate[tid];
+    }
+    lds_barrier();
   }
-  const int e = di.e, off = di.off, ne = di.ne;
-  const int r = blockIdx.x * 16 + 2 * w;  // this wave's first row
-  const uint8_t* w1b = a.w1 + (size_t)e * a.stride[0] + (size_t)r * (H / 2);
-  const uint8_t* w3b = a.w3 + (size_t)e * a.stride[2] + (size_t)r * (H / 2);
-  const uint8_t* s1b = a.s1 + (size_t)e * a.stride[1] + (size_t)r * CPR;
-  const uint8_t* s3b = a.s3 + (size_t)e * a.stride[3] + (size_t)r * CPR;
+  bf16x8 X[NXG][4];
+#pragma unroll
+  for (int i = 0; i < NXG; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) X[i][q] = as_bf16x8(sel4(lane + kWave * i < CPR, xr[i][q]));
 
-  // Unfused: x rows of this expert's tokens.  Their loads go out before the
-  // weight loads so that waiting for them never waits for the weight stream.
-  int trow[NT];
-  u32x4 xr[kDX];
-  const bool stage = !(NT == 1 && a.fused_route);
-  if (stage) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) trow[t] = a.sorted_pairs[off + (t < ne ? t : 0)] / a.k;
-#pragma unroll
-    for (int q = 0; q < kDX; ++q) {
-      const int i = tid + q * kThreads;
-      const bool ok = i < ne * C8;
-      const int ii = ok ? i : 0, n = ii / C8, c = ii - n * C8;
-      int t = trow[0];
-#pragma unroll
-      for (int u = 1; u < NT; ++u) t = n == u ? trow[u] : t;
-      xr[q] = ld16(a.x + (size_t)t * H + c * 8);
-    }
-  }
+  const int nunits = a.k * I;
+  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
+  const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;  // units of this wave
+  if (F == 0) return;
+  const int wbytes = I * (H / 2), sbytes = I * CPR;
 
-  float a1[NT][2], a3[NT][2];
+  struct Unit {
+    u32x4 q1[NXG], q3[NXG];
+    uint32_t s1[NXG], s3[NXG];
+  };
+  auto issue = [&](int f, Unit& B) {
+    const int u = wid + f * nw, d = u / I, r = u - d * I;
+    const int e = uniform(tb.de[d]);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
+    const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
+    const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
+    const __amdgpu_buffer_rsrc_t q3 = rsrc(a.s3 + (size_t)e * a.stride[3], sbytes);
+    const int ow = r * (H / 2), os = r * CPR;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) a1[t][0] = a1[t][1] = a3[t][0] = a3[t][1] = 0.f;
-  for (int c0 = 0; c0 < C2; c0 += kDJ13 * kWave) {
-    u32x4 q1[kDJ13], q3[kDJ13];
-    uint32_t e1[kDJ13], e3[kDJ13];
-#pragma unroll
-    for (int j = 0; j < kDJ13; ++j) {
-      const int c = c0 + j * kWave + lane;
-      const bool ok = c < C2;
-      const int cc = ok ? c : 0;
-      q1[j] = sel4(ok, ld16(w1b + (size_t)cc * 16));
-      q3[j] = sel4(ok, ld16(w3b + (size_t)cc * 16));
-      const uint32_t x1 = s1b[cc], x3 = s3b[cc];
-      e1[j] = ok ? x1 : 0u;
-      e3[j] = ok ? x3 : 0u;
+    for (int i = 0; i < NXG; ++i) {
+      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, gc[i] * 16, ow, 0));
+      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, gc[i] * 16, ow, 0));
+      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, gc[i], os, 0);
+      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, gc[i], os, 0);
     }
-    if (c0 == 0) {
-      if (stage) {
+  };
+  auto compute = [&](int f, const Unit& B) {
+    const int u = wid + f * nw, d = u / I, r = u - d * I;
+    float G = 0.f, U = 0.f;
 #pragma unroll
-        for (int q = 0; q < kDX; ++q) {
-          const int i = tid + q * kThreads;
-          if (i < ne * C8) {
-            const int n = i / C8, c = i - n * C8;
-            st16(xs + n * XS + grp_chunk(c), xr[q]);
-          }
-        }
-      }
-      lds_barrier();
-    }
+    for (int i = 0; i < NXG; ++i) {
+      const float c1 = ue8m0_to_f32(B.s1[i]), c3 = ue8m0_to_f32(B.s3[i]);
 #pragma unroll
-    for (int j = 0; j < kDJ13; ++j) {
-      const int c = c0 + j * kWave + lane;
-      const int rl = c >= CPR ? 1 : 0;
-      const int g = c < C2 ? c - rl * CPR : 0;
-      const float sc1 = ue8m0_to_f32(e1[j]), sc3 = ue8m0_to_f32(e3[j]);
-      float p1[NT], p3[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) p1[t] = p3[t] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 A1 = fp4x8_to_bf16x8(q1[j][i], sc1);
-        const bf16x8 A3 = fp4x8_to_bf16x8(q3[j][i], sc3);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x8 X = as_bf16x8(ld16(xs + t * XS + g * kGS + 8 * i));
-          p1[t] = dot8_bf16(A1, X, p1[t]);
-          p3[t] = dot8_bf16(A3, X, p3[t]);
-        }
-      }
-      if (c < C2) {  // a lane past the end adds nothing (not even 0 * inf)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (rl) { a1[t][1] += p1[t]; a3[t][1] += p3[t]; }
-          else { a1[t][0] += p1[t]; a3[t][0] += p3[t]; }
-        }
+      for (int q = 0; q < 4; ++q) {
+        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), X[i][q], G);
+        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), X[i][q], U);
       }
     }
+    G = wave_sum_f32(G);
+    U = wave_sum_f32(U);
+    if (lane == 0) a.h[(size_t)d * I + r] = swiglu_bf16(G, U);
+  };
+
+  // Two register buffers; the loop body has no conditional loads, so each wait
+  // is for the older buffer only and the next unit stays in flight.  The
+  // scheduling barriers keep the compiler from sinking a unit's loads below
+  // the computation they are meant to overlap.
+  Unit A, B;
+  issue(0, A);
+  int f = 0;
+  for (; f + 2 < F; f += 2) {
+    issue(f + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f, A);
+    issue(f + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f + 1, B);
   }
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int rl = 0; rl < 2; ++rl) {
-      const float G = wave_sum_f32(a1[t][rl]), U = wave_sum_f32(a3[t][rl]);
-      if (lane == 0 && t < ne) a.h[(size_t)(off + t) * a.I + r + rl] = swiglu_bf16(G, U);
-    }
+  if (F - f == 2) {
+    issue(f + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f, A);
+    compute(f + 1, B);
+  } else {
+    compute(f, A);
+  }
 }
 
-// y rows m, m+1 of this wave for the step's tokens: sum over the distinct
-// experts of gate * (w2 row . h row), chunk by chunk, then one DPP reduction.
-// Chunk c of the wave enumerates (expert d, row, 32-input group) with d major;
-// a load instruction spans at most two experts, whose ids are read with
-// scalar loads.
-template <int NT, int KH>
-__global__ void __launch_bounds__(kThreads) gemv2_dot_kernel(LayerArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int P = a.T * a.k;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int I = a.I, CPR = I / 32, C2 = 2 * CPR, IS = grp_row(I), C8 = I / 8;
-  const int m = blockIdx.x * 16 + 2 * w;  // this wave's first output row
-  const int nd = a.meta[0];
-  uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
-  float* s_gate = reinterpret_cast<float*>(smem + align256((size_t)P * IS * 2));  // per slot
-  int* s_tok = reinterpret_cast<int*>(s_gate + kDotMaxPairs);
-  int* s_off = s_tok + kDotMaxPairs;  // per distinct expert
-  int* s_ne = s_off + kDotMaxPairs;
+// y rows [m0, m1) of this workgroup: every (slot, group) pair of the step's
+// k chosen experts is owned by one lane of one wave (its 32 h values held in
+// registers), so each w2 row costs each wave NPL 16-byte loads per lane; the
+// lane sums gate * (chunk . h), the wave reduces with DPP, and the 8 wave
+// partials of a row are added in a fixed order.  No atomics: y is bitwise
+// reproducible.
+template <int NPL>
+__global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
+  __shared__ float part[kWaves][kOneRowsMax];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = uniform(tid / kWave);
+  const int H = a.H, I = a.I, CPR = I / 32;
+  const int NP = a.k * CPR, PW = (NP + kWaves - 1) / kWaves;
+  const int R = (H + gridDim.x - 1) / gridDim.x, m0 = blockIdx.x * R;
+  const int m1 = min(H, m0 + R);
+  if (m0 >= H) return;  // whole workgroup
 
-  // h rows (all pairs of the step, sorted order): loads first
-  u32x4 hr[KH];
+  const uint8_t* wp[NPL];
+  const uint8_t* sp[NPL];
+  float gt[NPL];
+  bf16x8 Hv[NPL][4];
+  {
+    int ev[NPL], sl[NPL], gg[NPL];
+    u32x4 hr[NPL][4];
 #pragma unroll
-  for (int q = 0; q < KH; ++q) {
-    const int i = tid + q * kThreads;
-    hr[q] = ld16(a.h + (size_t)(i < P * C8 ? i : 0) * 8);
-  }
-  const int total = nd * C2;
-  float acc[NT][2];
+    for (int j = 0; j < NPL; ++j) {
+      const int p = w * PW + lane + kWave * j;
+      const int pc = (lane + kWave * j < PW && p < NP) ? p : 0;
+      sl[j] = pc / CPR;
+      gg[j] = pc - sl[j] * CPR;
+      ev[j] = a.dinfo[4 * sl[j]];
+      gt[j] = a.slot_gate[sl[j]];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = 0.f;
-  for (int c0 = 0; c0 < total; c0 += kDJ2 * kWave) {
-    u32x4 q[kDJ2];
-    uint32_t ev[kDJ2];
-#pragma unroll
-    for (int j = 0; j < kDJ2; ++j) {
-      const int cb = c0 + j * kWave;  // uniform
-      const int c = cb + lane;
-      const bool ok = c < total;
-      int e, cr;
-      if (C2 >= kWave) {  // uniform: the instruction spans at most two experts
-        const int dlo = min(cb / C2, nd - 1);
-        const int dhi = min(dlo + 1, nd - 1);
-        const int elo = a.dinfo[4 * dlo], ehi = a.dinfo[4 * dhi];
-        const bool hi = c >= (dlo + 1) * C2;
-        e = hi ? ehi : elo;
-        cr = ok ? c - (hi ? dhi : dlo) * C2 : 0;
-      } else {            // narrow w2 rows: look the expert up per lane
-        const int cc = ok ? c : 0, dd = cc / C2;
-        e = a.dinfo[4 * dd];
-        cr = cc - dd * C2;
-      }
-      q[j] = sel4(ok, ld16(a.w2 + (size_t)e * a.stride[4] + (size_t)m * (I / 2) + (size_t)cr * 16));
-      const uint32_t x = a.s2[(size_t)e * a.stride[5] + (size_t)m * CPR + cr];
-      ev[j] = ok ? x : 0u;
-    }
-    if (c0 == 0) {
-#pragma unroll
-      for (int qq = 0; qq < KH; ++qq) {
-        const int i = tid + qq * kThreads;
-        if (i < P * C8) {
-          const int n = i / C8, c = i - n * C8;
-          st16(hs + n * IS + grp_chunk(c), hr[qq]);
-        }
-      }
-      for (int i = tid + KH * kThreads; i < P * C8; i += kThreads) {
-        const int n = i / C8, c = i - n * C8;
-        st16(hs + n * IS + grp_chunk(c), ld16(a.h + (size_t)i * 8));
-      }
-      for (int s = tid; s < P; s += kThreads) {
-        const int p = a.sorted_pairs[s];
-        s_gate[s] = a.gates[p];
-        s_tok[s] = p / a.k;
-      }
-      for (int dd = tid; dd < nd; dd += kThreads) {
-        const DInfo di = load_dinfo(a.dinfo, dd);
-        s_off[dd] = di.off;
-        s_ne[dd] = di.ne;
-      }
-      lds_barrier();
+      for (int q = 0; q < 4; ++q) hr[j][q] = ld16(a.h + (size_t)sl[j] * I + gg[j] * 32 + 8 * q);
     }
 #pragma unroll
-    for (int j = 0; j < kDJ2; ++j) {
-      const int cb = c0 + j * kWave;  // uniform
-      const int c = cb + lane;
-      const bool ok = c < total;
-      const int cc = ok ? c : 0;
-      int dd;
-      if (C2 >= kWave) {  // same bracketing as the loads
-        const int dlo = min(cb / C2, nd - 1);
-        dd = cc >= (dlo + 1) * C2 ? dlo + 1 : dlo;
-      } else {
-        dd = cc / C2;
-      }
-      const int cr = cc - dd * C2;
-      const int rl = cr >= CPR ? 1 : 0;
-      const int g = cr - rl * CPR;
-      const int off = s_off[dd], nex = s_ne[dd];
-      const float sc = ue8m0_to_f32(ev[j]);
-      bf16x8 A[4];
+    for (int j = 0; j < NPL; ++j) {
+      const int p = w * PW + lane + kWave * j;
+      const bool ok = lane + kWave * j < PW && p < NP;
+      wp[j] = a.w2 + (size_t)ev[j] * a.stride[4] + gg[j] * 16;
+      sp[j] = a.s2 + (size_t)ev[j] * a.stride[5] + gg[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = fp4x8_to_bf16x8(q[j][i], sc);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        if (ok && u < nex) {
-          const int s = off + u;
-          float p = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p = dot8_bf16(A[i], as_bf16x8(ld16(hs + s * IS + g * kGS + 8 * i)), p);
-          const float gp = s_gate[s] * p;
-          const int t = s_tok[s];
-#pragma unroll
-          for (int tt = 0; tt < NT; ++tt)
-            if (t == tt) {
-              if (rl) acc[tt][1] += gp; else acc[tt][0] += gp;
-            }
-        }
-      }
+      for (int q = 0; q < 4; ++q) Hv[j][q] = as_bf16x8(sel4(ok, hr[j][q]));
     }
   }
+
+  const size_t wrow = I / 2;
+  u32x4 qb[kOneDP][NPL];
+  uint32_t sb[kOneDP][NPL];
+  auto load = [&](int b, int m) {
+    const int mc = m < m1 ? m : m1 - 1;  // past the end: a row already loaded
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int rl = 0; rl < 2; ++rl) {
-      const float Y = wave_sum_f32(acc[t][rl]);
-      if (lane == 0 && t < a.T) {
-        float* yp = a.y + (size_t)t * a.H + m + rl;
-        *yp = a.accumulate ? *yp + Y : Y;
-      }
+    for (int j = 0; j < NPL; ++j) {
+      qb[b][j] = ld16(wp[j] + (size_t)mc * wrow);
+      sb[b][j] = sp[j][(size_t)mc * CPR];
     }
+  };
+  // loads complete in issue order: issue the ring in the order it is consumed
+#pragma unroll
+  for (int b = 0; b < kOneDP; ++b) {
+    load(b, m0 + b);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int m = m0; m < m1; m += kOneDP) {
+#pragma unroll
+    for (int b = 0; b < kOneDP; ++b) {
+      if (m + b < m1) {
+        float p = 0.f;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+          const float sc = ue8m0_to_f32(sb[b][j]);
+          float t = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t = dot8_bf16(fp4x8_to_bf16x8(qb[b][j][q], sc), Hv[j][q], t);
+          p += gt[j] * t;
+        }
+        p = wave_sum_f32(p);
+        if (lane == 0) part[w][m + b - m0] = p;
+      }
+      load(b, m + b + kOneDP);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  lds_barrier();
+  if (tid < m1 - m0) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) s += part[q][tid];
+    float* yp = a.y + m0 + tid;
+    *yp = a.accumulate ? *yp + s : s;
+  }
 }
 
-// One or two tokens take the row-contiguous kernels (x staged ahead of the
-// weights needs T * H <= 8 * kDX * kThreads); up to 16, the MFMA kernels.
-bool use_dot(int T, int H) { return T <= 2 && T * (H / 8) <= kDX * kThreads; }
+// Workgroups of `kernel` (kThreads threads, `lds` bytes of dynamic LDS) that the
+// current device holds at once, and its compute units.  Cached per (device,
+// kernel, lds).
+struct Residency {
+  int wgs, cus;
+};
+Residency residency(const void* kernel, size_t lds) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    size_t lds;
+    Residency r;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Residency{0, 0};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& x : cache)
+      if (x.dev == dev && x.kernel == kernel && x.lds == lds) return x.r;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return Residency{0, 0};
+  const Residency r{cus * per_cu, cus};
+  std::lock_guard<std::mutex> lock(mu);
+  cache.push_back(Entry{dev, kernel, lds, r});
+  return r;
+}
+
+template <int NXG>
+const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NXG>); }
+
+hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
+  const hipEvent_t* ev = a.stage_events;
+  const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
+  const void* k13 = nxg == 1 ? k13_one<1>() : nxg == 2 ? k13_one<2>() : nxg == 3 ? k13_one<3>()
+                                                                             : k13_one<4>();
+  const Residency res = residency(k13, 0);
+  if (res.wgs <= 0) return hipErrorInvalidValue;
+  const int units = a.k * a.I;
+  const dim3 blk(kThreads), g13(std::min(res.wgs, (units + kWaves - 1) / kWaves));
+  switch (nxg) {
+    case 1: hipLaunchKernelGGL(gemv13_one_kernel<1>, g13, blk, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(gemv13_one_kernel<2>, g13, blk, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(gemv13_one_kernel<3>, g13, blk, 0, stream, a); break;
+    default: hipLaunchKernelGGL(gemv13_one_kernel<4>, g13, blk, 0, stream, a); break;
+  }
+  if (ev) (void)hipEventRecord(ev[0], stream);
+  // w2: one workgroup per compute unit, at most kOneRowsMax rows each
+  const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
+  const dim3 g2(n2);
+  if (npl == 1)
+    hipLaunchKernelGGL(gemv2_one_kernel<1>, g2, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemv2_one_kernel<2>, g2, blk, 0, stream, a);
+  return hipSuccess;
+}
 
 }  // namespace
 
 bool decode_fits(int T, int H, int I, int k) {
+  if (T == 1 && one_token_fits(H, I, k)) return true;
   const int P = T * k;
-  if (use_dot(T, H))
-    return P <= kDotMaxPairs && lds13_dot_bytes(T, H) <= kDecodeLds &&
-           lds2_dot_bytes(P, I) <= kDecodeLds;
   return T <= kDecodeMaxTokens && I <= kWaves * kB2 * 128 && lds13_bytes(T, H) <= kDecodeLds &&
          lds2_bytes(P, I) <= kDecodeLds;
 }
 
-bool decode_fuses_route(int T, int H, int E) {
-  return T == 1 && use_dot(T, H) && E <= kFusedVPL * kWave;
+bool decode_fuses_route(int T, int H, int I, int E, int k) {
+  return T == 1 && one_token_fits(H, I, k) && E <= kFusedVPL * kWave;
 }
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream) {
   const int P = a.T * a.k;
-  const int dmax = P < a.E ? P : a.E;  // distinct experts can not exceed either
   const hipEvent_t* ev = a.stage_events;
-  const dim3 blk(kThreads), g13(a.I / 16, dmax), g2(a.H / 16);
-  if (!use_dot(a.T, a.H)) {
+  if (a.T == 1 && one_token_fits(a.H, a.I, a.k)) {
+    const hipError_t e = launch_one(a, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    const int dmax = P < a.E ? P : a.E;  // distinct experts can not exceed either
+    const dim3 blk(kThreads), g13(a.I / 16, dmax), g2(a.H / 16);
     hipLaunchKernelGGL(gemv13_kernel, g13, blk, lds13_bytes(a.T, a.H), stream, a);
     if (ev) (void)hipEventRecord(ev[0], stream);
     hipLaunchKernelGGL(gemv2_combine_kernel, g2, blk, lds2_bytes(P, a.I), stream, a);
-  } else {
-    const size_t l13 = lds13_dot_bytes(a.T, a.H), l2 = lds2_dot_bytes(P, a.I);
-    const bool small_h = P * (a.I / 8) <= 4 * kThreads;
-    if (a.T == 1) {
-      hipLaunchKernelGGL(gemv13_dot_kernel<1>, g13, blk, l13, stream, a);
-      if (ev) (void)hipEventRecord(ev[0], stream);
-      if (small_h)
-        hipLaunchKernelGGL((gemv2_dot_kernel<1, 4>), g2, blk, l2, stream, a);
-      else
-        hipLaunchKernelGGL((gemv2_dot_kernel<1, 8>), g2, blk, l2, stream, a);
-    } else {
-      hipLaunchKernelGGL(gemv13_dot_kernel<2>, g13, blk, l13, stream, a);
-      if (ev) (void)hipEventRecord(ev[0], stream);
-      if (small_h)
-        hipLaunchKernelGGL((gemv2_dot_kernel<2, 4>), g2, blk, l2, stream, a);
-      else
-        hipLaunchKernelGGL((gemv2_dot_kernel<2, 8>), g2, blk, l2, stream, a);
-    }
   }
   if (ev) {
     (void)hipEventRecord(ev[1], stream);

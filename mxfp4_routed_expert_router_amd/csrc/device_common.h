@@ -42,9 +42,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// silu(g) * u in fp32, then one rounding to bf16.
+// silu(g) * u in fp32, then one rounding to bf16.  silu(g) = g * sigmoid(g).
+// For g < 0 the exponential is taken of g itself (never overflows), and below
+// g = -64 of g + 64 (exact for g >= -128), the product being multiplied by
+// fp32(e^-64) at the end: e^g would otherwise be an fp32 subnormal with few
+// significant bits while silu(g) * u can still be a normal bf16 (|u| is large
+// when the scales are).  The relative error stays within a few fp32 ulps.
 __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
-  return f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
+  constexpr float kExpM64 = 0x1.969d48p-93f;   // e^-64 rounded to fp32
+  if (g >= 0.0f) return f32_to_bf16_rne(g / (1.0f + expf(-g)) * u);
+  const bool deep = g < -64.0f;
+  const float e = expf(deep ? g + 64.0f : g);  // e^g, times e^64 when deep
+  const float s = deep ? e : e / (1.0f + e);   // sigmoid(g) (1 + e^g rounds to 1 when deep)
+  const float h = (g * s) * u;
+  return f32_to_bf16_rne(deep ? h * kExpM64 : h);
 }
 
 // 16x16x32 bf16 MFMA: D[i][j] += sum_k A[i][k] B[k][j].  Lane l supplies

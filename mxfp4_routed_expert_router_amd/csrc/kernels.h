@@ -18,6 +18,9 @@ struct RouteArgs {
   int T, E, k;
   int32_t *idx, *counts, *offsets, *sorted_pairs, *pair_slot, *dinfo, *meta;  // dinfo: per distinct expert {id, first sorted slot, pairs, 0}
   float* gates;
+  // optional (forward path): per sorted slot, the pair's gate and token
+  float* slot_gate;
+  int32_t* slot_tok;
 };
 
 // Weights and routing state shared by the expert kernels.
@@ -28,6 +31,8 @@ struct LayerArgs {
   int64_t stride[6];  // resolved byte strides between experts
   const int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *dinfo, *meta;  // dinfo: per distinct expert {id, first sorted slot, pairs, 0}
   const float* gates;
+  const float* slot_gate;   // [T*k] gate of the pair in each sorted slot
+  const int32_t* slot_tok;  // [T*k] token of the pair in each sorted slot
   uint16_t* h;   // [T*k][I] bf16, rows in sorted (by-expert) order
   float* ypair;  // [T*k][H] fp32 gate-scaled expert outputs, sorted order (prefill only)
   float* y;      // [T][H]
@@ -42,7 +47,7 @@ struct LayerArgs {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 bool decode_fits(int T, int H, int I, int k);  // shapes the decode kernels take
-bool decode_fuses_route(int T, int H, int E);  // decode computes the routing in its first kernel
+bool decode_fuses_route(int T, int H, int I, int E, int k);  // decode routes in its first kernel
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);

@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_kernel(LayerArgs a) {
         const int tok = 16 * nt + c16;
         if (act[rt] && tok < nc) {
           const int s = off + c0 + tok;
-          const float gate = a.gates[a.sorted_pairs[s]];
+          const float gate = a.slot_gate[s];
           const f32x4 v = acc[0][rt][nt];
           const float4 o = {gate * v[0], gate * v[1], gate * v[2], gate * v[3]};
           *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;

@@ -79,10 +79,13 @@ __device__ void block_excl_scan_e(int (&vals)[kMaxExperts / NTH], int* s_wsum, i
 // inside a chunk a pair's position is base[e] + (pairs of e in earlier waves of
 // the chunk) + (pairs of e in earlier lanes of its wave), so the result is the
 // stable order whatever the timing of the LDS atomics in the histogram.
+// With `slot_gate` non-null, also writes per sorted slot the pair's gate
+// (read from `gsrc`, LDS or global) and token (pair id / k).
 template <int NTH>
-__device__ void block_permute(const int32_t* idx, int P, int E, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* dinfo,
-                              int32_t* meta, PermSmem<NTH>& sm) {
+__device__ void block_permute(const int32_t* idx, int P, int E, int k, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot,
+                              int32_t* dinfo, int32_t* meta, const float* gsrc, float* slot_gate,
+                              int32_t* slot_tok, PermSmem<NTH>& sm) {
   constexpr int NW = NTH / kWave, PER = kMaxExperts / NTH;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   for (int e = tid; e < kMaxExperts; e += NTH) {
@@ -147,6 +150,10 @@ __device__ void block_permute(const int32_t* idx, int P, int E, int32_t* counts,
       for (int q = 0; q < w; ++q) pos += sm.wcnt[q][e];
       sorted_pairs[pos] = p;
       pair_slot[p] = pos;
+      if (slot_gate) {
+        slot_gate[pos] = gsrc[p];
+        slot_tok[pos] = p / k;
+      }
     }
     lds_barrier();
     if (c0 + NTH < P) {  // advance the per-expert bases for the next chunk
@@ -168,8 +175,9 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermLdsPairs = 16384;  // expert ids staged in LDS up to this many pairs
 
 __global__ void __launch_bounds__(kPermThreads)
-permute_kernel(const int32_t* __restrict__ idx, int P, int E, int32_t* counts, int32_t* offsets,
-               int32_t* sorted_pairs, int32_t* pair_slot, int32_t* dinfo, int32_t* meta) {
+permute_kernel(const int32_t* __restrict__ idx, const float* __restrict__ gates, int P, int E,
+               int k, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot,
+               int32_t* dinfo, int32_t* meta, float* slot_gate, int32_t* slot_tok) {
   __shared__ PermSmem<kPermThreads> sm;
   __shared__ int32_t s_idx[kPermLdsPairs];
   const int32_t* src = idx;
@@ -178,8 +186,8 @@ permute_kernel(const int32_t* __restrict__ idx, int P, int E, int32_t* counts, i
     lds_barrier();
     src = s_idx;
   }
-  block_permute<kPermThreads>(src, P, E, counts, offsets, sorted_pairs, pair_slot, dinfo, meta,
-                              sm);
+  block_permute<kPermThreads>(src, P, E, k, counts, offsets, sorted_pairs, pair_slot, dinfo, meta,
+                              gates, slot_gate, slot_tok, sm);
 }
 
 // Small batches: top-k and permutation in one launch of 256 threads.  The four
@@ -190,7 +198,8 @@ template <int VPL>
 __global__ void __launch_bounds__(kSmallThreads)
 route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* idx,
                    float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
-                   int32_t* pair_slot, int32_t* dinfo, int32_t* meta) {
+                   int32_t* pair_slot, int32_t* dinfo, int32_t* meta, float* slot_gate,
+                   int32_t* slot_tok) {
   __shared__ PermSmem<kSmallThreads> sm;
   __shared__ int32_t s_idx[kSmallRoutePairs];
   __shared__ float s_g[kSmallRoutePairs];
@@ -203,8 +212,8 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_
     idx[p] = s_idx[p];
     gates[p] = s_g[p];
   }
-  block_permute<kSmallThreads>(s_idx, P, E, counts, offsets, sorted_pairs, pair_slot, dinfo,
-                               meta, sm);
+  block_permute<kSmallThreads>(s_idx, P, E, k, counts, offsets, sorted_pairs, pair_slot, dinfo,
+                               meta, s_g, slot_gate, slot_tok, sm);
 }
 
 int vpl_for(int E) {
@@ -221,7 +230,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
 #define MOE_ROUTE_SMALL(V)                                                                       \
   hipLaunchKernelGGL(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, a.logits,  \
                      a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets, a.sorted_pairs,        \
-                     a.pair_slot, a.dinfo, a.meta)
+                     a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok)
     switch (vpl) {
       case 1: MOE_ROUTE_SMALL(1); break;
       case 2: MOE_ROUTE_SMALL(2); break;
@@ -245,8 +254,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
       default: MOE_TOPK(16); break;
     }
 #undef MOE_TOPK
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, a.idx, P, a.E,
-                       a.counts, a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta);
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, a.idx, a.gates, P,
+                       a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta,
+                       a.slot_gate, a.slot_tok);
   }
   return hipGetLastError();
 }

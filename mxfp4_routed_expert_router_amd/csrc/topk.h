@@ -23,13 +23,13 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-// One wave ranks the E logits of one token and writes its k best experts and
-// their gates.  Lane l holds experts l, l+64, ...  Each round takes the
+// One wave ranks the E logits of one token; lane j < k receives the expert of
+// rank j and its gate.  Lane l holds experts l, l+64, ...  Each round takes the
 // wave-wide maximum key (DPP), and among lanes holding it the lowest expert id,
 // then clears that entry.  Requires k <= E and all 64 lanes active.
 template <int VPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, int lane,
-                          int32_t* __restrict__ idx_out, float* __restrict__ g_out) {
+__device__ __forceinline__ void wave_topk_regs(const float* __restrict__ lrow, int E, int k,
+                                               int lane, int& e_out, float& g_out) {
   uint32_t keys[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -63,9 +63,20 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E,
     s += expf(v - v0);  // softmax denominator, summed in rank order
     if (j == lane) { my_e = (int)e_win; my_v = v; }
   }
+  e_out = my_e;
+  g_out = expf(my_v - v0) / s;
+}
+
+// As wave_topk_regs, writing the k experts and gates to idx_out / g_out.
+template <int VPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, int lane,
+                                          int32_t* __restrict__ idx_out, float* __restrict__ g_out) {
+  int e;
+  float g;
+  wave_topk_regs<VPL>(lrow, E, k, lane, e, g);
   if (lane < k) {
-    idx_out[lane] = my_e;
-    g_out[lane] = expf(my_v - v0) / s;
+    idx_out[lane] = e;
+    g_out[lane] = g;
   }
 }
 
