@@ -32,6 +32,8 @@ METRIC = "FP4 MoE layer: decode µs/token (HBM GB/s) & 2048-tok prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 SPIN_CYCLES = 200_000_000       # head start for the host to enqueue profiled steps
+# the one-token decode kernels (w1/w3 with the routing inside; w2 with the combine inside)
+DECODE_KERNELS = {"w13": "gemv13_one_kernel", "w2": "gemv2_one_kernel"}
 
 
 def log(*a):
@@ -51,10 +53,38 @@ def decode_bytes(wl, idx):
     H, I, T, k = wl.H, wl.I, wl.T, wl.k
     D = len(np.unique(idx))
     P = T * k
+    broute = T * wl.E * 4 + P * 4 * 4
     b13 = D * 2 * (I * H // 2 + I * H // 32) + T * H * 2 + P * I * 2
     b2 = D * (H * I // 2 + H * I // 32) + P * I * 2 + T * H * 4
-    broute = T * wl.E * 4 + P * 4 * 4
+    if T == 1:  # the routing runs inside the w1/w3 kernel
+        b13, broute = b13 + broute, 0
     return {"route": broute, "w13": b13, "w2": b2, "D": D}
+
+
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "moe_layer_decode_T1_prefill_T2048_hbm_traffic.md")
+
+
+def profiled_traffic(kernel):
+    """HBM bytes (read + written) per launch of `kernel` from the committed
+    rocprofv3 PMC summary (FETCH_SIZE / WRITE_SIZE scaled by a device-copy
+    calibration), or None when the library sources differ from the ones the
+    counters were taken with."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic_json: "))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line[len("traffic_json: "):])
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mxfp4_routed_expert_router_amd",
+                        "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if h.hexdigest()[:16] != rec["src_sha256_16"] or kernel not in rec["kernels"]:
+        return None
+    k = rec["kernels"][kernel]
+    return float(k["read_bytes"] + k["write_bytes"])
 
 
 def main():
@@ -126,9 +156,10 @@ def main():
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
 
-    # Kernel durations: HIP events recorded between the layer's kernels on its
-    # stream.  The steps are enqueued behind a spin kernel so that they are all
-    # queued before the first one runs and execute back to back, as in the graph.
+    # Kernel durations: each kernel's dispatch records a start and an end event
+    # on the layer's stream (moe_fp4_forward_profiled).  The steps are enqueued
+    # behind a spin kernel so that they are all queued before the first one runs
+    # and execute back to back, as in the graph.
     evs = [moe.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(SPIN_CYCLES)
@@ -136,7 +167,7 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
-    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[4]) / args.steps
+    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[-1]) / args.steps
     stage = np.array([e.stage_ms() for e in evs])  # [steps, 4]: route, w13, w2, combine
     k_ms = {"route": float(stage[:, 0].mean()), "w13": float(stage[:, 1].mean()),
             "w2": float(stage[:, 2].mean())}
@@ -147,7 +178,7 @@ def main():
     dom = max(("w13", "w2"), key=lambda n: k_ms[n])
     achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
     log(f"decode: {us_tok:.2f} us/token graph replay ({step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s "
-        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us between stage events); kernels route "
+        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us per step with timed dispatches); kernels route "
         f"{k_ms['route'] * 1e3:.2f} us, w1/w3 {k_ms['w13'] * 1e3:.2f} us, "
         f"w2+combine {k_ms['w2'] * 1e3:.2f} us")
     eager_t0 = time.perf_counter()
@@ -174,7 +205,7 @@ def main():
             step(args.warmup + i, evc[i])
         torch.cuda.synchronize()
         st = np.array([e.stage_ms() for e in evc])
-        tot = st[:, :3].sum(1)
+        tot = st[:, 1:3].sum(1)  # w1/w3 (routing inside) + w2 (combine inside)
         cold = {"us_per_token": float(tot.mean() * 1e3),
                 "w13_us": float(st[:, 1].mean() * 1e3), "w2_us": float(st[:, 2].mean() * 1e3),
                 "w13_GBps": float(k_bytes["w13"] / (st[:, 1].mean() * 1e-3) / 1e9),
@@ -256,14 +287,16 @@ def main():
                    "T": wl.T, "E": wl.E, "k": wl.k, "H": wl.H, "I": wl.I},
         "tokens_per_s": 1e3 / ms_per_step * wl.T,
         "hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": {"w13": "gemv13_kernel", "w2": "gemv2_combine_kernel"}[dom],
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNELS[dom],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": profiled_traffic(DECODE_KERNELS[dom]), "traffic_unit": "bytes/launch",
                      "bytes_per_launch": k_bytes[dom], "avg_us": k_ms[dom] * 1e3},
         "kernels_us": {n: round(v * 1e3, 3) for n, v in k_ms.items()},
         "timing": "value: HIP graph of all steps, replayed once (wall clock); kernel durations: "
-                  "HIP events recorded between the layer's kernels on its stream, steps queued "
-                  "back to back",
+                  "start/end events recorded by each kernel's own dispatch on the layer's "
+                  "stream, steps queued back to back; one-token routing runs inside the w1/w3 "
+                  "kernel and its bytes (logits) are counted there",
         "us_per_token_with_events": ms_per_step_prof * 1e3 / wl.T,
         "us_per_token_eager": us_eager,
         "cold": cold,

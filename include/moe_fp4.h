@@ -141,14 +141,16 @@ int moe_fp4_forward_debug(const moe_fp4_dims *dims, const uint16_t *x, const flo
                           size_t ws_bytes, hipStream_t stream, uint16_t *h_out,
                           moe_fp4_route_out *route_out);
 
-/* As moe_fp4_forward, and records HIP events on `stream` at the stage
- * boundaries, for timing each kernel of the layer on the stream it runs on:
- *   events[0] before routing            events[1] after routing
- *   events[2] after the w1/w3 stage     events[3] after the w2 stage
- *   events[4] after the combine (PREFILL; in DECODE the combine is fused into
- *             the w2 stage and events[4] is recorded right after events[3]).
- * `events` holds n_events >= 5 events created by the caller.
- * Errors: as moe_fp4_forward, and EINVAL for null events or n_events < 5. */
+/* As moe_fp4_forward, and times the kernels of each stage on `stream`.
+ * Stage s is 0 routing, 1 w1/w3, 2 w2, 3 combine; the dispatch of the stage's
+ * first kernel records events[2s] when it starts and the dispatch of its last
+ * kernel records events[2s+1] when it ends (hipExtLaunchKernel), so
+ * hipEventElapsedTime(events[2s], events[2s+1]) is kernel time without launch
+ * gaps.  A stage that has no kernel of its own has both events recorded
+ * together: routing for one token in DECODE (it runs inside the w1/w3 kernel)
+ * and the combine in DECODE (inside the w2 kernel).
+ * `events` holds n_events >= 8 events created by the caller.
+ * Errors: as moe_fp4_forward, and EINVAL for null events or n_events < 8. */
 int moe_fp4_forward_profiled(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
                              const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
                              size_t ws_bytes, hipStream_t stream, hipEvent_t *events,

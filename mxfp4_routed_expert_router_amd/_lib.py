@@ -225,24 +225,30 @@ def moe_fp4_forward_debug(x, logits, weights: ExpertWeights, k: int, y=None, mod
 
 
 class StageEvents:
-    """Five HIP events for moe_fp4_forward_profiled (created with timing on)."""
+    """Eight HIP events for moe_fp4_forward_profiled (created with timing on):
+    start and end of the kernels of routing, w1/w3, w2 and combine."""
+
+    N = 8
 
     def __init__(self):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(self.N)]
         for e in self.events:
             e.record()  # materialise the underlying hipEvent_t
-        self._arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in self.events])
+        self._arr = (ctypes.c_void_p * self.N)(*[e.cuda_event for e in self.events])
 
     def stage_ms(self):
-        """Elapsed ms of route, w1/w3 stage, w2 stage, combine (after a sync)."""
+        """Kernel ms of routing, w1/w3, w2, combine (after a sync)."""
         ev = self.events
-        return [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+        return [ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(4)]
+
+    def span_ms(self):
+        """ms from the start of routing to the end of the combine."""
+        return self.events[0].elapsed_time(self.events[-1])
 
 
 def moe_fp4_forward_profiled(x, logits, weights: ExpertWeights, k: int, events: StageEvents,
                              y=None, mode=MODE_AUTO, accumulate=False, workspace=None):
-    """As moe_fp4_forward, recording `events` at the stage boundaries on the
-    stream the kernels run on."""
+    """As moe_fp4_forward, timing the kernels of each stage with `events`."""
     T, H = x.shape
     E = logits.shape[1]
     I = weights.intermediate()
@@ -255,7 +261,7 @@ def moe_fp4_forward_profiled(x, logits, weights: ExpertWeights, k: int, events: 
     _check(_lib.moe_fp4_forward_profiled(
         ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(), logits.data_ptr(), ctypes.byref(ws),
         y.data_ptr(), mode, ACCUMULATE if accumulate else 0, workspace.data_ptr(),
-        workspace.numel(), _stream(x), events._arr, 5), "moe_fp4_forward_profiled")
+        workspace.numel(), _stream(x), events._arr, events.N), "moe_fp4_forward_profiled")
     return y
 
 

@@ -111,9 +111,11 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   r.slot_tok = at<int32_t>(ws, L.slot_tok);
   // A one-token decode ranks the logits inside its first expert kernel.
   const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.I, d.E, d.k);
-  if (events) (void)hipEventRecord(events[0], stream);
-  if (!fused && launch_route(r, stream) != hipSuccess) return MOE_FP4_EHIP;
-  if (events) (void)hipEventRecord(events[1], stream);
+  r.ev = events;
+  if (fused)
+    ev_empty(events, 0, stream);  // routing runs inside the w1/w3 kernel
+  else if (launch_route(r, stream) != hipSuccess)
+    return MOE_FP4_EHIP;
 
   LayerArgs a{};
   a.T = d.T; a.H = d.H; a.I = d.I; a.E = d.E; a.k = d.k;
@@ -127,7 +129,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   a.ypair = rmode == MOE_FP4_MODE_PREFILL ? at<float>(ws, L.ypair) : nullptr;
   a.y = y;
   a.accumulate = (flags & MOE_FP4_ACCUMULATE) ? 1 : 0;
-  a.stage_events = events ? events + 2 : nullptr;
+  a.ev = events;
   a.fused_route = fused ? 1 : 0;
   a.route = r;
   a.logits = logits;
@@ -195,8 +197,8 @@ int moe_fp4_forward_profiled(const moe_fp4_dims* dims, const uint16_t* x, const 
                              const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
                              size_t ws_bytes, hipStream_t stream, hipEvent_t* events,
                              int n_events) {
-  if (!events || n_events < 5) return MOE_FP4_EINVAL;
-  for (int i = 0; i < 5; ++i)
+  if (!events || n_events < 2 * kStages) return MOE_FP4_EINVAL;
+  for (int i = 0; i < 2 * kStages; ++i)
     if (!events[i]) return MOE_FP4_EINVAL;
   return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, nullptr, nullptr,
                       events);

@@ -572,7 +572,7 @@ template <int NXG>
 const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NXG>); }
 
 hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
-  const hipEvent_t* ev = a.stage_events;
+  const hipEvent_t* ev = a.ev;
   const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
   const void* k13 = nxg == 1 ? k13_one<1>() : nxg == 2 ? k13_one<2>() : nxg == 3 ? k13_one<3>()
                                                                              : k13_one<4>();
@@ -580,20 +580,20 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
   if (res.wgs <= 0) return hipErrorInvalidValue;
   const int units = a.k * a.I;
   const dim3 blk(kThreads), g13(std::min(res.wgs, (units + kWaves - 1) / kWaves));
+  const hipEvent_t e0 = ev_start(ev, 1), e1 = ev_stop(ev, 1);
   switch (nxg) {
-    case 1: hipLaunchKernelGGL(gemv13_one_kernel<1>, g13, blk, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(gemv13_one_kernel<2>, g13, blk, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(gemv13_one_kernel<3>, g13, blk, 0, stream, a); break;
-    default: hipLaunchKernelGGL(gemv13_one_kernel<4>, g13, blk, 0, stream, a); break;
+    case 1: launch_k(gemv13_one_kernel<1>, g13, blk, 0, stream, e0, e1, a); break;
+    case 2: launch_k(gemv13_one_kernel<2>, g13, blk, 0, stream, e0, e1, a); break;
+    case 3: launch_k(gemv13_one_kernel<3>, g13, blk, 0, stream, e0, e1, a); break;
+    default: launch_k(gemv13_one_kernel<4>, g13, blk, 0, stream, e0, e1, a); break;
   }
-  if (ev) (void)hipEventRecord(ev[0], stream);
   // w2: one workgroup per compute unit, at most kOneRowsMax rows each
   const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
   const dim3 g2(n2);
   if (npl == 1)
-    hipLaunchKernelGGL(gemv2_one_kernel<1>, g2, blk, 0, stream, a);
+    launch_k(gemv2_one_kernel<1>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   else
-    hipLaunchKernelGGL(gemv2_one_kernel<2>, g2, blk, 0, stream, a);
+    launch_k(gemv2_one_kernel<2>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   return hipSuccess;
 }
 
@@ -612,21 +612,19 @@ bool decode_fuses_route(int T, int H, int I, int E, int k) {
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream) {
   const int P = a.T * a.k;
-  const hipEvent_t* ev = a.stage_events;
+  const hipEvent_t* ev = a.ev;
   if (a.T == 1 && one_token_fits(a.H, a.I, a.k)) {
     const hipError_t e = launch_one(a, stream);
     if (e != hipSuccess) return e;
   } else {
     const int dmax = P < a.E ? P : a.E;  // distinct experts can not exceed either
     const dim3 blk(kThreads), g13(a.I / 16, dmax), g2(a.H / 16);
-    hipLaunchKernelGGL(gemv13_kernel, g13, blk, lds13_bytes(a.T, a.H), stream, a);
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(gemv2_combine_kernel, g2, blk, lds2_bytes(P, a.I), stream, a);
+    launch_k(gemv13_kernel, g13, blk, lds13_bytes(a.T, a.H), stream, ev_start(ev, 1), ev_stop(ev, 1),
+             a);
+    launch_k(gemv2_combine_kernel, g2, blk, lds2_bytes(P, a.I), stream, ev_start(ev, 2),
+             ev_stop(ev, 2), a);
   }
-  if (ev) {
-    (void)hipEventRecord(ev[1], stream);
-    (void)hipEventRecord(ev[2], stream);
-  }
+  ev_empty(ev, 3, stream);  // the combine is part of the w2 kernels here
   return hipGetLastError();
 }
 

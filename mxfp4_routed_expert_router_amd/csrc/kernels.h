@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI layer (api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,6 +14,29 @@ constexpr int kSmallRoutePairs = 1024;
 constexpr int kDecodeMaxTokens = 16;   // decode GEMV: one 16-token MFMA tile per expert
 constexpr size_t kDecodeLds = 65536;   // LDS budget of each decode kernel (x / h rows staged whole)
 
+// Optional kernel timing.  `ev` holds 2 events per stage (0 route, 1 w1/w3,
+// 2 w2, 3 combine): the dispatch of the stage's first kernel records ev[2s]
+// when it starts and that of its last kernel ev[2s+1] when it ends, so the
+// elapsed time is kernel time only.  A stage without a kernel of its own has
+// both events recorded together.
+constexpr int kStages = 4;
+inline hipEvent_t ev_start(const hipEvent_t* ev, int stage) { return ev ? ev[2 * stage] : nullptr; }
+inline hipEvent_t ev_stop(const hipEvent_t* ev, int stage) { return ev ? ev[2 * stage + 1] : nullptr; }
+inline void ev_empty(const hipEvent_t* ev, int stage, hipStream_t s) {
+  if (ev) {
+    (void)hipEventRecord(ev[2 * stage], s);
+    (void)hipEventRecord(ev[2 * stage + 1], s);
+  }
+}
+template <typename K, typename... Args>
+inline void launch_k(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t start,
+                     hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
 struct RouteArgs {
   const float* logits;
   int T, E, k;
@@ -21,6 +45,7 @@ struct RouteArgs {
   // optional (forward path): per sorted slot, the pair's gate and token
   float* slot_gate;
   int32_t* slot_tok;
+  const hipEvent_t* ev;  // optional stage timing (see ev_start)
 };
 
 // Weights and routing state shared by the expert kernels.
@@ -37,7 +62,7 @@ struct LayerArgs {
   float* ypair;  // [T*k][H] fp32 gate-scaled expert outputs, sorted order (prefill only)
   float* y;      // [T][H]
   int accumulate;
-  const hipEvent_t* stage_events;  // optional: recorded after each expert-stage kernel
+  const hipEvent_t* ev;  // optional stage timing (see ev_start)
   // one-token decode: the first expert kernel ranks the logits itself and
   // publishes the routing result (no separate routing launch)
   int fused_route;

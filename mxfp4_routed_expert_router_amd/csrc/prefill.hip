@@ -296,14 +296,12 @@ unsigned xcd_grid(int n) { return (unsigned)(((n + 7) / 8) * 8); }
 
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
   const dim3 blk(kThreads);
-  const hipEvent_t* ev = a.stage_events;
+  const hipEvent_t* ev = a.ev;
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
-  hipLaunchKernelGGL(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[0], stream);
-  hipLaunchKernelGGL(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream, a);
-  if (ev) (void)hipEventRecord(ev[2], stream);
+  launch_k(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, ev_start(ev, 1), ev_stop(ev, 1), a);
+  launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+  launch_k(combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream, ev_start(ev, 3),
+           ev_stop(ev, 3), a);
   return hipGetLastError();
 }
 

@@ -228,9 +228,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int vpl = vpl_for(a.E);
   if (a.T <= kSmallRouteTokens && P <= kSmallRoutePairs) {
 #define MOE_ROUTE_SMALL(V)                                                                       \
-  hipLaunchKernelGGL(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, a.logits,  \
-                     a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets, a.sorted_pairs,        \
-                     a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok)
+  launch_k(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, ev_start(a.ev, 0),    \
+           ev_stop(a.ev, 0), a.logits, a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets,       \
+           a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok)
     switch (vpl) {
       case 1: MOE_ROUTE_SMALL(1); break;
       case 2: MOE_ROUTE_SMALL(2); break;
@@ -244,7 +244,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
     const int wpb = 4;
     const dim3 grid((a.T + wpb - 1) / wpb), block(wpb * kWave);
 #define MOE_TOPK(V) \
-  hipLaunchKernelGGL(topk_kernel<V>, grid, block, 0, stream, a.logits, a.T, a.E, a.k, a.idx, a.gates)
+  launch_k(topk_kernel<V>, grid, block, 0, stream, ev_start(a.ev, 0), (hipEvent_t) nullptr, \
+           a.logits, a.T, a.E, a.k, a.idx, a.gates)
     switch (vpl) {
       case 1: MOE_TOPK(1); break;
       case 2: MOE_TOPK(2); break;
@@ -254,9 +255,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
       default: MOE_TOPK(16); break;
     }
 #undef MOE_TOPK
-    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, a.idx, a.gates, P,
-                       a.E, a.k, a.counts, a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta,
-                       a.slot_gate, a.slot_tok);
+    launch_k(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, (hipEvent_t) nullptr,
+             ev_stop(a.ev, 0), (const int32_t*)a.idx, (const float*)a.gates, P, a.E, a.k, a.counts,
+             a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok);
   }
   return hipGetLastError();
 }

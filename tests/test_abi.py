@@ -176,3 +176,17 @@ def test_prenorm_validation(lib):
     assert f(None, FAKE, 1, 64, 1e-6, None) == lib.EINVAL
     assert f(FAKE, FAKE, 0, 64, 1e-6, None) == lib.EINVAL
     assert f(FAKE, FAKE, 1, 48, 1e-6, None) == lib.EUNSUPPORTED
+
+
+def test_profiled_needs_eight_events(lib):
+    """Stage timing takes a start and an end event for each of the four stages."""
+    d = lib.Dims(4, 256, 128, 16, 2)
+    w = _weights(lib)
+    n = ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == lib.OK
+    fake_events = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    args = (ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), FAKE, 0, 0, FAKE, n.value, None)
+    assert lib._lib.moe_fp4_forward_profiled(*args, None, 8) == lib.EINVAL
+    assert lib._lib.moe_fp4_forward_profiled(*args, fake_events, 7) == lib.EINVAL
+    fake_events[3] = None
+    assert lib._lib.moe_fp4_forward_profiled(*args, fake_events, 8) == lib.EINVAL
