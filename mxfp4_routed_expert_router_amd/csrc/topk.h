@@ -30,12 +30,17 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 template <int VPL>
 __device__ __forceinline__ void wave_topk_regs(const float* __restrict__ lrow, int E, int k,
                                                int lane, int& e_out, float& g_out) {
-  uint32_t keys[VPL];
+  // The loads are unconditional (a clamped index, the value discarded past E):
+  // inside a branch each one would be waited for before the next is issued.
+  float vals[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    keys[i] = (e < E) ? order_key(lrow[e]) : 0u;
+    vals[i] = lrow[e < E ? e : E - 1];
   }
+  uint32_t keys[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) keys[i] = (lane + kWave * i < E) ? order_key(vals[i]) : 0u;
   int my_e = 0;
   float my_v = 0.f, v0 = 0.f, s = 0.f;
   for (int j = 0; j < k; ++j) {
