@@ -40,6 +40,11 @@ constexpr int kPF13 = 3;                  // K blocks in flight per wave, w1/w3 
 constexpr int kPF2 = 4;                   // K blocks in flight per wave, w2 pass
 constexpr int kXC = (kTok * kKB / 8) / kThreads;  // 16-byte activation chunks per thread, block
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 struct Smem {
   uint16_t xs[2][kTok][kXS];
   int row[kTok];
@@ -55,46 +60,54 @@ __device__ __forceinline__ bool xcd_tile(int n, int& logical) {
   return slot < per && logical < n;
 }
 
-// One pass over all K for up to kTok staged token rows (sm.row[n] for n < nc,
+// One pass over all K for up to NT*16 staged token rows (sm.row[n] for n < nc,
 // row length ld in src): acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].
 // M weight matrices share the activation tile.  Row tiles with act[rt] false
-// load nothing (their rows lie past the end) but the wave still takes part in
-// the staging and the barriers.
-template <int M, int kPF, int kRT>
+// read a valid chunk they do not use (scale 0) but the wave still takes part
+// in the staging and the barriers.  NT (16-token column tiles) is a template
+// argument so that the MFMA loop has no branches: a branch around MFMAs makes
+// the compiler copy the accumulators at every join.
+template <int M, int kPF, int kRT, int NT>
 __device__ __forceinline__ void gemm_pass(Smem& sm, const uint8_t* const (&wr)[M][kRT],
                                           const uint8_t* const (&sr)[M][kRT], const bool (&act)[kRT],
                                           const uint16_t* __restrict__ src, int ld, int nc, int K,
-                                          f32x4 (&acc)[M][kRT][kNT]) {
+                                          f32x4 (&acc)[M][kRT][NT]) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int c16 = lane & 15, kb = lane >> 4;
   const int NG = K / 32, NB = (K + kKB - 1) / kKB;
-  const int ntile = (nc + 15) / 16;
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 q[kPF][M][kRT];
   uint32_t sv[kPF][M][kRT];
   u32x4 xv[kPF][kXC];
   // Every load is issued unconditionally from an address that is always valid
-  // (out-of-range blocks, rows or tokens read row 0 / token 0 / block 0) and
-  // its value is zeroed afterwards.  With no branches around the loads the
-  // compiler counts outstanding loads exactly and waits only for the oldest.
+  // (out-of-range blocks, rows or tokens read row 0 / token 0 / block 0), and
+  // validity is applied where the value is used: a weight chunk past the end
+  // gets scale 0 (every E2M1 code times 0 is 0), an activation chunk past the
+  // end is stored to LDS as zeros.  A select on a loaded register right after
+  // its load would make the compiler wait for it there (and at the loop's back
+  // edge), draining the prefetch; with no branches and no selects around the
+  // loads each wait is for the oldest block only.
+  auto w_ok = [&](int b, int rt) { return b < NB && act[rt] && 4 * b + kb < NG; };
+  auto x_ok = [&](int b, int u) {
+    const int id = tid + u * kThreads;
+    const int n = id / (kKB / 8), c = id % (kKB / 8);
+    return b < NB && n < nc && b * kKB + c * 8 < K;
+  };
   auto issue_w = [&](int b, int s) {
     const int g = 4 * b + kb;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const bool ok = b < NB && act[rt] && g < NG;
-        const int gg = ok ? g : 0;
-        const u32x4 v = ld16(wr[m][rt] + (size_t)gg * 16);
-        const uint32_t e8 = sr[m][rt][gg];
-        q[s][m][rt] = sel4(ok, v);
-        sv[s][m][rt] = ok ? e8 : 0u;
+        const int gg = w_ok(b, rt) ? g : 0;
+        q[s][m][rt] = ld16(wr[m][rt] + (size_t)gg * 16);
+        sv[s][m][rt] = sr[m][rt][gg];
       }
   };
   auto issue_x = [&](int b, int s) {
@@ -102,26 +115,24 @@ __device__ __forceinline__ void gemm_pass(Smem& sm, const uint8_t* const (&wr)[M
     for (int u = 0; u < kXC; ++u) {
       const int id = tid + u * kThreads;
       const int n = id / (kKB / 8), c = id % (kKB / 8);
-      const int kk = b * kKB + c * 8;
-      const bool ok = b < NB && n < nc && kk < K;
-      const u32x4 v = ld16(src + (size_t)sm.row[ok ? n : 0] * ld + (ok ? kk : 0));
-      xv[s][u] = sel4(ok, v);
+      const bool ok = x_ok(b, u);
+      xv[s][u] = ld16(src + (size_t)sm.row[ok ? n : 0] * ld + (ok ? b * kKB + c * 8 : 0));
     }
   };
-  auto write_x = [&](int s, int buf) {
+  auto write_x = [&](int s, int buf, int b) {
 #pragma unroll
     for (int u = 0; u < kXC; ++u) {
       const int id = tid + u * kThreads;
       const int n = id / (kKB / 8), c = id % (kKB / 8);
-      st16(&sm.xs[buf][n][c * 8], xv[s][u]);
+      st16(&sm.xs[buf][n][c * 8], sel4(x_ok(b, u), xv[s][u]));
     }
   };
-  auto compute = [&](int s, int buf) {
+  auto compute = [&](int s, int buf, int b) {
     float sc[M][kRT];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) sc[m][rt] = ue8m0_to_f32(sv[s][m][rt]);
+      for (int rt = 0; rt < kRT; ++rt) sc[m][rt] = w_ok(b, rt) ? ue8m0_to_f32(sv[s][m][rt]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf16x8 A[M][kRT];
@@ -130,14 +141,12 @@ __device__ __forceinline__ void gemm_pass(Smem& sm, const uint8_t* const (&wr)[M
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) A[m][rt] = fp4x8_to_bf16x8(q[s][m][rt][i], sc[m][rt]);
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        if (nt < ntile) {
-          const bf16x8 B = as_bf16x8(ld16(&sm.xs[buf][16 * nt + c16][kb * 32 + 8 * i]));
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 B = as_bf16x8(ld16(&sm.xs[buf][16 * nt + c16][kb * 32 + 8 * i]));
 #pragma unroll
-          for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int rt = 0; rt < kRT; ++rt) acc[m][rt][nt] = mfma16x16x32(A[m][rt], B, acc[m][rt][nt]);
-        }
+          for (int rt = 0; rt < kRT; ++rt) acc[m][rt][nt] = mfma16x16x32(A[m][rt], B, acc[m][rt][nt]);
       }
     }
   };
@@ -150,14 +159,14 @@ __device__ __forceinline__ void gemm_pass(Smem& sm, const uint8_t* const (&wr)[M
     issue_x(s, s);
     issue_w(s, s);
   }
-  write_x(0, 0);
+  write_x(0, 0, 0);
   for (int b0 = 0; b0 < NB; b0 += kPF) {
 #pragma unroll
     for (int s = 0; s < kPF; ++s) {
       const int b = b0 + s;
       lds_barrier();  // block b's tile is in LDS; the other buffer is free
-      write_x((s + 1) % kPF, (b + 1) & 1);
-      compute(s, b & 1);
+      write_x((s + 1) % kPF, (b + 1) & 1, b + 1);
+      compute(s, b & 1, b);
       issue_x(b + kPF, s);
       issue_w(b + kPF, s);
     }
@@ -193,24 +202,33 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_kernel(LayerArgs a) {
   }
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
-    if (tid < nc) sm.row[tid] = a.sorted_pairs[off + c0 + tid] / a.k;
+    if (tid < nc) sm.row[tid] = a.slot_tok[off + c0 + tid];
     lds_barrier();
-    f32x4 acc[2][kRT13][kNT];
-    gemm_pass<2, kPF13, kRT13>(sm, wr, sr, act, a.x, a.H, nc, a.H, acc);
+    auto pass = [&](auto nt_const) {
+      constexpr int NT = decltype(nt_const)::value;
+      f32x4 acc[2][kRT13][NT];
+      gemm_pass<2, kPF13, kRT13, NT>(sm, wr, sr, act, a.x, a.H, nc, a.H, acc);
 #pragma unroll
-    for (int rt = 0; rt < kRT13; ++rt)
+      for (int rt = 0; rt < kRT13; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int tok = 16 * nt + c16;
-        if (act[rt] && tok < nc) {
-          uint16_t hv[4];
+        for (int nt = 0; nt < NT; ++nt) {
+          const int tok = 16 * nt + c16;
+          if (act[rt] && tok < nc) {
+            uint16_t hv[4];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) hv[qq] = swiglu_bf16(acc[0][rt][nt][qq], acc[1][rt][nt][qq]);
-          const uint2 pk = {(uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
-                            (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
-          *reinterpret_cast<uint2*>(a.h + (size_t)(off + c0 + tok) * a.I + rw + 16 * rt + 4 * kb) = pk;
+            for (int qq = 0; qq < 4; ++qq) hv[qq] = swiglu_bf16(acc[0][rt][nt][qq], acc[1][rt][nt][qq]);
+            const uint2 pk = {(uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
+                              (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+            *reinterpret_cast<uint2*>(a.h + (size_t)(off + c0 + tok) * a.I + rw + 16 * rt + 4 * kb) = pk;
+          }
         }
-      }
+    };
+    switch ((nc + 15) / 16) {
+      case 1: pass(IntC<1>{}); break;
+      case 2: pass(IntC<2>{}); break;
+      case 3: pass(IntC<3>{}); break;
+      default: pass(IntC<4>{}); break;
+    }
   }
 }
 
@@ -242,21 +260,30 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_kernel(LayerArgs a) {
     const int nc = min(kTok, ne - c0);
     if (tid < nc) sm.row[tid] = off + c0 + tid;
     lds_barrier();
-    f32x4 acc[1][kRT2][kNT];
-    gemm_pass<1, kPF2, kRT2>(sm, wr, sr, act, a.h, a.I, nc, a.I, acc);
+    auto pass = [&](auto nt_const) {
+      constexpr int NT = decltype(nt_const)::value;
+      f32x4 acc[1][kRT2][NT];
+      gemm_pass<1, kPF2, kRT2, NT>(sm, wr, sr, act, a.h, a.I, nc, a.I, acc);
 #pragma unroll
-    for (int rt = 0; rt < kRT2; ++rt)
+      for (int rt = 0; rt < kRT2; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const int tok = 16 * nt + c16;
-        if (act[rt] && tok < nc) {
-          const int s = off + c0 + tok;
-          const float gate = a.slot_gate[s];
-          const f32x4 v = acc[0][rt][nt];
-          const float4 o = {gate * v[0], gate * v[1], gate * v[2], gate * v[3]};
-          *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
+        for (int nt = 0; nt < NT; ++nt) {
+          const int tok = 16 * nt + c16;
+          if (act[rt] && tok < nc) {
+            const int s = off + c0 + tok;
+            const float gate = a.slot_gate[s];
+            const f32x4 v = acc[0][rt][nt];
+            const float4 o = {gate * v[0], gate * v[1], gate * v[2], gate * v[3]};
+            *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
+          }
         }
-      }
+    };
+    switch ((nc + 15) / 16) {
+      case 1: pass(IntC<1>{}); break;
+      case 2: pass(IntC<2>{}); break;
+      case 3: pass(IntC<3>{}); break;
+      default: pass(IntC<4>{}); break;
+    }
   }
 }
 
