@@ -65,6 +65,13 @@ class Oracle:
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
                                       _f32p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_forward_mx8.restype = ctypes.c_int
+        lib.oracle_forward_mx8.argtypes = lib.oracle_forward.argtypes + [ctypes.c_double]
+        lib.oracle_e4m3.restype = ctypes.c_double
+        lib.oracle_e4m3.argtypes = [ctypes.c_int]
+        lib.oracle_mx8_quant.restype = None
+        lib.oracle_mx8_quant.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
         lib.oracle_prenorm.restype = None
         lib.oracle_prenorm.argtypes = [ctypes.c_int, ctypes.c_int, _f32p, ctypes.c_double,
                                        ctypes.c_void_p]
@@ -121,11 +128,25 @@ class Oracle:
         ow = _OW(**{n: ctypes.cast(arrs[n], ctypes.POINTER(ctypes.c_void_p)) for n in arrs})
         return ow, (keep, arrs)
 
+    def e4m3(self, code: int) -> float:
+        return self.lib.oracle_e4m3(code)
+
+    def mx8_quant(self, v: np.ndarray):
+        """MXFP8 blocks of 32 along the last axis: (E4M3 codes uint8, UE8M0 scales uint8)."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        assert v.shape[-1] % 32 == 0
+        codes = np.empty(v.shape, np.uint8)
+        scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+        self.lib.oracle_mx8_quant(v.size, v.ctypes.data, codes.ctypes.data, scales.ctypes.data)
+        return codes, scales
+
     def forward(self, H: int, I: int, E: int, k: int, x_bits: np.ndarray, logits: np.ndarray,
                 experts: Dict[int, Dict[str, np.ndarray]], tokens: Optional[Sequence[int]] = None,
-                want_h: bool = False):
+                want_h: bool = False, mx8: bool = False, gamma: float = 0.0):
         """y for the listed tokens (default all).  `experts` maps expert id -> its six
         byte tensors; only experts the router selects for the listed tokens are needed.
+        With mx8, x and the bf16 h are quantised to MXFP8 before the matrices that
+        read them, and hbound uses `gamma` as the relative accumulation bound.
         Returns dict(y, idx, gates[, h, hpre, hbound])."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -140,11 +161,12 @@ class Oracle:
         hpre = np.zeros((T * k, I), np.float64) if want_h else None
         hbound = np.zeros((T * k, I), np.float64) if want_h else None
         ow, keep = self._weights(experts, E)
-        rc = self.lib.oracle_forward(
-            T, H, I, E, k, x_bits.ctypes.data, logits, ctypes.byref(ow), n_tok,
-            None if tok is None else tok.ctypes.data, y,
-            None if h is None else h.ctypes.data, None if hpre is None else hpre.ctypes.data,
-            None if hbound is None else hbound.ctypes.data, idx.ctypes.data, g.ctypes.data)
+        args = (T, H, I, E, k, x_bits.ctypes.data, logits, ctypes.byref(ow), n_tok,
+                None if tok is None else tok.ctypes.data, y,
+                None if h is None else h.ctypes.data, None if hpre is None else hpre.ctypes.data,
+                None if hbound is None else hbound.ctypes.data, idx.ctypes.data, g.ctypes.data)
+        rc = (self.lib.oracle_forward_mx8(*args, float(gamma)) if mx8
+              else self.lib.oracle_forward(*args))
         del keep
         if rc != 0:
             raise KeyError("the router selected an expert whose weights were not given")

@@ -90,6 +90,82 @@ uint16_t oracle_double_to_bf16(double v) {
     return (uint16_t)(u >> 16);
 }
 
+/* ------------------------------------------------------------------ MXFP8
+ * The optional prefill mode feeds the matrix cores FP8 activations in the OCP
+ * MX layout (blocks of 32 values sharing one UE8M0 scale).  Readings: E4M3 as
+ * in the OCP FP8 format; the shared exponent is floor(log2(amax)) minus 8, the
+ * largest E4M3 exponent; elements round to nearest, ties to even, and saturate
+ * to +-448; the sign of a value that rounds to zero is kept. */
+
+/* E4M3 code -> value: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits
+ * 2..0; exponent field 0 is subnormal (m/8 * 2^-6); 0x7F and 0xFF are NaN. */
+double oracle_e4m3(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* r -> E4M3 code: round to nearest, ties to even, saturate to 448. */
+static int e4m3_code(double r) {
+    int s = (signbit(r) && MUT(15) == 0) ? 1 : 0;
+    double a = fabs(r), q;
+    if (a >= ldexp(1.0, -6)) {
+        int e;
+        frexp(a, &e);                          /* a in [2^(e-1), 2^e) */
+        double quantum = ldexp(1.0, e - 1 - 3); /* 3 mantissa bits */
+        q = (MUT(16) ? round(a / quantum) : nearbyint(a / quantum)) * quantum;
+    } else {
+        q = (MUT(16) ? round(a / ldexp(1.0, -9)) : nearbyint(a / ldexp(1.0, -9))) * ldexp(1.0, -9);
+    }
+    if (q > 448.0 && MUT(14) == 0) q = 448.0;
+    int code;
+    if (q == 0.0) {
+        code = 0;
+    } else if (q < ldexp(1.0, -6)) {
+        code = (int)(q / ldexp(1.0, -9));      /* subnormal: m * 2^-9 */
+    } else {
+        int e;
+        frexp(q, &e);                          /* q in [2^(e-1), 2^e) */
+        int m = (int)(ldexp(q, -(e - 1)) * 8.0 - 8.0);
+        code = ((e - 1 + 7) << 3) | m;
+    }
+    return (s << 7) | code;
+}
+
+/* Quantise n values (n a multiple of 32) to MXFP8 blocks of 32: scales[b] is
+ * the UE8M0 byte of block b, codes[i] the E4M3 code of v[i] / 2^(byte - 127).
+ * A block of zeros gets byte 0 and zero codes. */
+void oracle_mx8_quant(int n, const double *v, uint8_t *codes, uint8_t *scales) {
+    for (int b = 0; b < n / 32; ++b) {
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[32 * b + i]));
+        int se = 0;
+        if (amax > 0.0) {
+            int e;
+            frexp(amax, &e);                   /* amax in [2^(e-1), 2^e) */
+            se = (e - 1) - 8 + MUT(13) + 127;
+            if (se < 0) se = 0;
+            if (se > 254) se = 254;
+        }
+        scales[b] = (uint8_t)se;
+        for (int i = 0; i < 32; ++i) {
+            double r = v[32 * b + i] / ldexp(1.0, se - 127);
+            codes[32 * b + i] = (uint8_t)e4m3_code(r);
+        }
+    }
+}
+
+/* v <- dequantised MXFP8 of v (in place), blocks of 32. */
+static void mx8_round_trip(int n, double *v) {
+    uint8_t *c = (uint8_t *)malloc((size_t)n);
+    uint8_t *s = (uint8_t *)malloc((size_t)n / 32);
+    oracle_mx8_quant(n, v, c, s);
+    for (int i = 0; i < n; ++i) v[i] = oracle_e4m3(c[i]) * ldexp(1.0, s[i / 32] - 127);
+    free(s);
+    free(c);
+}
+
 /* ------------------------------------------------------------------ weights */
 
 /* Decoded weight element: row r, input column c of a [rows][cols/2] nibble
@@ -191,9 +267,9 @@ static void decode_row(const uint8_t *w, const uint8_t *s, int cols, int r, doub
  * absolute products), plus 8 fp32 ulps for the epilogue. */
 static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const uint8_t *s1,
                        const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
-                       uint16_t *h, double *hpre, double *hbound, double *Y) {
+                       int mx8, double gamma, uint16_t *h, double *hpre, double *hbound, double *Y) {
     const double u32 = ldexp(1.0, -24);
-    const double gam = H * u32 / (1.0 - H * u32);
+    const double gam = gamma > 0.0 ? gamma : H * u32 / (1.0 - H * u32);
     double *hv = (double *)malloc(sizeof(double) * (size_t)I);
     #pragma omp parallel
     {
@@ -223,6 +299,7 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
         free(r3);
         free(r1);
     }
+    if (mx8) mx8_round_trip(I, hv);  /* the bf16 h, quantised to MXFP8 along I */
     #pragma omp parallel
     {
         double *r2 = (double *)malloc(sizeof(double) * (size_t)I);
@@ -251,10 +328,10 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
  *   hbound optional [T*k][I] double (fp32 evaluation bound of hpre, see expert_ffn)
  *   idx, gates optional [T*k] outputs of the router
  * Returns 0, or -1 if a selected expert's weights were not provided. */
-int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
-                   const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
-                   uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
-                   float *gates_out) {
+static int forward_impl(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
+                        const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
+                        uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
+                        float *gates_out, int mx8, double gamma) {
     int P = T * k;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     float *g = (float *)malloc(sizeof(float) * (size_t)P);
@@ -272,6 +349,7 @@ int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const f
     for (int i = 0; i < n_tok && rc == 0; ++i) {
         int t = tok ? tok[i] : i;
         for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(x[(size_t)t * H + c]);
+        if (mx8) mx8_round_trip(H, xd);  /* x quantised to MXFP8 along H */
         for (int m = 0; m < H; ++m) acc[m] = 0.0;
         for (int j = 0; j < k; ++j) {
             int e = idx[(size_t)t * k + j];
@@ -279,8 +357,8 @@ int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const f
                 rc = -1;
                 break;
             }
-            expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], h,
-                       hp, hbound ? hb : NULL, Y);
+            expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], mx8,
+                       gamma, h, hp, hbound ? hb : NULL, Y);
             size_t p = (size_t)t * k + j;
             if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
             if (hpre) memcpy(hpre + p * I, hp, sizeof(double) * (size_t)I);
@@ -292,6 +370,26 @@ int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const f
     }
     free(hb); free(hp); free(h); free(acc); free(Y); free(xd); free(g); free(idx);
     return rc;
+}
+
+int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
+                   const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
+                   uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
+                   float *gates_out) {
+    return forward_impl(T, H, I, E, k, x, logits, W, n_tok, tok, y, h_out, hpre, hbound, idx_out,
+                        gates_out, 0, 0.0);
+}
+
+/* The MXFP8 mode: as oracle_forward, with x quantised to MXFP8 along H before
+ * w1/w3 and the bf16 h quantised to MXFP8 along I before w2.  hbound uses
+ * `gamma` as the relative accumulation bound of G and U (the summation error
+ * is at most gamma times the sum of absolute products). */
+int oracle_forward_mx8(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
+                       const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
+                       uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
+                       float *gates_out, double gamma) {
+    return forward_impl(T, H, I, E, k, x, logits, W, n_tok, tok, y, h_out, hpre, hbound, idx_out,
+                        gates_out, 1, gamma);
 }
 
 /* Pre-normalisation of the layer stack: u = bf16(x / sqrt(mean(x^2) + eps)). */

@@ -327,6 +327,130 @@ def pin_numpy_matmul(o):
         assert np.allclose(out["y"][t], acc.astype(np.float32), rtol=1e-6, atol=1e-6 * np.abs(acc).max())
 
 
+# ---------------------------------------------------------------- MXFP8 mode
+def _e4m3_values():
+    """All finite E4M3 values by code, from the bit fields (sign 7, exponent 6..3
+    with bias 7, mantissa 2..0, exponent 0 subnormal), as exact fractions."""
+    from fractions import Fraction
+    vals = {}
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue  # NaN
+        e, m = (c >> 3) & 15, c & 7
+        v = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        vals[c] = -v if c & 0x80 else v
+    return vals
+
+
+def _mx8_brute(block):
+    """Independent MXFP8 quantiser for one block of 32 (exact rationals, exhaustive
+    search over the finite E4M3 codes).  Returns (codes, scale byte)."""
+    from fractions import Fraction
+    vals = _e4m3_values()
+    fr = [Fraction(float(v)) for v in block]
+    amax = max(abs(v) for v in fr)
+    if amax == 0:
+        se = 0
+    else:
+        e = 0
+        while Fraction(2) ** (e + 1) <= amax:
+            e += 1
+        while Fraction(2) ** e > amax:
+            e -= 1
+        se = min(254, max(0, e - 8 + 127))
+    scale = Fraction(2) ** (se - 127)
+    pos = sorted((v, c) for c, v in vals.items() if c < 0x80)  # non-negative values
+    codes = []
+    for v, f in zip(block, fr):
+        r = min(abs(f) / scale, Fraction(448))   # saturate
+        best = min(pos, key=lambda vc: (abs(vc[0] - r), vc[1] & 1))  # nearest, ties to even code
+        codes.append(best[1] | (0x80 if math.copysign(1.0, float(v)) < 0 else 0))
+    return codes, se
+
+
+def pin_e4m3_table(o):
+    """E4M3 decode of all 256 codes against torch's float8_e4m3fn."""
+    import torch
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    for c in range(256):
+        got, want = o.e4m3(c), float(ref[c])
+        assert (math.isnan(got) and math.isnan(want)) or got == want, (hex(c), got, want)
+
+
+def pin_mx8_quant(o):
+    """MXFP8 quantiser against the exhaustive-search version on random blocks of
+    mixed magnitudes (signs, subnormal results, exact ties, zeros)."""
+    rng = np.random.default_rng(41)
+    blocks = []
+    for b in range(24):
+        v = rng.standard_normal(32) * np.ldexp(1.0, int(rng.integers(-20, 20)))
+        v[rng.integers(0, 32, 4)] *= np.ldexp(1.0, -12)   # values far below the block max
+        v[rng.integers(0, 32, 2)] = 0.0
+        blocks.append(v)
+    # ties at several binades: 17 (16 vs 18), 1.0625 (1 vs 1.125), 9*2^-10 (subnormal 4 vs 5)
+    t = np.zeros(32)
+    t[:6] = [256.0, 17.0, -1.0625, 9 * 2.0 ** -10 * 256, 19.0, -0.0]
+    blocks.append(t)
+    for v in blocks:
+        codes, scales = o.mx8_quant(v)
+        want, se = _mx8_brute(v)
+        assert int(scales[0]) == se, (int(scales[0]), se)
+        assert list(codes) == want, (list(codes), want)
+
+
+def pin_mx8_special(o):
+    """Closed forms: a block whose max is 2^k has scale byte k - 8 + 127 and that
+    element is 256 = code 0x78; a max of 511 * 2^k saturates to 448 (0x7E); a
+    zero block has byte 0 and zero codes; -0 keeps its sign."""
+    for k in (-30, -3, 0, 5, 40):
+        v = np.zeros(32)
+        v[3] = 2.0 ** k
+        v[7] = -(2.0 ** k)
+        codes, sc = o.mx8_quant(v)
+        assert int(sc[0]) == k - 8 + 127 and codes[3] == 0x78 and codes[7] == 0xF8
+        v[5] = 511 * 2.0 ** (k - 8)       # max of the block now: 511 * 2^(k-8) < 2^(k+1)
+        codes, sc = o.mx8_quant(v)
+        assert int(sc[0]) == k - 8 + 127 and codes[5] == 0x7E
+    codes, sc = o.mx8_quant(np.zeros(64))
+    assert not codes.any() and not sc.any()
+    v = np.zeros(32)
+    v[0], v[1] = 1.0, -0.0
+    codes, _ = o.mx8_quant(v)
+    assert codes[1] == 0x80
+
+
+def pin_mx8_forward(o):
+    """The MXFP8 mode against numpy: x and the bf16 h go through the (pinned)
+    quantiser, everything else is float64 dequantisation + matmul."""
+    rng = np.random.default_rng(45)
+    H, I, E, k, T = 128, 64, 5, 2, 3
+    experts = {e: random_expert(rng, H, I) for e in range(E)}
+    x = rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    out = o.forward(H, I, E, k, x, lg, experts, want_h=True, mx8=True)
+
+    def rt(v):
+        c, sc = o.mx8_quant(v)
+        d = np.array([o.e4m3(int(q)) for q in c.ravel()]).reshape(c.shape)
+        return d * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=-1)
+
+    for t in range(T):
+        xq = rt(bf16_to_f64(x[t]))
+        acc = np.zeros(H)
+        for j in range(k):
+            e = int(out["idx"][t, j])
+            W1 = _dequant(experts[e]["w1"], experts[e]["s1"])
+            W3 = _dequant(experts[e]["w3"], experts[e]["s3"])
+            W2 = _dequant(experts[e]["w2"], experts[e]["s2"])
+            G, U = W1 @ xq, W3 @ xq
+            hp = G / (1.0 + np.exp(-G)) * U
+            p = t * k + j
+            assert np.allclose(out["hpre"][p], hp, rtol=1e-12, atol=1e-12 * np.abs(hp).max())
+            acc += float(out["gates"][t, j]) * (W2 @ rt(bf16_to_f64(out["h"][p])))
+        assert np.allclose(out["y"][t], acc.astype(np.float32), rtol=1e-6, atol=1e-6 * np.abs(acc).max())
+
+
 ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pin_router_special,
             pin_permute, pin_probe_w1, pin_probe_w2, pin_closed_form_swiglu, pin_prenorm,
-            pin_brute, pin_numpy_matmul]
+            pin_brute, pin_numpy_matmul, pin_e4m3_table, pin_mx8_quant, pin_mx8_special,
+            pin_mx8_forward]
