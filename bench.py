@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP4 MoE layer: decode µs/token (HBM GB/s) & 2048-tok prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 MFMA (the FP4 x FP8 scaled MFMA is priced at it)
 SPIN_CYCLES = 200_000_000       # head start for the host to enqueue profiled steps
 # the one-token decode kernels (w1/w3 with the routing inside; w2 with the combine inside)
 DECODE_KERNELS = {"w13": "gemv13_one_kernel", "w2": "gemv2_one_kernel"}
@@ -220,35 +221,46 @@ def main():
     lp_np = synth.gen_logits(pf, 0)
     lp = torch.from_numpy(lp_np).to(dev)
     yp = torch.empty((pf.T, pf.H), dtype=torch.float32, device=dev)
-    wsp = torch.empty(moe.moe_fp4_workspace_size(pf.T, pf.H, pf.I, pf.E, pf.k), dtype=torch.uint8,
-                      device=dev)
-    for _ in range(2):
-        moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, workspace=wsp)
-    torch.cuda.synchronize()
-    evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
-    tp0 = time.perf_counter()
-    for i in range(args.prefill_reps):
-        moe.moe_fp4_forward_profiled(xp, lp, w, pf.k, evp[i], y=yp, workspace=wsp)
-    torch.cuda.synchronize()
-    tp1 = time.perf_counter()
-    pst = np.array([e.stage_ms() for e in evp])
-    p_ms = (tp1 - tp0) * 1e3 / args.prefill_reps
     pairs = pf.T * pf.k
     flops = pairs * (2 * 2 * pf.H * pf.I + 2 * pf.I * pf.H)
     Dp = len(np.unique(topk_sets(lp_np, pf.k)))
     p_bytes = Dp * expert_bytes(pf.H, pf.I) + pf.T * pf.H * 2 + pf.T * pf.H * 4
-    prefill = {
-        "workload": "prefill chunk T=2048, E=384, top-6, H=5120, I=2304, Zipf(0.3) logit bias",
-        "ms_per_chunk": p_ms, "tflops": flops / (p_ms * 1e-3) / 1e12, "gflop": flops / 1e9,
-        "distinct_experts": Dp, "weight_GB": Dp * expert_bytes(pf.H, pf.I) / 1e9,
-        "hbm_frac": p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "mfma_bf16_frac": flops / (p_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "kernel_ms": {"route": float(pst[:, 0].mean()), "gemm13": float(pst[:, 1].mean()),
-                      "gemm2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
-    }
-    prefill["roofline_frac"] = max(prefill["hbm_frac"], prefill["mfma_bf16_frac"])
-    log(f"prefill: {p_ms:.3f} ms/chunk, {prefill['tflops']:.1f} TFLOP/s, HBM frac "
-        f"{prefill['hbm_frac']:.2f}, kernels {prefill['kernel_ms']}")
+
+    def run_prefill(mode, label, mfma_peak):
+        wsp = torch.empty(moe.moe_fp4_workspace_size(pf.T, pf.H, pf.I, pf.E, pf.k, mode),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp)
+        torch.cuda.synchronize()
+        evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
+        tp0 = time.perf_counter()
+        for i in range(args.prefill_reps):
+            moe.moe_fp4_forward_profiled(xp, lp, w, pf.k, evp[i], y=yp, mode=mode, workspace=wsp)
+        torch.cuda.synchronize()
+        tp1 = time.perf_counter()
+        pst = np.array([e.stage_ms() for e in evp])
+        p_ms = (tp1 - tp0) * 1e3 / args.prefill_reps
+        out = {
+            "workload": "prefill chunk T=2048, E=384, top-6, H=5120, I=2304, Zipf(0.3) logit bias",
+            "activations": label,
+            "ms_per_chunk": p_ms, "tflops": flops / (p_ms * 1e-3) / 1e12, "gflop": flops / 1e9,
+            "distinct_experts": Dp, "weight_GB": Dp * expert_bytes(pf.H, pf.I) / 1e9,
+            "hbm_frac": p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "mfma_frac": flops / (p_ms * 1e-3) / 1e12 / mfma_peak, "mfma_peak_tflops": mfma_peak,
+            "kernel_ms": {"route": float(pst[:, 0].mean()), "w13": float(pst[:, 1].mean()),
+                          "w2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
+        }
+        out["roofline_frac"] = max(out["hbm_frac"], out["mfma_frac"])
+        log(f"prefill ({label}): {p_ms:.3f} ms/chunk, {out['tflops']:.1f} TFLOP/s, HBM frac "
+            f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}")
+        del wsp
+        return out
+
+    prefill = run_prefill(moe.MODE_PREFILL, "bf16 (MFMA 16x16x32 bf16, FP4 decoded in registers)",
+                          BF16_PEAK_TFLOPS)
+    prefill_mx = run_prefill(moe.MODE_PREFILL_MXFP8,
+                             "MXFP8 (x and h quantised; FP4 x FP8 scaled MFMA 16x16x128)",
+                             FP8_PEAK_TFLOPS)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -301,6 +313,7 @@ def main():
         "us_per_token_eager": us_eager,
         "cold": cold,
         "prefill": prefill,
+        "prefill_mxfp8": prefill_mx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

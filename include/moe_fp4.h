@@ -57,6 +57,14 @@ extern "C" {
 #define MOE_FP4_MODE_AUTO     0  /* DECODE where it supports the dims, else PREFILL  */
 #define MOE_FP4_MODE_DECODE   1  /* GEMV path for a few tokens (see below)           */
 #define MOE_FP4_MODE_PREFILL  2  /* grouped-GEMM path; any T                         */
+#define MOE_FP4_MODE_PREFILL_MXFP8 3  /* grouped GEMM on FP4 x FP8 scaled MFMA (below)  */
+/* MOE_FP4_MODE_PREFILL_MXFP8 computes the layer with the activations in the OCP
+ * MX FP8 format: x is quantised to MXFP8 along H before w1/w3 and the bf16 h
+ * along I before w2 (see moe_fp4_quant_mxfp8); the matrix cores then take the
+ * FP4 weights and their UE8M0 scales as stored.  Routing, the SwiGLU epilogue
+ * (h rounded to bf16 first) and the combine are as in PREFILL.  Requires H and
+ * I to be multiples of 128.  Its results differ from PREFILL by the FP8
+ * quantisation of the activations (about 5e-2 relative), not by rounding. */
 /* DECODE supports T <= 16 (T <= 2 on row-contiguous dot kernels, more on MFMA
  * kernels) as far as the T activation rows and the T*k h rows it stages in LDS
  * fit 64 KiB; at H = 5120, I = 2304, k = 6 that is T <= 4.  I <= 3072 beyond
@@ -164,6 +172,18 @@ int moe_fp4_prenorm_bf16(const float *x, uint16_t *u, int32_t T, int32_t H, floa
                          hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
+/* MXFP8 quantisation (OCP MX, blocks of 32 consecutive values of a row):
+ *   src     [rows][K] bf16 bits, 16-byte aligned, K a multiple of 32
+ *   codes   [rows][K] E4M3 codes, 8-byte aligned
+ *   scales  [rows][K/32] UE8M0 bytes
+ * Per block: byte = floor(log2(max |v|)) - 8 + 127, clamped to [0, 254] (0 for a
+ * block of zeros); code = E4M3(v / 2^(byte - 127)) rounded to nearest, ties to
+ * even, saturated to +-448, sign kept for zero.  This is the quantiser of
+ * MOE_FP4_MODE_PREFILL_MXFP8.
+ * Errors: EINVAL (null, sizes < 1), EUNSUPPORTED (K % 32), EALIGN, EHIP. */
+int moe_fp4_quant_mxfp8(const uint16_t *src, int32_t rows, int32_t K, uint8_t *codes,
+                        uint8_t *scales, hipStream_t stream);
+
 const char *moe_fp4_status_string(int status);
 
 #ifdef __cplusplus

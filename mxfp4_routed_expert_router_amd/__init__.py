@@ -5,7 +5,8 @@ w1/w3/w2 are FP4 E2M1 codes with UE8M0 scales per 32 inputs, gate-weighted
 combine -- runs entirely in the HIP kernels of libmoe_fp4.so (gfx950).  This
 package is its thin Python binding; see include/moe_fp4.h for the C-ABI.
 """
-from ._lib import (ACCUMULATE, MODE_AUTO, MODE_DECODE, MODE_PREFILL, ExpertWeights,  # noqa: F401
-                   MoeFp4Error, Route, StageEvents, moe_fp4_forward, moe_fp4_forward_debug,
-                   moe_fp4_forward_profiled,
-                   moe_fp4_prenorm_bf16, moe_fp4_route, moe_fp4_workspace_size, status_string)
+from ._lib import (ACCUMULATE, MODE_AUTO, MODE_DECODE, MODE_PREFILL,  # noqa: F401
+                   MODE_PREFILL_MXFP8, ExpertWeights, MoeFp4Error, Route, StageEvents,
+                   moe_fp4_forward, moe_fp4_forward_debug, moe_fp4_forward_profiled,
+                   moe_fp4_prenorm_bf16, moe_fp4_quant_mxfp8, moe_fp4_route,
+                   moe_fp4_workspace_size, status_string)

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
-MODE_AUTO, MODE_DECODE, MODE_PREFILL = 0, 1, 2
+MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_PREFILL_MXFP8 = 0, 1, 2, 3
 ACCUMULATE = 1
 TENSORS = ("w1", "s1", "w3", "s3", "w2", "s2")
 
@@ -58,6 +58,7 @@ def _load():
     lib.moe_fp4_forward_profiled.restype = ctypes.c_int
     lib.moe_fp4_prenorm_bf16.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]
     lib.moe_fp4_status_string.argtypes = [I32]
+    lib.moe_fp4_quant_mxfp8.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16"):
@@ -273,3 +274,15 @@ def moe_fp4_prenorm_bf16(x: torch.Tensor, eps: float = 1e-6,
     _check(_lib.moe_fp4_prenorm_bf16(x.data_ptr(), u.data_ptr(), T, H, eps, _stream(x)),
            "moe_fp4_prenorm_bf16")
     return u
+
+
+def moe_fp4_quant_mxfp8(x: torch.Tensor):
+    """MXFP8 quantisation of bf16 rows [rows, K] (blocks of 32 along K):
+    returns (E4M3 codes uint8 [rows, K], UE8M0 scales uint8 [rows, K/32])."""
+    _need(x, "x", (torch.bfloat16,), 2)
+    rows, K = x.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.moe_fp4_quant_mxfp8(x.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                                    _stream(x)), "moe_fp4_quant_mxfp8")
+    return codes, scales

@@ -28,13 +28,16 @@ int resolve_mode(const moe_fp4_dims& d, int mode) {
     case MOE_FP4_MODE_AUTO: return decode_ok ? MOE_FP4_MODE_DECODE : MOE_FP4_MODE_PREFILL;
     case MOE_FP4_MODE_DECODE: return decode_ok ? MOE_FP4_MODE_DECODE : -1;
     case MOE_FP4_MODE_PREFILL: return MOE_FP4_MODE_PREFILL;
+    case MOE_FP4_MODE_PREFILL_MXFP8:  // one scaled MFMA covers 128 inputs
+      return d.H % 128 == 0 && d.I % 128 == 0 ? MOE_FP4_MODE_PREFILL_MXFP8 : -1;
     default: return -1;
   }
 }
 
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
-  size_t idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h, ypair, total;
+  size_t idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h, ypair, xq,
+      xqs, hq, hqs, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
@@ -53,7 +56,14 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   L.meta = o;     o = align_up(o + 64);
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
   L.ypair = o;
-  if (rmode == MOE_FP4_MODE_PREFILL) o = align_up(o + P * (size_t)d.H * 4);
+  const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
+  if (rmode == MOE_FP4_MODE_PREFILL || mx) o = align_up(o + P * (size_t)d.H * 4);
+  if (mx) {
+    L.xq = o;  o = align_up(o + (size_t)d.T * d.H);
+    L.xqs = o; o = align_up(o + (size_t)d.T * d.H / 32);
+    L.hq = o;  o = align_up(o + P * (size_t)d.I);
+    L.hqs = o; o = align_up(o + P * (size_t)d.I / 32);
+  }
   L.total = o;
   return L;
 }
@@ -126,7 +136,14 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   a.pair_slot = r.pair_slot; a.dinfo = r.dinfo; a.meta = r.meta; a.gates = r.gates;
   a.slot_gate = r.slot_gate; a.slot_tok = r.slot_tok;
   a.h = at<uint16_t>(ws, L.h);
-  a.ypair = rmode == MOE_FP4_MODE_PREFILL ? at<float>(ws, L.ypair) : nullptr;
+  const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
+  a.ypair = rmode == MOE_FP4_MODE_PREFILL || mx ? at<float>(ws, L.ypair) : nullptr;
+  if (mx) {
+    a.xq = at<uint8_t>(ws, L.xq);
+    a.xqs = at<uint8_t>(ws, L.xqs);
+    a.hq = at<uint8_t>(ws, L.hq);
+    a.hqs = at<uint8_t>(ws, L.hqs);
+  }
   a.y = y;
   a.accumulate = (flags & MOE_FP4_ACCUMULATE) ? 1 : 0;
   a.ev = events;
@@ -134,7 +151,8 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   a.route = r;
   a.logits = logits;
   const hipError_t err = rmode == MOE_FP4_MODE_DECODE ? launch_decode(a, stream)
-                                                      : launch_prefill(a, stream);
+                         : mx                          ? launch_prefill_mx8(a, stream)
+                                                       : launch_prefill(a, stream);
   if (err != hipSuccess) return MOE_FP4_EHIP;
 
   if (h_out && launch_unsort_h(a, h_out, stream) != hipSuccess) return MOE_FP4_EHIP;
@@ -217,6 +235,15 @@ int moe_fp4_prenorm_bf16(const float* x, uint16_t* u, int32_t T, int32_t H, floa
   if (!x || !u || T < 1 || H < 1) return MOE_FP4_EINVAL;
   if (H % 32 || H > 16384) return MOE_FP4_EUNSUPPORTED;
   return launch_prenorm(x, u, T, H, eps, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
+}
+
+int moe_fp4_quant_mxfp8(const uint16_t* src, int32_t rows, int32_t K, uint8_t* codes,
+                        uint8_t* scales, hipStream_t stream) {
+  if (!src || !codes || !scales || rows < 1 || K < 1) return MOE_FP4_EINVAL;
+  if (K % 32) return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(codes, 8)) return MOE_FP4_EALIGN;
+  return launch_quant_mx8(src, rows, K, codes, scales, stream) == hipSuccess ? MOE_FP4_OK
+                                                                              : MOE_FP4_EHIP;
 }
 
 const char* moe_fp4_status_string(int status) {

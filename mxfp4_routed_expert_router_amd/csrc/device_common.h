@@ -142,4 +142,20 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return umin32(umin32(r0, r1), umin32(r2, r3));
 }
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Grouped-GEMM workgroups are dealt to the 8 XCDs round robin; give each XCD a
+// contiguous run of `n` logical tiles, so that the tiles of one expert share an
+// XCD's L2.  Returns false for padding blocks.
+__device__ __forceinline__ bool xcd_tile(int n, int& logical) {
+  const int per = (n + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  logical = (blockIdx.x & 7) * per + slot;
+  return slot < per && logical < n;
+}
+inline unsigned xcd_grid(int n) { return (unsigned)(((n + 7) / 8) * 8); }
+
 }  // namespace moe_fp4

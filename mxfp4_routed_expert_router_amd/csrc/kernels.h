@@ -60,6 +60,9 @@ struct LayerArgs {
   const int32_t* slot_tok;  // [T*k] token of the pair in each sorted slot
   uint16_t* h;   // [T*k][I] bf16, rows in sorted (by-expert) order
   float* ypair;  // [T*k][H] fp32 gate-scaled expert outputs, sorted order (prefill only)
+  // MXFP8 prefill: E4M3 codes and UE8M0 scales (one per 32 along the row) of x
+  // [T][H] and of h [T*k][I] (sorted order)
+  uint8_t *xq, *xqs, *hq, *hqs;
   float* y;      // [T][H]
   int accumulate;
   const hipEvent_t* ev;  // optional stage timing (see ev_start)
@@ -75,6 +78,10 @@ bool decode_fits(int T, int H, int I, int k);  // shapes the decode kernels take
 bool decode_fuses_route(int T, int H, int I, int E, int k);  // decode routes in its first kernel
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_combine(const LayerArgs& a, hipStream_t stream);
+hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);
 

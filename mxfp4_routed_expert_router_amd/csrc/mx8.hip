@@ -1,0 +1,370 @@
+// MXFP8 mode of the prefill path.  The activations are quantised to the OCP MX
+// FP8 format (E4M3 codes, one UE8M0 scale per 32 consecutive inputs) so that
+// the matrix cores take the FP4 weights exactly as the checkpoint stores them:
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies A = 16 rows x 128 inputs of
+// E2M1 codes by B = 128 inputs x 16 tokens of E4M3 codes, each operand with one
+// UE8M0 scale per 32 inputs.  Lane l supplies A row l % 16, inputs 32 (l/16) ..
+// +31 -- one 16-byte scale group of a weight row, low nibble first, with that
+// group's scale byte -- and B column l % 16, inputs 16 (l/16) .. +15 and
+// 64 + 16 (l/16) .. +15, with the scale byte of column l % 16's group l / 16;
+// it receives D rows 4 (l/16) .. +3 of column l % 16.  One instruction covers
+// four scale groups, with no FP4 decode on the vector units.
+//
+// What the mode computes is the plain layer with x quantised before w1/w3 and
+// the bf16 h quantised before w2 (DeepSeek-V4.1-Flash pages: the expert weights
+// are FP4 E2M1 with UE8M0 scales, 10100.com page, section on the expert-capacity
+// bottleneck; the FP8 activations are this mode's reading).
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe_fp4 {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ quantiser
+// One thread per 8 values; the 4 threads of a quad hold one block of 32 and
+// take its maximum with quad_perm exchanges.  Shared exponent: the UE8M0 byte
+// floor(log2(amax)) - 8 + 127 (8 = largest E4M3 exponent), clamped to
+// [0, 254]; 0 for a zero block.  Element: v * 2^(127 - byte) (exact: a power
+// of two), clamped to +-448 and converted by v_cvt_scalef32_pk_fp8_f32 (round
+// to nearest even, sign kept for zero).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  if (amax == 0.0f) return 0u;
+  const int ef = (int)((b >> 23) & 0xFF);
+  // floor(log2(amax)): from the exponent field, or the mantissa's top bit when subnormal
+  const int e = ef ? ef - 127 : (31 - __builtin_clz(b & 0x7FFFFF)) - 149;
+  const int se = e - 8 + 127;
+  return (uint32_t)(se < 0 ? 0 : se > 254 ? 254 : se);
+}
+
+// 2^(127 - se) for se in [0, 254] (a subnormal fp32 for se = 254).
+__device__ __forceinline__ float mx8_inv_scale(uint32_t se) {
+  const int e = 127 - (int)se;
+  return e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(1u << (e + 149));
+}
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  s16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+__global__ void __launch_bounds__(256) quant_mx8_kernel(const uint16_t* __restrict__ src, size_t n8,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  // n8 (8-value chunks) is a multiple of 4 and so is the grid stride: the four
+  // threads of a quad are always active together
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const u32x4 raw = ld16(src + i * 8);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(raw[j] << 16);
+      v[2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = quad_max(amax);
+    const uint32_t se = mx8_scale_byte(amax);
+    const float f = mx8_inv_scale(se);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fminf(fmaxf(v[j] * f, -448.0f), 448.0f);
+    const uint2 out = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
+    *reinterpret_cast<uint2*>(codes + i * 8) = out;
+    if ((i & 3) == 0) scales[i / 4] = (uint8_t)se;
+  }
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+// Every operand of the main loop reaches LDS by direct global->LDS loads
+// (global_load_lds, the destination given in M0; lane l's 16 or 4 bytes land at
+// M0 + 16 l or + 4 l), kStages K blocks deep, so the blocks in flight cost no
+// registers.  The loads are issued from inline assembly, and the loop waits for
+// them itself (s_waitcnt vmcnt(n) with n = this wave's loads still allowed in
+// flight): the compiler cannot tell which LDS block such a load writes, and
+// would otherwise wait for all of them before every LDS read.  The loop has no
+// other global loads, so the count is exact.  Each wave's weight chunks go to a
+// slot that only that wave reads; the activation tile is shared, so one
+// barrier per K block orders its loads before the reads and the reads before
+// the slot is loaded again.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTok = 64;                 // tokens per pass
+constexpr int kKB = 128;                 // inputs per K block (4 scale groups, one MFMA)
+constexpr int kRows13 = 16 * kWaves;     // w1/w3 rows per workgroup
+constexpr int kRows2 = 32 * kWaves;      // w2 rows per workgroup (two 16-row tiles per wave)
+constexpr int kStages = 5;               // K blocks resident in LDS (kStages - 1 in flight)
+constexpr int kTiles = 2;                // weight tiles per wave and block (M x row tiles)
+constexpr int kLoadsPerBlock = 2 * kTiles + 2;  // a wave's LDS loads per K block
+
+struct SmemMx {
+  uint8_t w[kStages][kWaves][kTiles][1024];   // 16 rows x 64 bytes, lane l's chunk at 16 l
+  uint32_t ws[kStages][kWaves][kTiles][64];   // lane l: the scale dword of its row's block
+  uint8_t x[kStages][kTok * kKB];             // E4M3 codes of 64 tokens, swizzled: see xoff
+  uint32_t xs[kStages][kWaves][64];           // lane l of wave w: token 8 w + (l & 7)'s 4 scales
+  int row[kTok];                              // source row of each staged token
+};
+
+// Byte offset in the activation tile of token t's 16-byte chunk c: wave t/8's
+// 1 KB, row t%8 of 128 bytes, chunk slot c ^ (t & 7).  The B reads of 16 lanes
+// (16 tokens, one chunk) then spread over the banks.
+__device__ __forceinline__ int xoff(int t, int c) { return t * 128 + ((c ^ (t & 7)) << 4); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+__device__ __forceinline__ void lds_load16(uint32_t lds_base, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+__device__ __forceinline__ void lds_load4(uint32_t lds_base, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+// Wait until at most N of this wave's LDS loads are in flight, then meet the
+// workgroup.  The memory clobber keeps the compiler's LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_blocks_then_barrier(int blocks_after) {
+  switch (blocks_after) {  // blocks_after <= kStages - 2
+    case 0: wait_then_barrier<0>(); break;
+    case 1: wait_then_barrier<kLoadsPerBlock>(); break;
+    case 2: wait_then_barrier<2 * kLoadsPerBlock>(); break;
+    default: wait_then_barrier<3 * kLoadsPerBlock>(); break;
+  }
+}
+static_assert(kStages - 2 <= 3, "wait_blocks_then_barrier covers up to 3 blocks in flight");
+
+// One pass over all K (a multiple of 128) for up to NT*16 staged token rows:
+// acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].  M * kRT == kTiles.
+// Weight rows past the end (act false) and tokens past nc load valid data whose
+// results are not stored.
+template <int M, int kRT, int NT>
+__device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&wr)[M][kRT],
+                                             const uint8_t* const (&sr)[M][kRT],
+                                             const uint8_t* __restrict__ q,
+                                             const uint8_t* __restrict__ qs, int nc, int K,
+                                             f32x4 (&acc)[M][kRT][NT]) {
+  static_assert(M * kRT == kTiles, "tile count");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int NB = K / kKB, KS = K / 32;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's activation chunk and scale dword (token rows past nc read token 0's)
+  const int xt = 8 * w + lane / 8, xc = (lane & 7) ^ (xt & 7);
+  const uint8_t* const xsrc = q + (size_t)sm.row[xt < nc ? xt : 0] * K + xc * 16;
+  const int st = 8 * w + (lane & 7);
+  const uint8_t* const ssrc = qs + (size_t)sm.row[st < nc ? st : 0] * KS;
+  auto issue = [&](int b, int s) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        lds_load16(lds_addr(&sm.w[s][w][m * kRT + rt][0]), wr[m][rt] + (size_t)(4 * b + kb) * 16);
+        lds_load4(lds_addr(&sm.ws[s][w][m * kRT + rt][0]), sr[m][rt] + 4 * b);
+      }
+    lds_load16(lds_addr(&sm.x[s][w * 1024]), xsrc + (size_t)b * kKB);
+    lds_load4(lds_addr(&sm.xs[s][w][0]), ssrc + 4 * b);
+  };
+  auto compute = [&](int s) {
+    u32x4 A[M][kRT];
+    int sa[M][kRT];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][16 * lane]);
+        sa[m][rt] = (int)((sm.ws[s][w][m * kRT + rt][lane] >> (8 * kb)) & 0xFFu);
+      }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = 16 * nt + c16;
+      const u32x4 lo = ld16(&sm.x[s][xoff(t, kb)]), hi = ld16(&sm.x[s][xoff(t, 4 + kb)]);
+      const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int sb = (int)((sm.xs[s][t / 8][t & 7] >> (8 * kb)) & 0xFFu);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const u32x4 a4 = A[m][rt];
+          const i32x8 Av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+          acc[m][rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              Av, B, acc[m][rt][nt], 4 /* A: E2M1 */, 0 /* B: E4M3 */, 0, sa[m][rt], 0, sb);
+        }
+    }
+  };
+
+  for (int b = 0; b < kStages - 1 && b < NB; ++b) issue(b, b);
+  for (int b = 0; b < NB; ++b) {
+    // block b's loads (this wave's) are done once at most the loads of the
+    // blocks issued after it are in flight; the barrier extends that to every
+    // wave's, and means every wave is done computing block b - 1
+    wait_blocks_then_barrier(min(kStages - 2, NB - 1 - b));
+    if (b + kStages - 1 < NB) issue(b + kStages - 1, (b + kStages - 1) % kStages);  // into b-1's slot
+    compute(b % kStages);
+  }
+  __syncthreads();  // the LDS is free for the caller (and its row table may change)
+}
+
+__global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
+  const int tpe = (a.I + kRows13 - 1) / kRows13;
+  int logical;
+  if (!xcd_tile(a.E * tpe, logical)) return;
+  const int e = logical / tpe, rtile = logical - e * tpe;
+  const int ne = a.counts[e];
+  if (ne == 0) return;
+  const int off = a.offsets[e];
+  __shared__ SmemMx sm;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int rw = rtile * kRows13 + w * 16;
+  const size_t wrow = (size_t)a.H / 2, srow = (size_t)a.H / 32;
+  const bool act = rw < a.I;
+  const size_t ro = (size_t)(act ? rw + c16 : 0);
+  const uint8_t* const wr[2][1] = {{a.w1 + (size_t)e * a.stride[0] + ro * wrow},
+                                   {a.w3 + (size_t)e * a.stride[2] + ro * wrow}};
+  const uint8_t* const sr[2][1] = {{a.s1 + (size_t)e * a.stride[1] + ro * srow},
+                                   {a.s3 + (size_t)e * a.stride[3] + ro * srow}};
+  for (int c0 = 0; c0 < ne; c0 += kTok) {
+    const int nc = min(kTok, ne - c0);
+    if (tid < nc) sm.row[tid] = a.slot_tok[off + c0 + tid];
+    lds_barrier();
+    auto pass = [&](auto nt_const) {
+      constexpr int NT = decltype(nt_const)::value;
+      f32x4 acc[2][1][NT];
+      gemm_pass_mx<2, 1, NT>(sm, wr, sr, a.xq, a.xqs, nc, a.H, acc);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = 16 * nt + c16;
+        if (act && tok < nc) {
+          uint16_t hv[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) hv[qq] = swiglu_bf16(acc[0][0][nt][qq], acc[1][0][nt][qq]);
+          const uint2 pk = {(uint32_t)hv[0] | ((uint32_t)hv[1] << 16),
+                            (uint32_t)hv[2] | ((uint32_t)hv[3] << 16)};
+          *reinterpret_cast<uint2*>(a.h + (size_t)(off + c0 + tok) * a.I + rw + 4 * kb) = pk;
+        }
+      }
+    };
+    switch ((nc + 15) / 16) {
+      case 1: pass(IntC<1>{}); break;
+      case 2: pass(IntC<2>{}); break;
+      case 3: pass(IntC<3>{}); break;
+      default: pass(IntC<4>{}); break;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
+  const int tpe = (a.H + kRows2 - 1) / kRows2;
+  int logical;
+  if (!xcd_tile(a.E * tpe, logical)) return;
+  const int e = logical / tpe, rtile = logical - e * tpe;
+  const int ne = a.counts[e];
+  if (ne == 0) return;
+  const int off = a.offsets[e];
+  __shared__ SmemMx sm;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int rw = rtile * kRows2 + w * 32;
+  const size_t wrow = (size_t)a.I / 2, srow = (size_t)a.I / 32;
+  bool act[2];
+  const uint8_t* wr[1][2];
+  const uint8_t* sr[1][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = rw + 16 * rt;
+    act[rt] = r < a.H;
+    const size_t ro = (size_t)(act[rt] ? r + c16 : 0);
+    wr[0][rt] = a.w2 + (size_t)e * a.stride[4] + ro * wrow;
+    sr[0][rt] = a.s2 + (size_t)e * a.stride[5] + ro * srow;
+  }
+  for (int c0 = 0; c0 < ne; c0 += kTok) {
+    const int nc = min(kTok, ne - c0);
+    if (tid < nc) sm.row[tid] = off + c0 + tid;
+    lds_barrier();
+    auto pass = [&](auto nt_const) {
+      constexpr int NT = decltype(nt_const)::value;
+      f32x4 acc[1][2][NT];
+      gemm_pass_mx<1, 2, NT>(sm, wr, sr, a.hq, a.hqs, nc, a.I, acc);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int tok = 16 * nt + c16;
+          if (act[rt] && tok < nc) {
+            const int s = off + c0 + tok;
+            const float gate = a.slot_gate[s];
+            const f32x4 v = acc[0][rt][nt];
+            const float4 o = {gate * v[0], gate * v[1], gate * v[2], gate * v[3]};
+            *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
+          }
+        }
+    };
+    switch ((nc + 15) / 16) {
+      case 1: pass(IntC<1>{}); break;
+      case 2: pass(IntC<2>{}); break;
+      case 3: pass(IntC<3>{}); break;
+      default: pass(IntC<4>{}); break;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  const size_t n8 = (size_t)rows * K / 8;
+  size_t blocks = (n8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, n8, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+// x is quantised first (stage 1 timing covers it with the w1/w3 GEMM), h after
+// the w1/w3 GEMM (stage 2 covers it with the w2 GEMM).
+hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream) {
+  const hipEvent_t* ev = a.ev;
+  const dim3 blk(kThreads);
+  const int P = a.T * a.k;
+  const size_t nx8 = (size_t)a.T * a.H / 8, nh8 = (size_t)P * a.I / 8;
+  const unsigned bx = (unsigned)std::min<size_t>((nx8 + 255) / 256, 4096);
+  const unsigned bh = (unsigned)std::min<size_t>((nh8 + 255) / 256, 4096);
+  const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
+  launch_k(quant_mx8_kernel, dim3(bx), dim3(256), 0, stream, ev_start(ev, 1), (hipEvent_t) nullptr,
+           (const uint16_t*)a.x, nx8, a.xq, a.xqs);
+  launch_k(gemm13_mx_kernel, dim3(xcd_grid(t13)), blk, 0, stream, (hipEvent_t) nullptr,
+           ev_stop(ev, 1), a);
+  launch_k(quant_mx8_kernel, dim3(bh), dim3(256), 0, stream, ev_start(ev, 2), (hipEvent_t) nullptr,
+           (const uint16_t*)a.h, nh8, a.hq, a.hqs);
+  launch_k(gemm2_mx_kernel, dim3(xcd_grid(t2)), blk, 0, stream, (hipEvent_t) nullptr, ev_stop(ev, 2),
+           a);
+  return launch_combine(a, stream);
+}
+
+}  // namespace moe_fp4

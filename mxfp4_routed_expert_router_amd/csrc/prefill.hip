@@ -40,25 +40,12 @@ constexpr int kPF13 = 3;                  // K blocks in flight per wave, w1/w3 
 constexpr int kPF2 = 4;                   // K blocks in flight per wave, w2 pass
 constexpr int kXC = (kTok * kKB / 8) / kThreads;  // 16-byte activation chunks per thread, block
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
 struct Smem {
   uint16_t xs[2][kTok][kXS];
   int row[kTok];
 };
 
 
-// Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous run
-// of `n` logical tiles.  Returns false for padding blocks.
-__device__ __forceinline__ bool xcd_tile(int n, int& logical) {
-  const int per = (n + 7) / 8;
-  const int slot = blockIdx.x >> 3;
-  logical = (blockIdx.x & 7) * per + slot;
-  return slot < per && logical < n;
-}
 
 // One pass over all K for up to NT*16 staged token rows (sm.row[n] for n < nc,
 // row length ld in src): acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].
@@ -317,9 +304,13 @@ __global__ void unsort_h_kernel(const uint16_t* __restrict__ hs, const int32_t* 
   }
 }
 
-unsigned xcd_grid(int n) { return (unsigned)(((n + 7) / 8) * 8); }
-
 }  // namespace
+
+hipError_t launch_combine(const LayerArgs& a, hipStream_t stream) {
+  launch_k(combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream, ev_start(a.ev, 3),
+           ev_stop(a.ev, 3), a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
   const dim3 blk(kThreads);
@@ -327,9 +318,7 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
   launch_k(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, ev_start(ev, 1), ev_stop(ev, 1), a);
   launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
-  launch_k(combine_kernel, dim3((a.H / 4 + 255) / 256, a.T), dim3(256), 0, stream, ev_start(ev, 3),
-           ev_stop(ev, 3), a);
-  return hipGetLastError();
+  return launch_combine(a, stream);
 }
 
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream) {

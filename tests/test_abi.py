@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
-              "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string"):
+              "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string",
+              "moe_fp4_quant_mxfp8"):
         assert n in names
 
 
@@ -190,3 +191,23 @@ def test_profiled_needs_eight_events(lib):
     assert lib._lib.moe_fp4_forward_profiled(*args, fake_events, 7) == lib.EINVAL
     fake_events[3] = None
     assert lib._lib.moe_fp4_forward_profiled(*args, fake_events, 8) == lib.EINVAL
+
+
+def test_mxfp8_mode_validation(lib):
+    """The MXFP8 prefill mode needs H and I to be multiples of 128."""
+    assert _fwd(lib, dims=(4, 256, 128, 16, 2), mode=lib.MODE_PREFILL_MXFP8, ws_bytes=0) == lib.EWORKSPACE
+    assert _fwd(lib, dims=(4, 288, 128, 16, 2), mode=lib.MODE_PREFILL_MXFP8, ws_bytes=0) == lib.EUNSUPPORTED
+    assert _fwd(lib, dims=(4, 256, 96, 16, 2), mode=lib.MODE_PREFILL_MXFP8, ws_bytes=0) == lib.EUNSUPPORTED
+    n_bf16, n_mx = ctypes.c_size_t(), ctypes.c_size_t()
+    d = lib.Dims(4, 256, 128, 16, 2)
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), lib.MODE_PREFILL, ctypes.byref(n_bf16)) == lib.OK
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), lib.MODE_PREFILL_MXFP8, ctypes.byref(n_mx)) == lib.OK
+    assert n_mx.value > n_bf16.value  # room for the FP8 activations and their scales
+
+
+def test_quant_mxfp8_validation(lib):
+    f = lib._lib.moe_fp4_quant_mxfp8
+    assert f(None, 4, 64, FAKE, FAKE, None) == lib.EINVAL
+    assert f(FAKE, 0, 64, FAKE, FAKE, None) == lib.EINVAL
+    assert f(FAKE, 4, 48, FAKE, FAKE, None) == lib.EUNSUPPORTED
+    assert f(FAKE + 8, 4, 64, FAKE, FAKE, None) == lib.EALIGN
