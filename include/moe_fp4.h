@@ -63,12 +63,15 @@ extern "C" {
  * along I before w2 (see moe_fp4_quant_mxfp8); the matrix cores then take the
  * FP4 weights and their UE8M0 scales as stored.  Routing, the SwiGLU epilogue
  * (h rounded to bf16 first) and the combine are as in PREFILL.  Requires H and
- * I to be multiples of 128.  Its results differ from PREFILL by the FP8
- * quantisation of the activations (about 5e-2 relative), not by rounding. */
-/* DECODE supports T <= 16 (T <= 2 on row-contiguous dot kernels, more on MFMA
- * kernels) as far as the T activation rows and the T*k h rows it stages in LDS
- * fit 64 KiB; at H = 5120, I = 2304, k = 6 that is T <= 4.  I <= 3072 beyond
- * two tokens.  moe_fp4_workspace_size(dims, MOE_FP4_MODE_DECODE, ...) returns
+ * I to be multiples of 128, and the scale tensors s1, s3, s2 to have 4-byte
+ * aligned bases and expert strides (MOE_FP4_EALIGN otherwise).  Its results
+ * differ from PREFILL by the FP8 quantisation of the activations (about 5e-2
+ * relative), not by rounding. */
+/* DECODE takes one token on a dedicated path (H <= 8192; k * I / 32 <= 1024,
+ * i.e. I <= 5440 at k = 6), and 2 <= T <= 16 on MFMA kernels as far as the T
+ * activation rows and the T*k h rows they stage in LDS fit 64 KiB each and
+ * I <= 3072; at H = 5120, I = 2304, k = 6 that is T <= 2.
+ * moe_fp4_workspace_size(dims, MOE_FP4_MODE_DECODE, ...) returns
  * MOE_FP4_EUNSUPPORTED outside that range. */
 
 /* ---- forward flags */
@@ -92,7 +95,8 @@ typedef struct {
  * expert_stride[i] is the byte distance between consecutive experts of tensor
  * i (order w1, s1, w3, s3, w2, s2); 0 means dense stacking (the per-expert size).
  * Nibble tensors (w1, w3, w2) need 16-byte aligned bases and strides; scale
- * tensors have no alignment rule.  Supported scale bytes are 2..252. */
+ * tensors have no alignment rule except in MOE_FP4_MODE_PREFILL_MXFP8 (4
+ * bytes).  Supported scale bytes are 2..252. */
 typedef struct {
   const uint8_t *w1, *s1, *w3, *s3, *w2, *s2;
   int64_t expert_stride[6];

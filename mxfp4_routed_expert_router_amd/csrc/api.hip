@@ -59,10 +59,11 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
   if (rmode == MOE_FP4_MODE_PREFILL || mx) o = align_up(o + P * (size_t)d.H * 4);
   if (mx) {
-    L.xq = o;  o = align_up(o + (size_t)d.T * d.H);
-    L.xqs = o; o = align_up(o + (size_t)d.T * d.H / 32);
-    L.hq = o;  o = align_up(o + P * (size_t)d.I);
-    L.hqs = o; o = align_up(o + P * (size_t)d.I / 32);
+    const size_t Hp = mx8_padded(d.H), Ip = mx8_padded(d.I);
+    L.xq = o;  o = align_up(o + (size_t)d.T * Hp);
+    L.xqs = o; o = align_up(o + (size_t)d.T * Hp / 32);
+    L.hq = o;  o = align_up(o + P * Ip);
+    L.hqs = o; o = align_up(o + P * Ip / 32);
   }
   L.total = o;
   return L;
@@ -102,6 +103,11 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(w->w1, 16) ||
       !aligned(w->w3, 16) || !aligned(w->w2, 16) || stride[0] % 16 || stride[2] % 16 ||
       stride[4] % 16 || (h_out && !aligned(h_out, 4)))
+    return MOE_FP4_EALIGN;
+  // the MXFP8 GEMMs read the scales a dword at a time
+  if (rmode == MOE_FP4_MODE_PREFILL_MXFP8 &&
+      (!aligned(w->s1, 4) || !aligned(w->s3, 4) || !aligned(w->s2, 4) || stride[1] % 4 ||
+       stride[3] % 4 || stride[5] % 4))
     return MOE_FP4_EALIGN;
   const WsLayout L = layout(d, rmode);
   if (ws_bytes < L.total) return MOE_FP4_EWORKSPACE;

@@ -82,6 +82,9 @@ hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_combine(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);
+// Row length in codes of the MXFP8 prefill's quantised activations: K rounded
+// up to its K block (the padding holds zeros).
+size_t mx8_padded(int K);
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);
 

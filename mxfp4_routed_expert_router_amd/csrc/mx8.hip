@@ -61,29 +61,39 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   return __builtin_bit_cast(uint32_t, w);
 }
 
-__global__ void __launch_bounds__(256) quant_mx8_kernel(const uint16_t* __restrict__ src, size_t n8,
-                                                        uint8_t* __restrict__ codes,
+// Rows of K values in, rows of Kp >= K codes out (Kp / 32 scale bytes); the
+// codes and scales of columns K .. Kp-1 are written as zeros.
+__global__ void __launch_bounds__(256) quant_mx8_kernel(const uint16_t* __restrict__ src, int rows,
+                                                        int K, int Kp, uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
-  // n8 (8-value chunks) is a multiple of 4 and so is the grid stride: the four
-  // threads of a quad are always active together
+  // K and Kp are multiples of 32 and the grid stride is a multiple of 4: the
+  // four threads of a quad always hold one block, and take the same branch
+  const int c8 = Kp / 8;
+  const size_t n8 = (size_t)rows * c8;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (size_t)gridDim.x * blockDim.x) {
-    const u32x4 raw = ld16(src + i * 8);
-    float v[8];
+    const size_t r = i / c8;
+    const int c = (int)(i - r * c8) * 8;
+    uint2 out = {0u, 0u};
+    uint32_t se = 0;
+    if (c < K) {
+      const u32x4 raw = ld16(src + r * K + c);
+      float v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(raw[j] << 16);
-      v[2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(raw[j] << 16);
+        v[2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = quad_max(amax);
+      se = mx8_scale_byte(amax);
+      const float f = mx8_inv_scale(se);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = fminf(fmaxf(v[j] * f, -448.0f), 448.0f);
+      out = uint2{fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = quad_max(amax);
-    const uint32_t se = mx8_scale_byte(amax);
-    const float f = mx8_inv_scale(se);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = fminf(fmaxf(v[j] * f, -448.0f), 448.0f);
-    const uint2 out = {fp8x4(v[0], v[1], v[2], v[3]), fp8x4(v[4], v[5], v[6], v[7])};
     *reinterpret_cast<uint2*>(codes + i * 8) = out;
     if ((i & 3) == 0) scales[i / 4] = (uint8_t)se;
   }
@@ -101,28 +111,43 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(const uint16_t* __restri
 // slot that only that wave reads; the activation tile is shared, so one
 // barrier per K block orders its loads before the reads and the reads before
 // the slot is loaded again.
+//
+// A K block is 256 inputs: 128 bytes of each weight row, one whole cache line,
+// read by 8 lanes together.  (Half-line blocks leave each line to be fetched
+// in two pieces a block apart, which costs a sixth of the bandwidth.)  The
+// quantised activations have rows padded with zeros to a multiple of 256
+// inputs; in a last block of 128 inputs the weight lanes of the upper half
+// re-read the lower half, whose products with those zeros vanish.
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTok = 64;                 // tokens per pass
-constexpr int kKB = 128;                 // inputs per K block (4 scale groups, one MFMA)
+constexpr int kKB = 256;                 // inputs per K block (two MFMAs)
 constexpr int kRows13 = 16 * kWaves;     // w1/w3 rows per workgroup
 constexpr int kRows2 = 32 * kWaves;      // w2 rows per workgroup (two 16-row tiles per wave)
-constexpr int kStages = 5;               // K blocks resident in LDS (kStages - 1 in flight)
+constexpr int kStages = 3;               // K blocks resident in LDS (kStages - 1 in flight)
 constexpr int kTiles = 2;                // weight tiles per wave and block (M x row tiles)
-constexpr int kLoadsPerBlock = 2 * kTiles + 2;  // a wave's LDS loads per K block
+constexpr int kWLoads = 3 * kTiles;      // per tile: two 1 KB halves and the scales
+constexpr int kXLoads = 3;               // per wave holding tokens: two 1 KB quarters and scales
 
 struct SmemMx {
-  uint8_t w[kStages][kWaves][kTiles][1024];   // 16 rows x 64 bytes, lane l's chunk at 16 l
-  uint32_t ws[kStages][kWaves][kTiles][64];   // lane l: the scale dword of its row's block
+  uint8_t w[kStages][kWaves][kTiles][2048];   // 16 rows x 128 bytes, swizzled: see woff
   uint8_t x[kStages][kTok * kKB];             // E4M3 codes of 64 tokens, swizzled: see xoff
-  uint32_t xs[kStages][kWaves][64];           // lane l of wave w: token 8 w + (l & 7)'s 4 scales
+  uint32_t ws[kStages][kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
+  uint32_t xs[kStages][kWaves][16];           // token 8 w + i: scale dword d at 8 d + i
   int row[kTok];                              // source row of each staged token
 };
 
-// Byte offset in the activation tile of token t's 16-byte chunk c: wave t/8's
-// 1 KB, row t%8 of 128 bytes, chunk slot c ^ (t & 7).  The B reads of 16 lanes
-// (16 tokens, one chunk) then spread over the banks.
-__device__ __forceinline__ int xoff(int t, int c) { return t * 128 + ((c ^ (t & 7)) << 4); }
+// Byte offset in a weight tile of row r's 16-byte chunk c: rows 0-7 fill the
+// first 1 KB, rows 8-15 the second, 128 bytes a row, chunk slot c ^ (r & 7) ^
+// (r >> 3).  The A reads of 16 lanes (16 rows, one chunk) then hit 16
+// different 16-byte bank groups.
+__device__ __forceinline__ int woff(int r, int c) {
+  return (r >> 3) * 1024 + (r & 7) * 128 + ((c ^ (r & 7) ^ (r >> 3)) << 4);
+}
+// Byte offset in the activation tile of token t's 16-byte chunk c (of 16):
+// 256 bytes a token, chunk slot c ^ (t & 15), so the B reads of 16 lanes
+// (16 tokens, one chunk) spread over the banks.
+__device__ __forceinline__ int xoff(int t, int c) { return t * 256 + ((c ^ (t & 15)) << 4); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
@@ -139,31 +164,25 @@ template <int N>
 __device__ __forceinline__ void wait_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void wait_blocks_then_barrier(int blocks_after) {
-  switch (blocks_after) {  // blocks_after <= kStages - 2
-    case 0: wait_then_barrier<0>(); break;
-    case 1: wait_then_barrier<kLoadsPerBlock>(); break;
-    case 2: wait_then_barrier<2 * kLoadsPerBlock>(); break;
-    default: wait_then_barrier<3 * kLoadsPerBlock>(); break;
-  }
-}
-static_assert(kStages - 2 <= 3, "wait_blocks_then_barrier covers up to 3 blocks in flight");
+static_assert(kStages == 3, "the loop below waits for all but at most one block");
 
-// One pass over all K (a multiple of 128) for up to NT*16 staged token rows:
-// acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].  M * kRT == kTiles.
-// Weight rows past the end (act false) and tokens past nc load valid data whose
-// results are not stored.
+// One pass over all K (Kp = K rounded up to 256) for up to NT*16 staged token
+// rows: acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].
+// M * kRT == kTiles.  wrow0[m][rt] points at row 0 of the wave's 16-row tile
+// (inside the weights even for rows past the end, whose results are not
+// stored); srow0 at that row's scales.  Tokens past nc load token 0's row.
 template <int M, int kRT, int NT>
-__device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&wr)[M][kRT],
-                                             const uint8_t* const (&sr)[M][kRT],
-                                             const uint8_t* __restrict__ q,
+__device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&wrow0)[M][kRT],
+                                             const uint8_t* const (&srow0)[M][kRT], size_t wrow,
+                                             size_t srow, const uint8_t* __restrict__ q,
                                              const uint8_t* __restrict__ qs, int nc, int K,
                                              f32x4 (&acc)[M][kRT][NT]) {
   static_assert(M * kRT == kTiles, "tile count");
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c16 = lane & 15, kb = lane >> 4;
-  const int NB = K / kKB, KS = K / 32;
+  const int Kp = (K + kKB - 1) / kKB * kKB, NB = Kp / kKB, KSp = Kp / 32;
+  const bool half_tail = K != Kp;          // the last block holds 128 inputs
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -171,57 +190,89 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's activation chunk and scale dword (token rows past nc read token 0's)
-  const int xt = 8 * w + lane / 8, xc = (lane & 7) ^ (xt & 7);
-  const uint8_t* const xsrc = q + (size_t)sm.row[xt < nc ? xt : 0] * K + xc * 16;
+  // weight lanes: half h covers rows 8 h + lane / 8, lane's LDS slot lane % 8,
+  // which holds chunk (lane % 8) ^ (lane / 8) ^ h (see woff)
+  const int wr_r = lane >> 3, wr_c0 = (lane & 7) ^ wr_r, wr_c1 = wr_c0 ^ 1;
+  // scale lanes (lane < 32): tile row lane % 16, dword lane / 16
+  const int sc_r = c16, sc_d = kb & 1;
+  // activation lanes: quarter h covers tokens 8 w + 4 h + lane / 16, LDS slot
+  // lane % 16 holding chunk (lane % 16) ^ (t & 15)
+  const bool xw = 8 * w < 16 * NT;         // this wave stages tokens that are read
+  const uint8_t* xsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 8 * w + 4 * h + (lane >> 4);
+    xsrc[h] = q + (size_t)sm.row[t < nc ? t : 0] * Kp + ((c16 ^ (t & 15)) << 4);
+  }
   const int st = 8 * w + (lane & 7);
-  const uint8_t* const ssrc = qs + (size_t)sm.row[st < nc ? st : 0] * KS;
+  const uint8_t* const ssrc = qs + (size_t)sm.row[st < nc ? st : 0] * KSp + 4 * ((lane >> 3) & 1);
+
   auto issue = [&](int b, int s) {
+    const bool tail = half_tail && b == NB - 1;
+    // in a half block, chunks 4..7 (and scale dword 1) re-read chunks 0..3 (dword 0)
+    const int c0 = tail ? wr_c0 & 3 : wr_c0, c1 = tail ? wr_c1 & 3 : wr_c1;
+    const int d = tail ? 0 : sc_d;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        lds_load16(lds_addr(&sm.w[s][w][m * kRT + rt][0]), wr[m][rt] + (size_t)(4 * b + kb) * 16);
-        lds_load4(lds_addr(&sm.ws[s][w][m * kRT + rt][0]), sr[m][rt] + 4 * b);
+        uint8_t* const dst = &sm.w[s][w][m * kRT + rt][0];
+        const uint8_t* const src = wrow0[m][rt] + (size_t)b * 128;
+        lds_load16(lds_addr(dst), src + wr_r * wrow + 16 * c0);
+        lds_load16(lds_addr(dst + 1024), src + (8 + wr_r) * wrow + 16 * c1);
+        if (lane < 32) lds_load4(lds_addr(&sm.ws[s][w][m * kRT + rt][0]),
+                                 srow0[m][rt] + sc_r * srow + (size_t)b * 8 + 4 * d);
       }
-    lds_load16(lds_addr(&sm.x[s][w * 1024]), xsrc + (size_t)b * kKB);
-    lds_load4(lds_addr(&sm.xs[s][w][0]), ssrc + 4 * b);
+    if (xw) {
+      lds_load16(lds_addr(&sm.x[s][(8 * w) * kKB]), xsrc[0] + (size_t)b * kKB);
+      lds_load16(lds_addr(&sm.x[s][(8 * w + 4) * kKB]), xsrc[1] + (size_t)b * kKB);
+      if (lane < 16) lds_load4(lds_addr(&sm.xs[s][w][0]), ssrc + (size_t)b * 8);
+    }
   };
   auto compute = [&](int s) {
-    u32x4 A[M][kRT];
-    int sa[M][kRT];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][16 * lane]);
-        sa[m][rt] = (int)((sm.ws[s][w][m * kRT + rt][lane] >> (8 * kb)) & 0xFFu);
-      }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int t = 16 * nt + c16;
-      const u32x4 lo = ld16(&sm.x[s][xoff(t, kb)]), hi = ld16(&sm.x[s][xoff(t, 4 + kb)]);
-      const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int sb = (int)((sm.xs[s][t / 8][t & 7] >> (8 * kb)) & 0xFFu);
+    for (int j = 0; j < 2; ++j) {
+      u32x4 A[M][kRT];
+      int sa[M][kRT];
 #pragma unroll
       for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
-          const u32x4 a4 = A[m][rt];
-          const i32x8 Av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-          acc[m][rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              Av, B, acc[m][rt][nt], 4 /* A: E2M1 */, 0 /* B: E4M3 */, 0, sa[m][rt], 0, sb);
+          A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * j + kb)]);
+          sa[m][rt] = (int)((sm.ws[s][w][m * kRT + rt][16 * j + c16] >> (8 * kb)) & 0xFFu);
         }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int t = 16 * nt + c16;
+        const u32x4 lo = ld16(&sm.x[s][xoff(t, 8 * j + kb)]);
+        const u32x4 hi = ld16(&sm.x[s][xoff(t, 8 * j + 4 + kb)]);
+        const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        const int sb = (int)((sm.xs[s][t / 8][8 * j + (t & 7)] >> (8 * kb)) & 0xFFu);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            const u32x4 a4 = A[m][rt];
+            const i32x8 Av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+            acc[m][rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                Av, B, acc[m][rt][nt], 4 /* A: E2M1 */, 0 /* B: E4M3 */, 0, sa[m][rt], 0, sb);
+          }
+      }
     }
   };
 
   for (int b = 0; b < kStages - 1 && b < NB; ++b) issue(b, b);
   for (int b = 0; b < NB; ++b) {
     // block b's loads (this wave's) are done once at most the loads of the
-    // blocks issued after it are in flight; the barrier extends that to every
+    // block issued after it are in flight; the barrier extends that to every
     // wave's, and means every wave is done computing block b - 1
-    wait_blocks_then_barrier(min(kStages - 2, NB - 1 - b));
+    if (b + 1 == NB)
+      wait_then_barrier<0>();
+    else if (xw)
+      wait_then_barrier<kWLoads + kXLoads>();
+    else
+      wait_then_barrier<kWLoads>();
     if (b + kStages - 1 < NB) issue(b + kStages - 1, (b + kStages - 1) % kStages);  // into b-1's slot
     compute(b % kStages);
   }
@@ -243,7 +294,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
   const int rw = rtile * kRows13 + w * 16;
   const size_t wrow = (size_t)a.H / 2, srow = (size_t)a.H / 32;
   const bool act = rw < a.I;
-  const size_t ro = (size_t)(act ? rw + c16 : 0);
+  const size_t ro = (size_t)(act ? rw : 0);  // a tile past the end reads rows 0..15
   const uint8_t* const wr[2][1] = {{a.w1 + (size_t)e * a.stride[0] + ro * wrow},
                                    {a.w3 + (size_t)e * a.stride[2] + ro * wrow}};
   const uint8_t* const sr[2][1] = {{a.s1 + (size_t)e * a.stride[1] + ro * srow},
@@ -255,7 +306,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[2][1][NT];
-      gemm_pass_mx<2, 1, NT>(sm, wr, sr, a.xq, a.xqs, nc, a.H, acc);
+      gemm_pass_mx<2, 1, NT>(sm, wr, sr, wrow, srow, a.xq, a.xqs, nc, a.H, acc);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = 16 * nt + c16;
@@ -299,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
   for (int rt = 0; rt < 2; ++rt) {
     const int r = rw + 16 * rt;
     act[rt] = r < a.H;
-    const size_t ro = (size_t)(act[rt] ? r + c16 : 0);
+    const size_t ro = (size_t)(act[rt] ? r : 0);
     wr[0][rt] = a.w2 + (size_t)e * a.stride[4] + ro * wrow;
     sr[0][rt] = a.s2 + (size_t)e * a.stride[5] + ro * srow;
   }
@@ -310,7 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[1][2][NT];
-      gemm_pass_mx<1, 2, NT>(sm, wr, sr, a.hq, a.hqs, nc, a.I, acc);
+      gemm_pass_mx<1, 2, NT>(sm, wr, sr, wrow, srow, a.hq, a.hqs, nc, a.I, acc);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -336,15 +387,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
 
 }  // namespace
 
+namespace {
+unsigned quant_blocks(int rows, int Kp) {
+  return (unsigned)std::min<size_t>(((size_t)rows * Kp / 8 + 255) / 256, 4096);
+}
+}  // namespace
+
 hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream) {
-  const size_t n8 = (size_t)rows * K / 8;
-  size_t blocks = (n8 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, n8, codes,
-                     scales);
+  hipLaunchKernelGGL(quant_mx8_kernel, dim3(quant_blocks(rows, K)), dim3(256), 0, stream, src, rows,
+                     K, K, codes, scales);
   return hipGetLastError();
 }
+
+size_t mx8_padded(int K) { return (size_t)(K + kKB - 1) / kKB * kKB; }
 
 // x is quantised first (stage 1 timing covers it with the w1/w3 GEMM), h after
 // the w1/w3 GEMM (stage 2 covers it with the w2 GEMM).
@@ -352,16 +408,14 @@ hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream) {
   const hipEvent_t* ev = a.ev;
   const dim3 blk(kThreads);
   const int P = a.T * a.k;
-  const size_t nx8 = (size_t)a.T * a.H / 8, nh8 = (size_t)P * a.I / 8;
-  const unsigned bx = (unsigned)std::min<size_t>((nx8 + 255) / 256, 4096);
-  const unsigned bh = (unsigned)std::min<size_t>((nh8 + 255) / 256, 4096);
+  const int Hp = (int)mx8_padded(a.H), Ip = (int)mx8_padded(a.I);
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
-  launch_k(quant_mx8_kernel, dim3(bx), dim3(256), 0, stream, ev_start(ev, 1), (hipEvent_t) nullptr,
-           (const uint16_t*)a.x, nx8, a.xq, a.xqs);
+  launch_k(quant_mx8_kernel, dim3(quant_blocks(a.T, Hp)), dim3(256), 0, stream, ev_start(ev, 1),
+           (hipEvent_t) nullptr, (const uint16_t*)a.x, a.T, a.H, Hp, a.xq, a.xqs);
   launch_k(gemm13_mx_kernel, dim3(xcd_grid(t13)), blk, 0, stream, (hipEvent_t) nullptr,
            ev_stop(ev, 1), a);
-  launch_k(quant_mx8_kernel, dim3(bh), dim3(256), 0, stream, ev_start(ev, 2), (hipEvent_t) nullptr,
-           (const uint16_t*)a.h, nh8, a.hq, a.hqs);
+  launch_k(quant_mx8_kernel, dim3(quant_blocks(P, Ip)), dim3(256), 0, stream, ev_start(ev, 2),
+           (hipEvent_t) nullptr, (const uint16_t*)a.h, P, a.I, Ip, a.hq, a.hqs);
   launch_k(gemm2_mx_kernel, dim3(xcd_grid(t2)), blk, 0, stream, (hipEvent_t) nullptr, ev_stop(ev, 2),
            a);
   return launch_combine(a, stream);

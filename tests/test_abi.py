@@ -205,6 +205,18 @@ def test_mxfp8_mode_validation(lib):
     assert n_mx.value > n_bf16.value  # room for the FP8 activations and their scales
 
 
+def test_mxfp8_scale_alignment(lib):
+    """The MXFP8 GEMMs read scales a dword at a time: bases and strides 4-aligned."""
+    dims = (4, 256, 128, 16, 2)
+    m = lib.MODE_PREFILL_MXFP8
+    assert _fwd(lib, dims=dims, mode=m, w=_weights(lib, s1=FAKE + 4), ws_bytes=0) == lib.EWORKSPACE
+    assert _fwd(lib, dims=dims, mode=m, w=_weights(lib, s3=FAKE + 2), ws_bytes=0) == lib.EALIGN
+    assert _fwd(lib, dims=dims, mode=m, w=_weights(lib, strides=(0, 0, 0, 0, 0, 1026)),
+                ws_bytes=0) == lib.EALIGN
+    assert _fwd(lib, dims=dims, mode=lib.MODE_PREFILL, w=_weights(lib, s3=FAKE + 2), ws_bytes=0) \
+        == lib.EWORKSPACE
+
+
 def test_quant_mxfp8_validation(lib):
     f = lib._lib.moe_fp4_quant_mxfp8
     assert f(None, 4, 64, FAKE, FAKE, None) == lib.EINVAL
