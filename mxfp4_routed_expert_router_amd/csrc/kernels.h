@@ -79,6 +79,11 @@ bool decode_fuses_route(int T, int H, int I, int E, int k);  // decode routes in
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream);
+// LDS-fed bf16 prefill GEMMs: taken when K is a multiple of 256 and the n
+// scale tensors have 4-byte aligned bases and strides.
+bool prefill_lds_takes(int K, const uint8_t* const* scales, const int64_t* strides, int n);
+hipError_t launch_gemm13_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+hipError_t launch_gemm2_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_combine(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,
                             hipStream_t stream);

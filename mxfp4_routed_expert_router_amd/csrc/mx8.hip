@@ -18,6 +18,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe_fp4 {
 namespace {
@@ -101,16 +102,10 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------------ grouped GEMM
 // Every operand of the main loop reaches LDS by direct global->LDS loads
-// (global_load_lds, the destination given in M0; lane l's 16 or 4 bytes land at
-// M0 + 16 l or + 4 l), kStages K blocks deep, so the blocks in flight cost no
-// registers.  The loads are issued from inline assembly, and the loop waits for
-// them itself (s_waitcnt vmcnt(n) with n = this wave's loads still allowed in
-// flight): the compiler cannot tell which LDS block such a load writes, and
-// would otherwise wait for all of them before every LDS read.  The loop has no
-// other global loads, so the count is exact.  Each wave's weight chunks go to a
-// slot that only that wave reads; the activation tile is shared, so one
-// barrier per K block orders its loads before the reads and the reads before
-// the slot is loaded again.
+// (lds_dma.h), kStages K blocks deep, so the blocks in flight cost no
+// registers.  Each wave's weight chunks go to a slot that only that wave
+// reads; the activation tile is shared, so one barrier per K block orders its
+// loads before the reads and the reads before the slot is loaded again.
 //
 // A K block is 256 inputs: 128 bytes of each weight row, one whole cache line,
 // read by 8 lanes together.  (Half-line blocks leave each line to be fetched
@@ -137,33 +132,11 @@ struct SmemMx {
   int row[kTok];                              // source row of each staged token
 };
 
-// Byte offset in a weight tile of row r's 16-byte chunk c: rows 0-7 fill the
-// first 1 KB, rows 8-15 the second, 128 bytes a row, chunk slot c ^ (r & 7) ^
-// (r >> 3).  The A reads of 16 lanes (16 rows, one chunk) then hit 16
-// different 16-byte bank groups.
-__device__ __forceinline__ int woff(int r, int c) {
-  return (r >> 3) * 1024 + (r & 7) * 128 + ((c ^ (r & 7) ^ (r >> 3)) << 4);
-}
 // Byte offset in the activation tile of token t's 16-byte chunk c (of 16):
 // 256 bytes a token, chunk slot c ^ (t & 15), so the B reads of 16 lanes
 // (16 tokens, one chunk) spread over the banks.
 __device__ __forceinline__ int xoff(int t, int c) { return t * 256 + ((c ^ (t & 15)) << 4); }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-__device__ __forceinline__ void lds_load16(uint32_t lds_base, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
-}
-__device__ __forceinline__ void lds_load4(uint32_t lds_base, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(g) : "memory");
-}
-// Wait until at most N of this wave's LDS loads are in flight, then meet the
-// workgroup.  The memory clobber keeps the compiler's LDS accesses on their side.
-template <int N>
-__device__ __forceinline__ void wait_then_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 static_assert(kStages == 3, "the loop below waits for all but at most one block");
 
 // One pass over all K (Kp = K rounded up to 256) for up to NT*16 staged token
@@ -190,9 +163,8 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weight lanes: half h covers rows 8 h + lane / 8, lane's LDS slot lane % 8,
-  // which holds chunk (lane % 8) ^ (lane / 8) ^ h (see woff)
-  const int wr_r = lane >> 3, wr_c0 = (lane & 7) ^ wr_r, wr_c1 = wr_c0 ^ 1;
+  // weight lanes: half h covers rows 8 h + lane / 8 (see woff)
+  const int wr_r = lane >> 3, wr_c0 = wtile_chunk(lane, 0), wr_c1 = wtile_chunk(lane, 1);
   // scale lanes (lane < 32): tile row lane % 16, dword lane / 16
   const int sc_r = c16, sc_d = kb & 1;
   // activation lanes: quarter h covers tokens 8 w + 4 h + lane / 16, LDS slot

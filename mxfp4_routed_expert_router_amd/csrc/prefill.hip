@@ -1,4 +1,5 @@
-// Prefill path: a chunk of many tokens, so each expert's weights are read once
+// Prefill path (register-fed GEMMs here; prefill_lds.hip holds LDS-fed ones,
+// used where K is a multiple of 256): a chunk of many tokens, so each expert's weights are read once
 // and reused by every token routed to it -- the reason prefill is far faster per
 // token than decode (ai-shiz.ru page, section on prefill; the 10100.com page uses
 // 2048-token prefill chunks, section on KV and prefill workspace).  Per expert
@@ -316,8 +317,16 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
   const dim3 blk(kThreads);
   const hipEvent_t* ev = a.ev;
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
-  launch_k(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, ev_start(ev, 1), ev_stop(ev, 1), a);
-  launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+  const uint8_t* const s13[2] = {a.s1, a.s3};
+  const int64_t st13[2] = {a.stride[1], a.stride[3]};
+  if (prefill_lds_takes(a.H, s13, st13, 2))
+    launch_gemm13_lds(a, stream, ev_start(ev, 1), ev_stop(ev, 1));
+  else
+    launch_k(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, ev_start(ev, 1), ev_stop(ev, 1), a);
+  if (prefill_lds_takes(a.I, &a.s2, &a.stride[5], 1))
+    launch_gemm2_lds(a, stream, ev_start(ev, 2), ev_stop(ev, 2));
+  else
+    launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   return launch_combine(a, stream);
 }
 

@@ -251,6 +251,41 @@ def test_expert_blob_layout(moe, orc):
     check_y(y.cpu().numpy(), ref["y"], "blob layout")
 
 
+@pytest.mark.parametrize("shift", [0, 1, 2])
+def test_prefill_scale_alignment(moe, orc, shift):
+    """H and I multiples of 256: 4-byte aligned scale tensors take the LDS-fed
+    GEMMs, scale tensors at an odd or 2 mod 4 offset the register-fed ones.
+    Both are checked against the oracle, h included."""
+    import torch
+    say(f"prefill with scale tensors shifted by {shift} bytes")
+    rng = np.random.default_rng(23 + shift)
+    T, H, I, E, k = 40, 512, 256, 6, 3
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    sizes = [experts[0][n].size for n in names]
+    offs, o = [], 0
+    for n, sz in zip(names, sizes):
+        o = (o + 15) // 16 * 16 + (shift if n.startswith("s") else 0)
+        offs.append(o)
+        o += sz
+    buf = np.zeros((E, (o + 255) // 256 * 256), np.uint8)
+    for e in range(E):
+        for n, off, sz in zip(names, offs, sizes):
+            buf[e, off:off + sz] = experts[e][n].ravel()
+    dbuf = torch.from_numpy(buf).cuda()
+    views = {n: dbuf.view(-1)[off:] for n, off in zip(names, offs)}
+    w = moe.ExpertWeights(strides=(buf.shape[1],) * 6, I=I, **views)
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True)
+    y, h, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k,
+                                            mode=moe.MODE_PREFILL)
+    torch.cuda.synchronize()
+    what = f"prefill scale shift {shift}"
+    check_h(host_bits(h), ref["h"], ref["hpre"], ref["hbound"], what)
+    check_y(y.cpu().numpy(), ref["y"], what)
+
+
 def test_prenorm(moe, orc):
     import torch
     rng = np.random.default_rng(4)
