@@ -67,8 +67,8 @@ extern "C" {
  * aligned bases and expert strides (MOE_FP4_EALIGN otherwise).  Its results
  * differ from PREFILL by the FP8 quantisation of the activations (about 5e-2
  * relative), not by rounding. */
-/* DECODE takes one token on a dedicated path (H <= 8192; k * I / 32 <= 1024,
- * i.e. I <= 5440 at k = 6), and 2 <= T <= 16 on MFMA kernels as far as the T
+/* DECODE takes one token on a dedicated path (H <= 8192 and k * I / 32 <=
+ * 1024), and 2 <= T <= 16 on MFMA kernels as far as the T
  * activation rows and the T*k h rows they stage in LDS fit 64 KiB each and
  * I <= 3072; at H = 5120, I = 2304, k = 6 that is T <= 2.
  * moe_fp4_workspace_size(dims, MOE_FP4_MODE_DECODE, ...) returns

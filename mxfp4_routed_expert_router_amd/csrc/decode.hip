@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(kThreads) gemv2_combine_kernel(LayerArgs a) {
 constexpr int kOneMaxXG = 4;      // x groups per lane: H <= 64 * 32 * 4
 constexpr int kOneMaxPL = 2;      // (slot, group) pairs per lane in the w2 kernel
 constexpr int kOneRowsMax = 64;   // w2 rows per workgroup
-constexpr int kOneDP = 8;         // w2 rows in flight per wave
+constexpr int kOneDP = 4;         // w2 rows in flight per wave (measured best of 2..12)
 
 int one_xg(int H) { return (H / 32 + kWave - 1) / kWave; }
 int one_pl(int I, int k) {

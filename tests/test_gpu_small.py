@@ -122,6 +122,9 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (17, 224, 160, 9, 4),     # two decode token tiles
     (32, 256, 192, 6, 6),     # every expert takes all 32 tokens
     (16, 256, 128, 20, 2),    # a full 16-token decode tile
+    (1, 352, 96, 7, 3),       # one token, ragged groups
+    (1, 256, 2080, 10, 5),    # one token, 65 groups per w2 row
+    (1, 256, 1024, 16, 16),   # one token, k = 16: k * I / 32 at the one-token path's limit
 ]
 
 
