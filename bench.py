@@ -189,6 +189,47 @@ def main():
     us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
     log(f"decode eager (one Python call per step): {us_eager:.2f} us/token")
 
+    # ---------------------------------------------------------------- decode from the router step
+    # The same steps with the logits computed on the GPU from x and a bf16
+    # router weight [E, H] (moe_fp4_forward_routed), and the router kernel
+    # alone; both as graph replays.
+    wr_d = torch.from_numpy(synth.gen_router(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    lg_out = torch.empty((1, wl.E), dtype=torch.float32, device=dev)
+
+    def step_routed(i):
+        j = i % n_gen
+        moe.moe_fp4_forward_routed(x_d[j:j + 1], wr_d, w, wl.k, y=y_d[j:j + 1], workspace=ws)
+
+    def step_router(i):
+        j = i % n_gen
+        moe.moe_fp4_router_logits(x_d[j:j + 1], wr_d, out=lg_out)
+
+    def graph_us(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(args.warmup + i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.steps
+
+    us_routed = graph_us(step_routed)
+    us_router = graph_us(step_router)
+    router_bytes = wl.E * wl.H * 2 + wl.H * 2 + wl.E * 4
+    routed = {"us_per_token": us_routed, "router_us": us_router,
+              "router_bytes": router_bytes, "router_GBps": router_bytes / (us_router * 1e-6) / 1e9,
+              "note": "x -> router logits (bf16 router weight [384, 5120], 3.9 MB) -> the same "
+                      "layer; graph replay; router_us: the router kernel alone, one call per "
+                      "step in a graph"}
+    log(f"decode with the router step: {us_routed:.2f} us/token; router kernel alone "
+        f"{us_router:.2f} us ({routed['router_GBps']:.0f} GB/s)")
+
     # ---------------------------------------------------------------- decode, cold caches
     # A read-only flush (summing a 1 GiB buffer) between steps evicts the
     # experts from L2 and the MALL without leaving dirty lines whose write-back
@@ -312,6 +353,7 @@ def main():
         "us_per_token_with_events": ms_per_step_prof * 1e3 / wl.T,
         "us_per_token_eager": us_eager,
         "cold": cold,
+        "decode_routed": routed,
         "prefill": prefill,
         "prefill_mxfp8": prefill_mx,
         "cpu_baseline": cpu,

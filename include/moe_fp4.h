@@ -168,6 +168,28 @@ int moe_fp4_forward_profiled(const moe_fp4_dims *dims, const uint16_t *x, const 
                              size_t ws_bytes, hipStream_t stream, hipEvent_t *events,
                              int n_events);
 
+/* Router logits, the step before routing (the router is one of the layer's
+ * resident weights: 10100.com page, section on the expert-capacity
+ * bottleneck; its format is not given and is taken as bf16):
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c]
+ *   x         [T][H] bf16 bits, 16-byte aligned (dims->T, dims->H)
+ *   w_router  [E][H] bf16 bits, row-major, 16-byte aligned (dims->E)
+ *   logits    [T][E] fp32, 4-byte aligned
+ * dims->I and dims->k are not used.  bf16 products are exact in fp32 and are
+ * summed in fp32 in a fixed order: the same inputs give the same bits.
+ * Errors: EINVAL (null, sizes < 1), EUNSUPPORTED (T > 65535, E > 1024, H not a
+ * multiple of 32 in [32, 16384]), EALIGN, EHIP. */
+int moe_fp4_router_logits(const moe_fp4_dims *dims, const uint16_t *x, const uint16_t *w_router,
+                          float *logits, hipStream_t stream);
+
+/* As moe_fp4_forward, with the logits computed from x and w_router (as
+ * moe_fp4_router_logits does) into the workspace first, in place of a logits
+ * argument.  Same workspace size.  w_router [E][H] bf16, 16-byte aligned.
+ * Errors: as moe_fp4_forward (EINVAL for a null w_router, EALIGN if misaligned). */
+int moe_fp4_forward_routed(const moe_fp4_dims *dims, const uint16_t *x, const uint16_t *w_router,
+                           const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* Pre-normalisation for a residual stack of layers:
  *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
  *   x [T][H] fp32, u [T][H] bf16 bits.
@@ -175,7 +197,6 @@ int moe_fp4_forward_profiled(const moe_fp4_dims *dims, const uint16_t *x, const 
 int moe_fp4_prenorm_bf16(const float *x, uint16_t *u, int32_t T, int32_t H, float eps,
                          hipStream_t stream);
 
-/* Static description of a status code (never NULL). */
 /* MXFP8 quantisation (OCP MX, blocks of 32 consecutive values of a row):
  *   src     [rows][K] bf16 bits, 16-byte aligned, K a multiple of 32
  *   codes   [rows][K] E4M3 codes, 8-byte aligned
@@ -188,6 +209,7 @@ int moe_fp4_prenorm_bf16(const float *x, uint16_t *u, int32_t T, int32_t H, floa
 int moe_fp4_quant_mxfp8(const uint16_t *src, int32_t rows, int32_t K, uint8_t *codes,
                         uint8_t *scales, hipStream_t stream);
 
+/* Static description of a status code (never NULL). */
 const char *moe_fp4_status_string(int status);
 
 #ifdef __cplusplus

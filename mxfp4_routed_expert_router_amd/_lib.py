@@ -59,9 +59,12 @@ def _load():
     lib.moe_fp4_prenorm_bf16.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, P]
     lib.moe_fp4_status_string.argtypes = [I32]
     lib.moe_fp4_quant_mxfp8.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.moe_fp4_router_logits.argtypes = [ctypes.POINTER(Dims), P, P, P, P]
+    lib.moe_fp4_forward_routed.argtypes = lib.moe_fp4_forward.argtypes
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
-              "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16"):
+              "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
+              "moe_fp4_router_logits", "moe_fp4_forward_routed"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -274,6 +277,50 @@ def moe_fp4_prenorm_bf16(x: torch.Tensor, eps: float = 1e-6,
     _check(_lib.moe_fp4_prenorm_bf16(x.data_ptr(), u.data_ptr(), T, H, eps, _stream(x)),
            "moe_fp4_prenorm_bf16")
     return u
+
+
+def moe_fp4_router_logits(x: torch.Tensor, w_router: torch.Tensor,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Router logits [T, E] fp32 = x [T, H] . w_router [E, H]^T (both bf16)."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _need(w_router, "w_router", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("x and w_router disagree on the hidden size")
+    lg = out if out is not None else torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _need(lg, "logits", (torch.float32,), 2)
+    _check(_lib.moe_fp4_router_logits(ctypes.byref(Dims(T, H, 0, E, 0)), x.data_ptr(),
+                                      w_router.data_ptr(), lg.data_ptr(), _stream(x)),
+           "moe_fp4_router_logits")
+    return lg
+
+
+def moe_fp4_forward_routed(x: torch.Tensor, w_router: torch.Tensor, weights: ExpertWeights, k: int,
+                           y: Optional[torch.Tensor] = None, mode: int = MODE_AUTO,
+                           accumulate: bool = False, workspace: Optional[torch.Tensor] = None):
+    """As moe_fp4_forward, with the logits computed from x and w_router [E, H] (bf16)."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _need(w_router, "w_router", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("x and w_router disagree on the hidden size")
+    I = weights.intermediate()
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs y")
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    need = moe_fp4_workspace_size(T, H, I, E, k, mode)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws = weights.as_struct()
+    _check(_lib.moe_fp4_forward_routed(ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(),
+                                       w_router.data_ptr(), ctypes.byref(ws), y.data_ptr(), mode,
+                                       ACCUMULATE if accumulate else 0, workspace.data_ptr(),
+                                       workspace.numel(), _stream(x)), "moe_fp4_forward_routed")
+    return y
 
 
 def moe_fp4_quant_mxfp8(x: torch.Tensor):

@@ -36,14 +36,15 @@ int resolve_mode(const moe_fp4_dims& d, int mode) {
 
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
-  size_t idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h, ypair, xq,
-      xqs, hq, hqs, total;
+  size_t logits, idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h,
+      ypair, xq, xqs, hq, hqs, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
   const size_t P = (size_t)d.T * d.k;
   WsLayout L{};
   size_t o = 0;
+  L.logits = o;   o = align_up(o + (size_t)d.T * d.E * 4);  // moe_fp4_forward_routed
   L.idx = o;      o = align_up(o + P * 4);
   L.gates = o;    o = align_up(o + P * 4);
   L.counts = o;   o = align_up(o + (size_t)d.E * 4);
@@ -76,11 +77,13 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Exactly one of logits and w_router is given; with w_router the logits are
+// computed into the workspace first.
 int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
-                 const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
-                 size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
+                 const uint16_t* w_router, const moe_fp4_weights* w, float* y, int mode, int flags,
+                 void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                  moe_fp4_route_out* route_out, const hipEvent_t* events) {
-  if (!dims || !x || !logits || !w || !y || !ws) return MOE_FP4_EINVAL;
+  if (!dims || !x || !(logits || w_router) || !w || !y || !ws) return MOE_FP4_EINVAL;
   if (!w->w1 || !w->s1 || !w->w3 || !w->s3 || !w->w2 || !w->s2) return MOE_FP4_EINVAL;
   if (route_out && (!route_out->topk_idx || !route_out->gates || !route_out->counts ||
                     !route_out->offsets || !route_out->sorted_pairs || !route_out->pair_slot))
@@ -102,7 +105,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   for (int i = 0; i < 6; ++i) stride[i] = w->expert_stride[i] ? w->expert_stride[i] : per[i];
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(w->w1, 16) ||
       !aligned(w->w3, 16) || !aligned(w->w2, 16) || stride[0] % 16 || stride[2] % 16 ||
-      stride[4] % 16 || (h_out && !aligned(h_out, 4)))
+      stride[4] % 16 || (h_out && !aligned(h_out, 4)) || (w_router && !aligned(w_router, 16)))
     return MOE_FP4_EALIGN;
   // the MXFP8 GEMMs read the scales a dword at a time
   if (rmode == MOE_FP4_MODE_PREFILL_MXFP8 &&
@@ -112,6 +115,12 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   const WsLayout L = layout(d, rmode);
   if (ws_bytes < L.total) return MOE_FP4_EWORKSPACE;
 
+  if (w_router) {
+    float* const lg = at<float>(ws, L.logits);
+    if (launch_router_logits(x, w_router, lg, d.T, d.H, d.E, stream) != hipSuccess)
+      return MOE_FP4_EHIP;
+    logits = lg;
+  }
   RouteArgs r{};
   r.logits = logits;
   r.T = d.T; r.E = d.E; r.k = d.k;
@@ -213,8 +222,29 @@ int moe_fp4_route(const moe_fp4_dims* dims, const float* logits, moe_fp4_route_o
 int moe_fp4_forward(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
                     const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, nullptr, nullptr,
-                      nullptr);
+  return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                      nullptr, nullptr);
+}
+
+int moe_fp4_forward_routed(const moe_fp4_dims* dims, const uint16_t* x, const uint16_t* w_router,
+                           const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (!w_router) return MOE_FP4_EINVAL;
+  return forward_impl(dims, x, nullptr, w_router, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                      nullptr, nullptr);
+}
+
+int moe_fp4_router_logits(const moe_fp4_dims* dims, const uint16_t* x, const uint16_t* w_router,
+                          float* logits, hipStream_t stream) {
+  if (!dims || !x || !w_router || !logits) return MOE_FP4_EINVAL;
+  const moe_fp4_dims d = *dims;
+  if (d.T < 1 || d.H < 1 || d.E < 1) return MOE_FP4_EINVAL;
+  if (d.T > 65535 || d.E > kMaxExperts || d.H < 32 || d.H > 16384 || d.H % 32)
+    return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(logits, 4)) return MOE_FP4_EALIGN;
+  return launch_router_logits(x, w_router, logits, d.T, d.H, d.E, stream) == hipSuccess
+             ? MOE_FP4_OK
+             : MOE_FP4_EHIP;
 }
 
 int moe_fp4_forward_profiled(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
@@ -224,16 +254,16 @@ int moe_fp4_forward_profiled(const moe_fp4_dims* dims, const uint16_t* x, const 
   if (!events || n_events < 2 * kStages) return MOE_FP4_EINVAL;
   for (int i = 0; i < 2 * kStages; ++i)
     if (!events[i]) return MOE_FP4_EINVAL;
-  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, nullptr, nullptr,
-                      events);
+  return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                      nullptr, events);
 }
 
 int moe_fp4_forward_debug(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
                           const moe_fp4_weights* w, float* y, int mode, int flags, void* ws,
                           size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                           moe_fp4_route_out* route_out) {
-  return forward_impl(dims, x, logits, w, y, mode, flags, ws, ws_bytes, stream, h_out, route_out,
-                      nullptr);
+  return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, h_out,
+                      route_out, nullptr);
 }
 
 int moe_fp4_prenorm_bf16(const float* x, uint16_t* u, int32_t T, int32_t H, float eps,

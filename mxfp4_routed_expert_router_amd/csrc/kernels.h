@@ -91,6 +91,8 @@ hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes
 // up to its K block (the padding holds zeros).
 size_t mx8_padded(int K);
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,
+                                int E, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);
 
 }  // namespace moe_fp4

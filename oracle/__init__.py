@@ -60,6 +60,8 @@ class Oracle:
         lib.oracle_route.argtypes = [ctypes.c_int] * 3 + [_f32p, _i32p, _f32p]
         lib.oracle_permute.restype = None
         lib.oracle_permute.argtypes = [ctypes.c_int] * 3 + [_i32p] * 5
+        lib.oracle_router_logits.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4
+        lib.oracle_router_logits.restype = None
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
@@ -102,6 +104,20 @@ class Oracle:
         g = np.empty((T, k), np.float32)
         self.lib.oracle_route(T, E, k, logits, idx, g)
         return idx, g
+
+    def router_logits(self, x_bits: np.ndarray, w_bits: np.ndarray):
+        """Router logits x . wr^T in double for bf16 bits x [T, H] and wr [E, H],
+        and the fp32 summation bound of each (see oracle_router_logits)."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+        T, H = x_bits.shape
+        E = w_bits.shape[0]
+        assert w_bits.shape[1] == H
+        lg = np.empty((T, E), np.float64)
+        b = np.empty((T, E), np.float64)
+        self.lib.oracle_router_logits(T, H, E, x_bits.ctypes.data, w_bits.ctypes.data,
+                                      lg.ctypes.data, b.ctypes.data)
+        return lg, b
 
     def permute(self, idx: np.ndarray, E: int):
         idx = np.ascontiguousarray(idx, dtype=np.int32)

@@ -216,6 +216,33 @@ void oracle_route(int T, int E, int k, const float *logits, int32_t *idx, float 
     free(keys);
 }
 
+/* Router logits (the step before routing; the router is one of the layer's
+ * resident dense weights, 10100.com page, section on the MoE expert-capacity
+ * bottleneck; its format is not given and is read as bf16):
+ *   logits[t][e] = sum_c x[t][c] * wr[e][c], x [T][H] and wr [E][H] bf16 bits.
+ * Summed in double (bf16 products are exact).  bound[t][e] is the standard
+ * bound on an fp32 evaluation of the same sum in any order,
+ * gamma_H * sum_c |x[t][c] * wr[e][c]| with gamma_H = H u / (1 - H u),
+ * u = 2^-24 (Higham). */
+void oracle_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t *wr,
+                          double *logits, double *bound) {
+    const double u = ldexp(1.0, -24), gam = H * u / (1.0 - H * u);
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0, a = 0.0;
+            const int n = MUT(17) ? H - 1 : H;
+            for (int c = 0; c < n; ++c) {
+                const double xv = oracle_bf16_to_double(x[(size_t)t * H + c]);
+                const double wv = oracle_bf16_to_double(
+                    MUT(18) ? wr[((size_t)c * E + e) % ((size_t)E * H)] : wr[(size_t)e * H + c]);
+                s += xv * wv;
+                a += fabs(xv * wv);
+            }
+            logits[(size_t)t * E + e] = s;
+            bound[(size_t)t * E + e] = gam * a;
+        }
+}
+
 /* Token permutation grouped by expert.  Pair p = t*k + j.  counts[e] = pairs
  * routed to e; offsets = exclusive prefix sum (E+1 entries); sorted_pairs lists
  * pair ids expert by expert, ascending p inside an expert; pair_slot is the

@@ -174,6 +174,13 @@ def logit_bias(wl: Workload, layer: int = 0) -> np.ndarray:
     return -ZIPF_ALPHA * wl.zipf_s * np.log(r.astype(np.float64))
 
 
+def gen_router(wl: Workload, layer: int = 0) -> np.ndarray:
+    """Router weight for the router-logits step: [E, H] bf16 bit patterns of
+    N(0, 1/H) draws, so that logits of N(0,1) activations are about N(0,1)."""
+    w = _rng(wl.input_seed, 4, layer).standard_normal((wl.E, wl.H), dtype=np.float32)
+    return f32_to_bf16_bits(w * np.float32(1.0 / np.sqrt(wl.H)))
+
+
 def gen_logits(wl: Workload, step: int = 0, layer: int = 0) -> np.ndarray:
     """Router logits for one step: [T, E] float32 = N(0,1) noise + per-expert bias."""
     noise = _rng(wl.input_seed, 0, step, layer).standard_normal((wl.T, wl.E), dtype=np.float32)

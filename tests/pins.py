@@ -450,7 +450,47 @@ def pin_mx8_forward(o):
         assert np.allclose(out["y"][t], acc.astype(np.float32), rtol=1e-6, atol=1e-6 * np.abs(acc).max())
 
 
+def pin_router_numpy(o):
+    """Router logits against numpy's float64 matmul of the same bf16 values, at
+    shapes that are not multiples of anything (T=5, H=224, E=19)."""
+    rng = np.random.default_rng(61)
+    T, H, E = 5, 224, 19
+    x = rand_bf16(rng, (T, H))
+    w = rand_bf16(rng, (E, H), scale=1.0 / np.sqrt(H))
+    lg, b = o.router_logits(x, w)
+    ref = bf16_to_f64(x) @ bf16_to_f64(w).T
+    assert np.allclose(lg, ref, rtol=0, atol=1e-12 * np.abs(ref).max()), np.abs(lg - ref).max()
+    assert np.all(b > 0)
+
+
+def pin_router_onehot(o):
+    """x a unit vector at column c gives logits[e] = wr[e][c] exactly, for the
+    first, a middle and the last column: pins operand orientation and that
+    every input is summed."""
+    rng = np.random.default_rng(62)
+    H, E = 96, 7
+    w = rand_bf16(rng, (E, H))
+    one = o.to_bf16(1.0)
+    for c in (0, 37, H - 1):
+        x = np.zeros((1, H), np.uint16)
+        x[0, c] = one
+        lg, _ = o.router_logits(x, w)
+        assert np.array_equal(lg[0], bf16_to_f64(w[:, c])), c
+
+
+def pin_router_bound(o):
+    """Closed form: x and wr all ones give logits = H exactly and the bound
+    gamma_H * H, gamma_H = H 2^-24 / (1 - H 2^-24)."""
+    H, E = 5120, 3
+    one = o.to_bf16(1.0)
+    x = np.full((2, H), one, np.uint16)
+    w = np.full((E, H), one, np.uint16)
+    lg, b = o.router_logits(x, w)
+    u = 2.0 ** -24
+    assert np.all(lg == H) and np.allclose(b, H * u / (1 - H * u) * H, rtol=1e-15)
+
+
 ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pin_router_special,
             pin_permute, pin_probe_w1, pin_probe_w2, pin_closed_form_swiglu, pin_prenorm,
             pin_brute, pin_numpy_matmul, pin_e4m3_table, pin_mx8_quant, pin_mx8_special,
-            pin_mx8_forward]
+            pin_mx8_forward, pin_router_numpy, pin_router_onehot, pin_router_bound]

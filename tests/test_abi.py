@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
               "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string",
-              "moe_fp4_quant_mxfp8"):
+              "moe_fp4_quant_mxfp8", "moe_fp4_router_logits", "moe_fp4_forward_routed"):
         assert n in names
 
 
@@ -223,3 +223,32 @@ def test_quant_mxfp8_validation(lib):
     assert f(FAKE, 0, 64, FAKE, FAKE, None) == lib.EINVAL
     assert f(FAKE, 4, 48, FAKE, FAKE, None) == lib.EUNSUPPORTED
     assert f(FAKE + 8, 4, 64, FAKE, FAKE, None) == lib.EALIGN
+
+
+def test_router_logits_validation(lib):
+    f = lib._lib.moe_fp4_router_logits
+    d = ctypes.byref(lib.Dims(4, 256, 0, 16, 0))
+    assert f(None, FAKE, FAKE, FAKE, None) == lib.EINVAL
+    assert f(d, None, FAKE, FAKE, None) == lib.EINVAL
+    assert f(d, FAKE, None, FAKE, None) == lib.EINVAL
+    assert f(d, FAKE, FAKE, None, None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(0, 256, 0, 16, 0)), FAKE, FAKE, FAKE, None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(4, 250, 0, 16, 0)), FAKE, FAKE, FAKE, None) == lib.EUNSUPPORTED
+    assert f(ctypes.byref(lib.Dims(4, 256, 0, 2000, 0)), FAKE, FAKE, FAKE, None) == lib.EUNSUPPORTED
+    assert f(d, FAKE + 8, FAKE, FAKE, None) == lib.EALIGN
+    assert f(d, FAKE, FAKE + 2, FAKE, None) == lib.EALIGN
+    assert f(d, FAKE, FAKE, FAKE + 2, None) == lib.EALIGN
+
+
+def test_forward_routed_validation(lib):
+    """Same checks as moe_fp4_forward, the router weight in place of the logits."""
+    f = lib._lib.moe_fp4_forward_routed
+    d = lib.Dims(4, 256, 128, 16, 2)
+    w = _weights(lib)
+    n = ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == lib.OK
+    args = lambda wr, ws_bytes: (ctypes.byref(d), FAKE, wr, ctypes.byref(w), FAKE, 0, 0, FAKE,
+                                 ws_bytes, None)
+    assert f(*args(None, n.value)) == lib.EINVAL
+    assert f(*args(FAKE + 2, n.value)) == lib.EALIGN
+    assert f(*args(FAKE, 0)) == lib.EWORKSPACE

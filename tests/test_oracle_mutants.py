@@ -5,7 +5,8 @@ swapped nibble order, silu on the wrong projection, scale bias off by one, one
 scale for the whole row, ties to the higher index, gates normalised over all
 experts, no gate in the combine, w2 read transposed, h left unrounded, last input
 column dropped, wrong subnormal, sign bit ignored; for the MXFP8 mode: scale
-exponent off by one, no saturation, sign of FP8 dropped, ties away from zero)."""
+exponent off by one, no saturation, sign of FP8 dropped, ties away from zero;
+for the router logits: last input dropped, weight read transposed)."""
 import pytest
 
 import oracle
@@ -15,7 +16,8 @@ MUTANTS = {1: "nibble order", 2: "silu on w3", 3: "scale bias 126", 4: "one scal
            5: "ties to higher index", 6: "softmax over all experts", 7: "no gate",
            8: "w2 transposed", 9: "h not rounded", 10: "last column dropped",
            11: "subnormal = 1.0", 12: "sign ignored", 13: "mx8 scale exponent off by one",
-           14: "fp8 not saturated", 15: "fp8 sign dropped", 16: "fp8 ties away from zero"}
+           14: "fp8 not saturated", 15: "fp8 sign dropped", 16: "fp8 ties away from zero",
+           17: "router last input dropped", 18: "router weight transposed"}
 
 
 @pytest.mark.parametrize("n", sorted(MUTANTS), ids=lambda n: MUTANTS[n].replace(" ", "_"))
