@@ -292,12 +292,24 @@ def main():
                           "w2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
         }
         out["roofline_frac"] = max(out["hbm_frac"], out["mfma_frac"])
+        # the same chunk with the saliency side output (moe_fp4_forward_saliency)
+        sal = torch.zeros(pf.E, dtype=torch.float32, device=dev)
+        moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode, workspace=wsp)
+        torch.cuda.synchronize()
+        ts0 = time.perf_counter()
+        for i in range(args.prefill_reps):
+            moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode,
+                                         workspace=wsp)
+        torch.cuda.synchronize()
+        out["ms_per_chunk_with_saliency"] = (time.perf_counter() - ts0) * 1e3 / args.prefill_reps
         log(f"prefill ({label}): {p_ms:.3f} ms/chunk, {out['tflops']:.1f} TFLOP/s, HBM frac "
-            f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}")
-        del wsp
+            f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}; with saliency "
+            f"{out['ms_per_chunk_with_saliency']:.3f} ms")
+        del wsp, sal
         return out
 
-    prefill = run_prefill(moe.MODE_PREFILL, "bf16 (MFMA 16x16x32 bf16, FP4 decoded in registers)",
+    prefill = run_prefill(moe.MODE_PREFILL, "bf16 (MFMA 16x16x32 bf16, FP4 staged in LDS and "
+                                            "decoded to bf16 in registers)",
                           BF16_PEAK_TFLOPS)
     prefill_mx = run_prefill(moe.MODE_PREFILL_MXFP8,
                              "MXFP8 (x and h quantised; FP4 x FP8 scaled MFMA 16x16x128)",

@@ -190,6 +190,20 @@ int moe_fp4_forward_routed(const moe_fp4_dims *dims, const uint16_t *x, const ui
                            const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
                            size_t ws_bytes, hipStream_t stream);
 
+/* As moe_fp4_forward, and adds each expert's saliency for this call to
+ * saliency[e] (fp32 [E], 4-byte aligned; the caller zeroes it once and sums a
+ * corpus over calls).  Saliency is the pruning signal of the 10100.com page
+ * (section on choosing experts, frequency against saliency): router weight
+ * times the L2 norm of the expert's output, summed over tokens; here
+ *   saliency[e] += sum over pairs (t, j) routed to e of gates[t][j] * ||Y_(t,j)||_2
+ * with Y the expert's w2 output before the gate.  Prefill modes only: AUTO
+ * runs PREFILL, DECODE is EUNSUPPORTED; the workspace is that of the mode run.
+ * The sums are in a fixed order: the same inputs give the same bits.
+ * Errors: as moe_fp4_forward, and EINVAL for a null saliency. */
+int moe_fp4_forward_saliency(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                             const moe_fp4_weights *w, float *y, float *saliency, int mode,
+                             int flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Pre-normalisation for a residual stack of layers:
  *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
  *   x [T][H] fp32, u [T][H] bf16 bits.

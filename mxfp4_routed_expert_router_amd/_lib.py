@@ -61,10 +61,12 @@ def _load():
     lib.moe_fp4_quant_mxfp8.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.moe_fp4_router_logits.argtypes = [ctypes.POINTER(Dims), P, P, P, P]
     lib.moe_fp4_forward_routed.argtypes = lib.moe_fp4_forward.argtypes
+    lib.moe_fp4_forward_saliency.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
+                                             P, P, I32, I32, P, SZ, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
-              "moe_fp4_router_logits", "moe_fp4_forward_routed"):
+              "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -321,6 +323,38 @@ def moe_fp4_forward_routed(x: torch.Tensor, w_router: torch.Tensor, weights: Exp
                                        ACCUMULATE if accumulate else 0, workspace.data_ptr(),
                                        workspace.numel(), _stream(x)), "moe_fp4_forward_routed")
     return y
+
+
+def moe_fp4_forward_saliency(x: torch.Tensor, logits: torch.Tensor, weights: ExpertWeights, k: int,
+                             saliency: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                             mode: int = MODE_PREFILL, accumulate: bool = False,
+                             workspace: Optional[torch.Tensor] = None):
+    """As moe_fp4_forward (prefill modes), also adding each expert's saliency --
+    sum over its pairs of gate * ||expert output||_2 -- to `saliency` [E] fp32
+    (zeros if None).  Returns (y, saliency)."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _need(logits, "logits", (torch.float32,), 2)
+    T, H = x.shape
+    E = logits.shape[1]
+    I = weights.intermediate()
+    if saliency is None:
+        saliency = torch.zeros(E, dtype=torch.float32, device=x.device)
+    _need(saliency, "saliency", (torch.float32,), 1)
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs y")
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    run = MODE_PREFILL if mode == MODE_AUTO else mode
+    need = moe_fp4_workspace_size(T, H, I, E, k, run)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws = weights.as_struct()
+    _check(_lib.moe_fp4_forward_saliency(ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(),
+                                         logits.data_ptr(), ctypes.byref(ws), y.data_ptr(),
+                                         saliency.data_ptr(), mode, ACCUMULATE if accumulate else 0,
+                                         workspace.data_ptr(), workspace.numel(), _stream(x)),
+           "moe_fp4_forward_saliency")
+    return y, saliency
 
 
 def moe_fp4_quant_mxfp8(x: torch.Tensor):

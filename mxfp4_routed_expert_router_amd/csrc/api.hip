@@ -34,10 +34,12 @@ int resolve_mode(const moe_fp4_dims& d, int mode) {
   }
 }
 
+int sal_tiles(int H) { return (H + kSalRows - 1) / kSalRows; }
+
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h,
-      ypair, xq, xqs, hq, hqs, total;
+      ypair, sal, xq, xqs, hq, hqs, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
@@ -58,7 +60,11 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
   L.ypair = o;
   const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
-  if (rmode == MOE_FP4_MODE_PREFILL || mx) o = align_up(o + P * (size_t)d.H * 4);
+  if (rmode == MOE_FP4_MODE_PREFILL || mx) {
+    o = align_up(o + P * (size_t)d.H * 4);
+    L.sal = o;  // saliency tile partials (moe_fp4_forward_saliency)
+    o = align_up(o + P * (size_t)sal_tiles(d.H) * 4);
+  }
   if (mx) {
     const size_t Hp = mx8_padded(d.H), Ip = mx8_padded(d.I);
     L.xq = o;  o = align_up(o + (size_t)d.T * Hp);
@@ -79,10 +85,12 @@ T* at(void* ws, size_t off) {
 
 // Exactly one of logits and w_router is given; with w_router the logits are
 // computed into the workspace first.
+// With saliency (prefill modes only) the per-expert saliency is added to it.
 int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
                  const uint16_t* w_router, const moe_fp4_weights* w, float* y, int mode, int flags,
                  void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
-                 moe_fp4_route_out* route_out, const hipEvent_t* events) {
+                 moe_fp4_route_out* route_out, const hipEvent_t* events,
+                 float* saliency = nullptr) {
   if (!dims || !x || !(logits || w_router) || !w || !y || !ws) return MOE_FP4_EINVAL;
   if (!w->w1 || !w->s1 || !w->w3 || !w->s3 || !w->w2 || !w->s2) return MOE_FP4_EINVAL;
   if (route_out && (!route_out->topk_idx || !route_out->gates || !route_out->counts ||
@@ -94,8 +102,10 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   if (d.T < 1 || d.H < 1 || d.I < 1 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_FP4_EINVAL;
   if (!dims_ok(d)) return MOE_FP4_EUNSUPPORTED;
   if (flags & ~MOE_FP4_ACCUMULATE) return MOE_FP4_EUNSUPPORTED;
-  const int rmode = resolve_mode(d, mode);
-  if (rmode < 0) return MOE_FP4_EUNSUPPORTED;
+  const int rmode = resolve_mode(d, saliency && mode == MOE_FP4_MODE_AUTO ? MOE_FP4_MODE_PREFILL
+                                                                            : mode);
+  if (rmode < 0 || (saliency && rmode == MOE_FP4_MODE_DECODE)) return MOE_FP4_EUNSUPPORTED;
+  if (saliency && !aligned(saliency, 4)) return MOE_FP4_EALIGN;
 
   // per-expert tensor sizes in bytes, in the order w1, s1, w3, s3, w2, s2
   const int64_t per[6] = {(int64_t)d.I * d.H / 2, (int64_t)d.I * d.H / 32,
@@ -165,10 +175,15 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   a.fused_route = fused ? 1 : 0;
   a.route = r;
   a.logits = logits;
+  if (saliency) {
+    a.sal_part = at<float>(ws, L.sal);
+    a.sal_tiles = sal_tiles(d.H);
+  }
   const hipError_t err = rmode == MOE_FP4_MODE_DECODE ? launch_decode(a, stream)
                          : mx                          ? launch_prefill_mx8(a, stream)
                                                        : launch_prefill(a, stream);
   if (err != hipSuccess) return MOE_FP4_EHIP;
+  if (saliency && launch_saliency(a, saliency, stream) != hipSuccess) return MOE_FP4_EHIP;
 
   if (h_out && launch_unsort_h(a, h_out, stream) != hipSuccess) return MOE_FP4_EHIP;
   if (route_out) {
@@ -232,6 +247,14 @@ int moe_fp4_forward_routed(const moe_fp4_dims* dims, const uint16_t* x, const ui
   if (!w_router) return MOE_FP4_EINVAL;
   return forward_impl(dims, x, nullptr, w_router, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
                       nullptr, nullptr);
+}
+
+int moe_fp4_forward_saliency(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                             const moe_fp4_weights* w, float* y, float* saliency, int mode,
+                             int flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!saliency) return MOE_FP4_EINVAL;
+  return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                      nullptr, nullptr, saliency);
 }
 
 int moe_fp4_router_logits(const moe_fp4_dims* dims, const uint16_t* x, const uint16_t* w_router,

@@ -60,6 +60,10 @@ struct LayerArgs {
   const int32_t* slot_tok;  // [T*k] token of the pair in each sorted slot
   uint16_t* h;   // [T*k][I] bf16, rows in sorted (by-expert) order
   float* ypair;  // [T*k][H] fp32 gate-scaled expert outputs, sorted order (prefill only)
+  // optional saliency side output (prefill only): per sorted slot and 256-row
+  // tile of w2, the sum of squares of the expert's output rows, [T*k][sal_tiles]
+  float* sal_part;
+  int sal_tiles;
   // MXFP8 prefill: E4M3 codes and UE8M0 scales (one per 32 along the row) of x
   // [T][H] and of h [T*k][I] (sorted order)
   uint8_t *xq, *xqs, *hq, *hqs;
@@ -91,6 +95,10 @@ hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes
 // up to its K block (the padding holds zeros).
 size_t mx8_padded(int K);
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream);
+// saliency[e] += sum over e's sorted slots s of slot_gate[s] * sqrt(sum_tiles sal_part[s][.])
+hipError_t launch_saliency(const LayerArgs& a, float* saliency, hipStream_t stream);
+constexpr int kSalRows = 256;  // w2 rows per workgroup tile in every prefill w2 kernel
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,
                                 int E, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);

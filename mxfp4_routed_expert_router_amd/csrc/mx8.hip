@@ -19,6 +19,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "saliency.h"
 
 namespace moe_fp4 {
 namespace {
@@ -130,6 +131,7 @@ struct SmemMx {
   uint32_t ws[kStages][kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
   uint32_t xs[kStages][kWaves][16];           // token 8 w + i: scale dword d at 8 d + i
   int row[kTok];                              // source row of each staged token
+  float sal[kWaves * 64];                     // saliency reduction (saliency.h)
 };
 
 // Byte offset in the activation tile of token t's 16-byte chunk c (of 16):
@@ -347,6 +349,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
             *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
           }
         }
+      if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
     };
     switch ((nc + 15) / 16) {
       case 1: pass(IntC<1>{}); break;
@@ -363,6 +366,8 @@ namespace {
 unsigned quant_blocks(int rows, int Kp) {
   return (unsigned)std::min<size_t>(((size_t)rows * Kp / 8 + 255) / 256, 4096);
 }
+static_assert(kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
+
 }  // namespace
 
 hipError_t launch_quant_mx8(const uint16_t* src, int rows, int K, uint8_t* codes, uint8_t* scales,

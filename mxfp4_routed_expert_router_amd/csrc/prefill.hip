@@ -23,6 +23,7 @@
 // share an XCD and its L2 serves their common token rows.
 #include "device_common.h"
 #include "kernels.h"
+#include "saliency.h"
 
 namespace moe_fp4 {
 namespace {
@@ -44,6 +45,7 @@ constexpr int kXC = (kTok * kKB / 8) / kThreads;  // 16-byte activation chunks p
 struct Smem {
   uint16_t xs[2][kTok][kXS];
   int row[kTok];
+  float sal[kWaves * 64];  // saliency reduction (saliency.h)
 };
 
 
@@ -265,6 +267,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_kernel(LayerArgs a) {
             *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
           }
         }
+      if (a.sal_part) saliency_tile<kRT2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
     };
     switch ((nc + 15) / 16) {
       case 1: pass(IntC<1>{}); break;
@@ -292,6 +295,23 @@ __global__ void __launch_bounds__(256) combine_kernel(LayerArgs a) {
     s.x = o.x + s.x; s.y = o.y + s.y; s.z = o.z + s.z; s.w = o.w + s.w;
   }
   *yp = s;
+}
+
+// saliency[e] += sum over e's sorted slots (ascending) of gate * sqrt(sum of the
+// slot's tile partials, in tile order); one wave per expert, lanes strided over
+// the slots and reduced in a fixed DPP order.
+__global__ void __launch_bounds__(kWave) saliency_kernel(LayerArgs a, float* __restrict__ sal) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  const int n = a.counts[e], off = a.offsets[e];
+  float v = 0.f;
+  for (int i = lane; i < n; i += kWave) {
+    const float* p = a.sal_part + (size_t)(off + i) * a.sal_tiles;
+    float ss = 0.f;
+    for (int t = 0; t < a.sal_tiles; ++t) ss += p[t];
+    v += a.slot_gate[off + i] * sqrtf(ss);
+  }
+  v = wave_sum_f32(v);
+  if (lane == 0) sal[e] += v;
 }
 
 // h rows from sorted (by-expert) order to pair order, for the debug entry point.
@@ -329,6 +349,13 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
     launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   return launch_combine(a, stream);
 }
+
+hipError_t launch_saliency(const LayerArgs& a, float* saliency, hipStream_t stream) {
+  hipLaunchKernelGGL(saliency_kernel, dim3(a.E), dim3(kWave), 0, stream, a, saliency);
+  return hipGetLastError();
+}
+
+static_assert(kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
 
 hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stream) {
   const int P = a.T * a.k;

@@ -15,6 +15,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "saliency.h"
 
 namespace moe_fp4 {
 namespace {
@@ -35,6 +36,7 @@ struct SmemL {
   uint8_t x[3][kTok * kHB * 2];         // 64 tokens x 128 bf16 (see xoff_h)
   uint32_t ws[3][kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
   int row[kTok];                        // source row of each staged token
+  float sal[kWaves * 64];               // saliency reduction (saliency.h)
 };
 
 // Byte offset in a half-block activation tile of token t's 16-byte chunk c (of
@@ -263,6 +265,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
             *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
           }
         }
+      if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
     };
     switch ((nc + 15) / 16) {
       case 1: pass(IntC<1>{}); break;
@@ -272,6 +275,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
     }
   }
 }
+
+static_assert(kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
 
 }  // namespace
 

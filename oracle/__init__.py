@@ -62,6 +62,11 @@ class Oracle:
         lib.oracle_permute.argtypes = [ctypes.c_int] * 3 + [_i32p] * 5
         lib.oracle_router_logits.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 4
         lib.oracle_router_logits.restype = None
+        lib.oracle_saliency.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
+                                                              ctypes.POINTER(_OW), ctypes.c_int,
+                                                              ctypes.c_void_p, ctypes.c_void_p,
+                                                              ctypes.c_int]
+        lib.oracle_saliency.restype = ctypes.c_int
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
@@ -190,6 +195,27 @@ class Oracle:
         if want_h:
             out["h"], out["hpre"], out["hbound"] = h, hpre, hbound
         return out
+
+    def saliency(self, H: int, I: int, E: int, k: int, x_bits: np.ndarray, logits: np.ndarray,
+                 experts: Dict[int, Dict[str, np.ndarray]],
+                 expert_list: Optional[Sequence[int]] = None, mx8: bool = False) -> np.ndarray:
+        """Saliency of the listed experts (default: all E, and then every expert's
+        weights are needed): for expert e, the sum over the pairs (t, j) routed to
+        it of g[t][j] * ||Y_(t,j)||_2, Y the expert's output before the gate."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        T = x_bits.shape[0]
+        assert x_bits.shape == (T, H) and logits.shape == (T, E)
+        lst = np.ascontiguousarray(np.arange(E) if expert_list is None else expert_list,
+                                   dtype=np.int32)
+        sal = np.empty(len(lst), np.float64)
+        ow, keep = self._weights(experts, E)
+        rc = self.lib.oracle_saliency(T, H, I, E, k, x_bits.ctypes.data, logits, ctypes.byref(ow),
+                                      len(lst), lst.ctypes.data, sal.ctypes.data, int(mx8))
+        del keep
+        if rc != 0:
+            raise KeyError("a listed expert's weights were not given")
+        return sal
 
     def prenorm(self, x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
         x = np.ascontiguousarray(x, dtype=np.float32)

@@ -419,6 +419,49 @@ int oracle_forward_mx8(int T, int H, int I, int E, int k, const uint16_t *x, con
                         gates_out, 1, gamma);
 }
 
+/* Expert saliency, the pruning signal of the 10100.com page (section on
+ * choosing experts, frequency against saliency): the router weight times the
+ * L2 norm of the expert's output, summed over the tokens.  Read as: for each
+ * listed expert e, sal[i] = sum over the pairs (t, j) with idx[t][j] = e, t
+ * ascending, of g[t][j] * ||Y_(t,j)||_2, with Y the expert's output before the
+ * gate (double throughout).  mx8 selects the MXFP8 activations of
+ * oracle_forward_mx8.  Returns 0, or -1 if a listed expert's weights are
+ * missing. */
+int oracle_saliency(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
+                    const oracle_weights *W, int n_exp, const int32_t *list, double *sal,
+                    int mx8) {
+    int P = T * k;
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
+    float *g = (float *)malloc(sizeof(float) * (size_t)P);
+    oracle_route(T, E, k, logits, idx, g);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *Y = (double *)malloc(sizeof(double) * (size_t)H);
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)I);
+    double *hp = (double *)malloc(sizeof(double) * (size_t)I);
+    int rc = 0;
+    for (int i = 0; i < n_exp && rc == 0; ++i) {
+        int e = list[i];
+        sal[i] = 0.0;
+        if (!W->w1[e] || !W->s1[e] || !W->w3[e] || !W->s3[e] || !W->w2[e] || !W->s2[e]) {
+            rc = -1;
+            break;
+        }
+        for (int p = 0; p < P; ++p) {
+            if (idx[p] != e) continue;
+            int t = p / k;
+            for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(x[(size_t)t * H + c]);
+            if (mx8) mx8_round_trip(H, xd);
+            expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], mx8,
+                       0.0, h, hp, NULL, Y);
+            double ss = 0.0;
+            for (int m = 0; m < H - MUT(19); ++m) ss += Y[m] * Y[m];
+            sal[i] += (MUT(20) ? 1.0 : (double)g[p]) * sqrt(ss);
+        }
+    }
+    free(hp); free(h); free(Y); free(xd); free(g); free(idx);
+    return rc;
+}
+
 /* Pre-normalisation of the layer stack: u = bf16(x / sqrt(mean(x^2) + eps)). */
 void oracle_prenorm(int T, int H, const float *x, double eps, uint16_t *u) {
     for (int t = 0; t < T; ++t) {

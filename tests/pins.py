@@ -490,7 +490,45 @@ def pin_router_bound(o):
     assert np.all(lg == H) and np.allclose(b, H * u / (1 - H * u) * H, rtol=1e-15)
 
 
+def pin_saliency_single(o):
+    """k = 1 and one token: the gate is 1, so the saliency of the chosen expert
+    is the L2 norm of the layer output y, and every other expert's is 0."""
+    rng = np.random.default_rng(71)
+    H, I, E = 128, 64, 4
+    experts = {e: random_expert(rng, H, I) for e in range(E)}
+    x = rand_bf16(rng, (1, H))
+    lg = rng.standard_normal((1, E)).astype(np.float32)
+    out = o.forward(H, I, E, 1, x, lg, experts)
+    sal = o.saliency(H, I, E, 1, x, lg, experts)
+    e = int(out["idx"][0, 0])
+    assert out["gates"][0, 0] == 1.0
+    assert abs(sal[e] - np.linalg.norm(out["y"][0].astype(np.float64))) <= 1e-6 * sal[e]
+    assert np.all(np.delete(sal, e) == 0.0)
+
+
+def pin_saliency_numpy(o):
+    """Saliency against numpy float64: each pair's Y from dequantised matrices
+    and the oracle's (pinned) bf16 h, its norm, times the gate, summed by expert."""
+    rng = np.random.default_rng(72)
+    H, I, E, k, T = 96, 64, 5, 2, 7
+    experts = {e: random_expert(rng, H, I) for e in range(E)}
+    x = rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    out = o.forward(H, I, E, k, x, lg, experts, want_h=True)
+    sal = o.saliency(H, I, E, k, x, lg, experts)
+    ref = np.zeros(E)
+    for t in range(T):
+        for j in range(k):
+            e = int(out["idx"][t, j])
+            hv = bf16_to_f64(out["h"][t * k + j])
+            Y = _dequant(experts[e]["w2"], experts[e]["s2"]) @ hv
+            ref[e] += float(out["gates"][t, j]) * np.linalg.norm(Y)
+    assert np.allclose(sal, ref, rtol=1e-12, atol=0), (sal, ref)
+    assert np.all(sal[np.setdiff1d(np.arange(E), out["idx"])] == 0.0)
+
+
 ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pin_router_special,
             pin_permute, pin_probe_w1, pin_probe_w2, pin_closed_form_swiglu, pin_prenorm,
             pin_brute, pin_numpy_matmul, pin_e4m3_table, pin_mx8_quant, pin_mx8_special,
-            pin_mx8_forward, pin_router_numpy, pin_router_onehot, pin_router_bound]
+            pin_mx8_forward, pin_router_numpy, pin_router_onehot, pin_router_bound,
+            pin_saliency_single, pin_saliency_numpy]

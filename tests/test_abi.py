@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
               "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string",
-              "moe_fp4_quant_mxfp8", "moe_fp4_router_logits", "moe_fp4_forward_routed"):
+              "moe_fp4_quant_mxfp8", "moe_fp4_router_logits", "moe_fp4_forward_routed",
+              "moe_fp4_forward_saliency"):
         assert n in names
 
 
@@ -252,3 +253,19 @@ def test_forward_routed_validation(lib):
     assert f(*args(None, n.value)) == lib.EINVAL
     assert f(*args(FAKE + 2, n.value)) == lib.EALIGN
     assert f(*args(FAKE, 0)) == lib.EWORKSPACE
+
+
+def test_forward_saliency_validation(lib):
+    """Prefill modes only; AUTO runs PREFILL, so its workspace is PREFILL's."""
+    f = lib._lib.moe_fp4_forward_saliency
+    d = lib.Dims(4, 256, 128, 16, 2)
+    w = _weights(lib)
+    n_pre, n_dec = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), lib.MODE_PREFILL, ctypes.byref(n_pre)) == 0
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), lib.MODE_DECODE, ctypes.byref(n_dec)) == 0
+    call = lambda sal, mode, nb: f(ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), FAKE, sal, mode, 0,
+                                   FAKE, nb, None)
+    assert call(None, 0, n_pre.value) == lib.EINVAL
+    assert call(FAKE, lib.MODE_DECODE, n_pre.value) == lib.EUNSUPPORTED
+    assert call(FAKE + 2, lib.MODE_PREFILL, n_pre.value) == lib.EALIGN
+    assert call(FAKE, lib.MODE_AUTO, n_dec.value) == lib.EWORKSPACE
