@@ -230,6 +230,36 @@ def main():
     log(f"decode with the router step: {us_routed:.2f} us/token; router kernel alone "
         f"{us_router:.2f} us ({routed['router_GBps']:.0f} GB/s)")
 
+    # ---------------------------------------------------------------- decode with the shared expert
+    # The routed layer plus the FP8 shared expert (moe_fp4_forward_shared),
+    # and the shared expert alone; graph replays.
+    sw_np = synth.gen_shared(wl)
+    sw_d = moe.SharedWeights.from_dict({n: torch.from_numpy(a).to(dev) for n, a in sw_np.items()})
+    h_s = torch.empty((1, wl.I), dtype=torch.bfloat16, device=dev)
+    y_s = torch.empty((1, wl.H), dtype=torch.float32, device=dev)
+
+    def step_shared(i):
+        j = i % n_gen
+        moe.moe_fp4_forward_shared(x_d[j:j + 1], lg_d[j:j + 1], w, sw_d, wl.k, y=y_d[j:j + 1],
+                                   workspace=ws)
+
+    def step_shared_only(i):
+        j = i % n_gen
+        moe.moe_fp4_shared_expert(x_d[j:j + 1], sw_d, y=y_s, h=h_s)
+
+    us_shared = graph_us(step_shared)
+    us_shared_only = graph_us(step_shared_only)
+    shared_bytes = sum(a.nbytes for a in sw_np.values()) + wl.H * 2 + wl.H * 4
+    shared = {"us_per_token": us_shared, "shared_expert_us": us_shared_only,
+              "shared_bytes": shared_bytes,
+              "shared_GBps": shared_bytes / (us_shared_only * 1e-6) / 1e9,
+              "note": "routed layer + shared expert (FP8 E4M3, 32x32 UE8M0 block scales, "
+                      "I = 2304; 35.4 MB); graph replay; shared_expert_us: the shared expert "
+                      "alone (two kernels), one call per step in a graph"}
+    log(f"decode with the shared expert: {us_shared:.2f} us/token; shared expert alone "
+        f"{us_shared_only:.2f} us ({shared['shared_GBps']:.0f} GB/s)")
+    del sw_d
+
     # ---------------------------------------------------------------- decode, cold caches
     # A read-only flush (summing a 1 GiB buffer) between steps evicts the
     # experts from L2 and the MALL without leaving dirty lines whose write-back
@@ -366,6 +396,7 @@ def main():
         "us_per_token_eager": us_eager,
         "cold": cold,
         "decode_routed": routed,
+        "decode_shared": shared,
         "prefill": prefill,
         "prefill_mxfp8": prefill_mx,
         "cpu_baseline": cpu,

@@ -204,6 +204,44 @@ int moe_fp4_forward_saliency(const moe_fp4_dims *dims, const uint16_t *x, const 
                              const moe_fp4_weights *w, float *y, float *saliency, int mode,
                              int flags, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The shared expert (one per layer beside the routed experts: ai-shiz.ru
+ * page, section "what the model is"; FP8 per the 10100.com page, plan two;
+ * 32 x 32 blocks for the main weights per the ai-shiz.ru page).  Taken as a
+ * SwiGLU expert of the routed experts' form, E4M3 weights, one UE8M0 scale per
+ * 32 x 32 block:
+ *   w1, w3  [I][H] E4M3 codes (row n = output n), 16-byte aligned
+ *   s1, s3  [I/32][H/32] UE8M0: W1[n][c] = E4M3(w1[n][c]) * 2^(s1[n/32][c/32] - 127)
+ *   w2      [H][I] E4M3 codes, 16-byte aligned
+ *   s2      [H/32][I/32] UE8M0
+ *   I       intermediate size, a multiple of 32 in [32, 16384]
+ * Scale tensors have no alignment rule. */
+typedef struct {
+  const uint8_t *w1, *s1, *w3, *s3, *w2, *s2;
+  int32_t I;
+} moe_fp4_shared_weights;
+
+/* The shared expert alone:
+ *   h[t] = bf16(silu(W1 x[t]) * (W3 x[t]))   (rounded once, as the routed h)
+ *   y[t] = W2 h[t], or y[t] += W2 h[t] with MOE_FP4_ACCUMULATE
+ *   dims  T and H used (I, E, k ignored)
+ *   x     [T][H] bf16 bits, 16-byte aligned;  y [T][H] fp32, 16-byte aligned
+ *   h     [T][sw->I] bf16 bits, 16-byte aligned: written (scratch and output)
+ * fp32 sums in a fixed order: the same inputs give the same bits.
+ * Errors: EINVAL (null), EUNSUPPORTED (sizes, flags), EALIGN, EHIP. */
+int moe_fp4_shared_expert(const moe_fp4_dims *dims, const uint16_t *x,
+                          const moe_fp4_shared_weights *sw, float *y, int flags, uint16_t *h,
+                          hipStream_t stream);
+
+/* As moe_fp4_forward, then adds the shared expert's output:
+ *   y[t] (+)= sum_j gates[t][j] * Y_(t,j) + W2s h_s[t]
+ * The shared expert's h uses the routed path's workspace, so sw->I <=
+ * dims->k * dims->I is required (EUNSUPPORTED otherwise); same workspace size
+ * as moe_fp4_forward.
+ * Errors: as moe_fp4_forward and moe_fp4_shared_expert. */
+int moe_fp4_forward_shared(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                           const moe_fp4_weights *w, const moe_fp4_shared_weights *sw, float *y,
+                           int mode, int flags, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Pre-normalisation for a residual stack of layers:
  *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
  *   x [T][H] fp32, u [T][H] bf16 bits.

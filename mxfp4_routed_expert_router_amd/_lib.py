@@ -38,6 +38,10 @@ class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in TENSORS] + [("expert_stride", ctypes.c_int64 * 6)]
 
 
+class SharedWeightsStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TENSORS] + [("I", ctypes.c_int32)]
+
+
 class RouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "gates", "counts", "offsets", "sorted_pairs", "pair_slot")]
@@ -61,12 +65,17 @@ def _load():
     lib.moe_fp4_quant_mxfp8.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.moe_fp4_router_logits.argtypes = [ctypes.POINTER(Dims), P, P, P, P]
     lib.moe_fp4_forward_routed.argtypes = lib.moe_fp4_forward.argtypes
+    lib.moe_fp4_shared_expert.argtypes = [ctypes.POINTER(Dims), P, ctypes.POINTER(SharedWeightsStruct),
+                                          P, I32, P, P]
+    lib.moe_fp4_forward_shared.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
+                                           ctypes.POINTER(SharedWeightsStruct), P, I32, I32, P, SZ, P]
     lib.moe_fp4_forward_saliency.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
                                              P, P, I32, I32, P, SZ, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
-              "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency"):
+              "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency",
+              "moe_fp4_shared_expert", "moe_fp4_forward_shared"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -355,6 +364,81 @@ def moe_fp4_forward_saliency(x: torch.Tensor, logits: torch.Tensor, weights: Exp
                                          workspace.data_ptr(), workspace.numel(), _stream(x)),
            "moe_fp4_forward_saliency")
     return y, saliency
+
+
+@dataclass
+class SharedWeights:
+    """The shared expert's tensors (uint8, on the GPU): w1, w3 [I, H] and w2 [H, I]
+    E4M3 codes; s1, s3 [I/32, H/32] and s2 [H/32, I/32] UE8M0 block scales."""
+    w1: torch.Tensor
+    s1: torch.Tensor
+    w3: torch.Tensor
+    s3: torch.Tensor
+    w2: torch.Tensor
+    s2: torch.Tensor
+
+    @classmethod
+    def from_dict(cls, d: Dict[str, torch.Tensor]) -> "SharedWeights":
+        return cls(**{n: d[n] for n in TENSORS})
+
+    def as_struct(self) -> SharedWeightsStruct:
+        sw = SharedWeightsStruct()
+        for n in TENSORS:
+            t = getattr(self, n)
+            if t.dtype != torch.uint8 or t.device.type != "cuda" or not t.is_contiguous():
+                raise TypeError(f"shared weight tensor {n} must be contiguous uint8 on the GPU")
+            setattr(sw, n, t.data_ptr())
+        sw.I = int(self.w1.shape[0])
+        return sw
+
+
+def moe_fp4_shared_expert(x: torch.Tensor, shared: SharedWeights, y: Optional[torch.Tensor] = None,
+                          accumulate: bool = False, h: Optional[torch.Tensor] = None):
+    """The shared expert alone: y [T, H] (+)= W2 bf16(silu(W1 x) * (W3 x)).
+    Returns (y, h) with h [T, I] bf16."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    T, H = x.shape
+    I = int(shared.w1.shape[0])
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs y")
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    if h is None:
+        h = torch.empty((T, I), dtype=torch.bfloat16, device=x.device)
+    sw = shared.as_struct()
+    _check(_lib.moe_fp4_shared_expert(ctypes.byref(Dims(T, H, 0, 0, 0)), x.data_ptr(),
+                                      ctypes.byref(sw), y.data_ptr(),
+                                      ACCUMULATE if accumulate else 0, h.data_ptr(), _stream(x)),
+           "moe_fp4_shared_expert")
+    return y, h
+
+
+def moe_fp4_forward_shared(x: torch.Tensor, logits: torch.Tensor, weights: ExpertWeights,
+                           shared: SharedWeights, k: int, y: Optional[torch.Tensor] = None,
+                           mode: int = MODE_AUTO, accumulate: bool = False,
+                           workspace: Optional[torch.Tensor] = None):
+    """The routed layer plus the shared expert: y (+)= sum_j g_j Y_j + W2s h_s."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _need(logits, "logits", (torch.float32,), 2)
+    T, H = x.shape
+    E = logits.shape[1]
+    I = weights.intermediate()
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs y")
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    need = moe_fp4_workspace_size(T, H, I, E, k, mode)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws, sw = weights.as_struct(), shared.as_struct()
+    _check(_lib.moe_fp4_forward_shared(ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(),
+                                       logits.data_ptr(), ctypes.byref(ws), ctypes.byref(sw),
+                                       y.data_ptr(), mode, ACCUMULATE if accumulate else 0,
+                                       workspace.data_ptr(), workspace.numel(), _stream(x)),
+           "moe_fp4_forward_shared")
+    return y
 
 
 def moe_fp4_quant_mxfp8(x: torch.Tensor):

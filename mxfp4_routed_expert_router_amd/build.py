@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_fp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "route.hip", "router.hip", "decode.hip", "prefill.hip", "prefill_lds.hip", "mx8.hip", "stack.hip"]
+SOURCES = ["api.hip", "route.hip", "router.hip", "decode.hip", "prefill.hip", "prefill_lds.hip", "mx8.hip", "shared.hip", "stack.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code (the host pass warns
 # that it does not know the feature; that is harmless).

@@ -201,6 +201,25 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   return MOE_FP4_OK;
 }
 
+// Checks of the shared expert's arguments (T and H from dims).
+int shared_check(const moe_fp4_dims& d, const uint16_t* x, const moe_fp4_shared_weights* sw,
+                 const float* y) {
+  if (!x || !sw || !y || !sw->w1 || !sw->s1 || !sw->w3 || !sw->s3 || !sw->w2 || !sw->s2)
+    return MOE_FP4_EINVAL;
+  if (d.T < 1 || d.H < 1 || sw->I < 1) return MOE_FP4_EINVAL;
+  if (d.T > 65535 || d.H < 32 || d.H > 16384 || d.H % 32 || sw->I < 32 || sw->I > 16384 ||
+      sw->I % 32)
+    return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(sw->w1, 16) || !aligned(sw->w3, 16) ||
+      !aligned(sw->w2, 16))
+    return MOE_FP4_EALIGN;
+  return MOE_FP4_OK;
+}
+const uint8_t* const* shared_tensors(const moe_fp4_shared_weights* sw, const uint8_t* (&t)[6]) {
+  t[0] = sw->w1; t[1] = sw->s1; t[2] = sw->w3; t[3] = sw->s3; t[4] = sw->w2; t[5] = sw->s2;
+  return t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +274,41 @@ int moe_fp4_forward_saliency(const moe_fp4_dims* dims, const uint16_t* x, const 
   if (!saliency) return MOE_FP4_EINVAL;
   return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
                       nullptr, nullptr, saliency);
+}
+
+int moe_fp4_shared_expert(const moe_fp4_dims* dims, const uint16_t* x,
+                          const moe_fp4_shared_weights* sw, float* y, int flags, uint16_t* h,
+                          hipStream_t stream) {
+  if (!dims || !h) return MOE_FP4_EINVAL;
+  const int rc = shared_check(*dims, x, sw, y);
+  if (rc != MOE_FP4_OK) return rc;
+  if (flags & ~MOE_FP4_ACCUMULATE) return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(h, 16)) return MOE_FP4_EALIGN;
+  const uint8_t* t[6];
+  return launch_shared(x, shared_tensors(sw, t), dims->T, dims->H, sw->I, y,
+                       (flags & MOE_FP4_ACCUMULATE) ? 1 : 0, h, stream) == hipSuccess
+             ? MOE_FP4_OK
+             : MOE_FP4_EHIP;
+}
+
+int moe_fp4_forward_shared(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                           const moe_fp4_weights* w, const moe_fp4_shared_weights* sw, float* y,
+                           int mode, int flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dims) return MOE_FP4_EINVAL;
+  int rc = shared_check(*dims, x, sw, y);
+  if (rc != MOE_FP4_OK) return rc;
+  // the shared expert's h reuses the routed h section once the routed path is done
+  if (sw->I > dims->k * dims->I) return MOE_FP4_EUNSUPPORTED;
+  rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                    nullptr, nullptr);
+  if (rc != MOE_FP4_OK) return rc;
+  const int rmode = resolve_mode(*dims, mode);
+  uint16_t* const h = at<uint16_t>(ws, layout(*dims, rmode).h);
+  const uint8_t* t[6];
+  return launch_shared(x, shared_tensors(sw, t), dims->T, dims->H, sw->I, y, 1, h, stream) ==
+                 hipSuccess
+             ? MOE_FP4_OK
+             : MOE_FP4_EHIP;
 }
 
 int moe_fp4_router_logits(const moe_fp4_dims* dims, const uint16_t* x, const uint16_t* w_router,

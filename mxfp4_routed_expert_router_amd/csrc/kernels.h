@@ -99,6 +99,10 @@ hipError_t launch_unsort_h(const LayerArgs& a, uint16_t* h_out, hipStream_t stre
 hipError_t launch_saliency(const LayerArgs& a, float* saliency, hipStream_t stream);
 constexpr int kSalRows = 256;  // w2 rows per workgroup tile in every prefill w2 kernel
 
+// The shared expert: h = bf16(silu(W1 x) * (W3 x)) [T][I], y (+)= W2 h.
+// w = {w1, s1, w3, s3, w2, s2}: E4M3 codes with 32 x 32 UE8M0 block scales.
+hipError_t launch_shared(const uint16_t* x, const uint8_t* const w[6], int T, int H, int I,
+                         float* y, int accumulate, uint16_t* h, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,
                                 int E, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);

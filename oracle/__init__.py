@@ -67,6 +67,8 @@ class Oracle:
                                                               ctypes.c_void_p, ctypes.c_void_p,
                                                               ctypes.c_int]
         lib.oracle_saliency.restype = ctypes.c_int
+        lib.oracle_shared.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 11
+        lib.oracle_shared.restype = None
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
@@ -216,6 +218,30 @@ class Oracle:
         if rc != 0:
             raise KeyError("a listed expert's weights were not given")
         return sal
+
+    def shared(self, x_bits: np.ndarray, sw: Dict[str, np.ndarray], want_h: bool = False):
+        """The shared expert's output y_s [T, H] (double) for bf16 bits x [T, H];
+        sw holds w1, w3 [I, H] and w2 [H, I] E4M3 bytes with s1, s3 [I/32, H/32]
+        and s2 [H/32, I/32] UE8M0 block scales.  With want_h also h (bf16 bits),
+        hpre and hbound [T, I]."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        T, H = x_bits.shape
+        I = sw["w1"].shape[0]
+        t = {n: np.ascontiguousarray(sw[n], dtype=np.uint8) for n in ("w1", "s1", "w3", "s3", "w2", "s2")}
+        assert t["w1"].shape == (I, H) and t["w3"].shape == (I, H) and t["w2"].shape == (H, I)
+        assert t["s1"].shape == (I // 32, H // 32) and t["s2"].shape == (H // 32, I // 32)
+        y = np.empty((T, H), np.float64)
+        h = np.empty((T, I), np.uint16) if want_h else None
+        hp = np.empty((T, I), np.float64) if want_h else None
+        hb = np.empty((T, I), np.float64) if want_h else None
+        ptr = lambda a: None if a is None else a.ctypes.data
+        self.lib.oracle_shared(T, H, I, x_bits.ctypes.data, *(t[n].ctypes.data for n in
+                               ("w1", "s1", "w3", "s3", "w2", "s2")), y.ctypes.data, ptr(h),
+                               ptr(hp), ptr(hb))
+        out = {"y": y}
+        if want_h:
+            out["h"], out["hpre"], out["hbound"] = h, hp, hb
+        return out
 
     def prenorm(self, x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
         x = np.ascontiguousarray(x, dtype=np.float32)

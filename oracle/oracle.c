@@ -462,6 +462,59 @@ int oracle_saliency(int T, int H, int I, int E, int k, const uint16_t *x, const 
     return rc;
 }
 
+/* ------------------------------------------------------------------ shared expert */
+
+/* The shared expert (one per layer beside the 384 routed ones: ai-shiz.ru
+ * page, section "what the model is"; kept in FP8 by the 10100.com page, plan
+ * two; main weights as FP8 in 32 x 32 blocks, ai-shiz.ru page, same section).
+ * Read as: SwiGLU of the routed experts' form with intermediate size I,
+ *   W1[n][c] = E4M3(w1[n][c]) * 2^(s1[n/32][c/32] - 127)   w1, w3 [I][H], s1, s3 [I/32][H/32]
+ *   W2[m][n] = E4M3(w2[m][n]) * 2^(s2[m/32][n/32] - 127)   w2 [H][I], s2 [H/32][I/32]
+ * h = bf16(silu(W1 x) * (W3 x)) rounded once, y_s = W2 h, added to the
+ * layer's output without a gate.  y [T][H] double; h, hpre, hbound [T][I]
+ * optional, as in expert_ffn. */
+static double fp8w(const uint8_t *w, const uint8_t *s, int cols, int r, int c) {
+    const int si = MUT(21) ? (c / 32) * (cols / 32) + r / 32 : (r / 32) * (cols / 32) + c / 32;
+    return oracle_e4m3(w[(size_t)r * cols + c]) * oracle_ue8m0(s[si]);
+}
+
+void oracle_shared(int T, int H, int I, const uint16_t *x, const uint8_t *w1, const uint8_t *s1,
+                   const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
+                   double *y, uint16_t *h_out, double *hpre, double *hbound) {
+    const double u32 = ldexp(1.0, -24), gam = H * u32 / (1.0 - H * u32);
+    for (int t = 0; t < T; ++t) {
+        double *hv = (double *)malloc(sizeof(double) * (size_t)I);
+        #pragma omp parallel for schedule(static)
+        for (int n = 0; n < I; ++n) {
+            double G = 0.0, U = 0.0, Ga = 0.0, Ua = 0.0;
+            for (int c = 0; c < H; ++c) {
+                const double xv = oracle_bf16_to_double(x[(size_t)t * H + c]);
+                const double a1 = xv * fp8w(w1, s1, H, n, c), a3 = xv * fp8w(w3, s3, H, n, c);
+                G += a1; U += a3; Ga += fabs(a1); Ua += fabs(a3);
+            }
+            const double a = G / (1.0 + exp(-G)) * U;
+            const size_t o = (size_t)t * I + n;
+            if (hpre) hpre[o] = a;
+            if (hbound) {
+                const double sg = 1.0 / (1.0 + exp(-G));
+                const double dsilu = sg * (1.0 + G * (1.0 - sg));
+                hbound[o] = fabs(dsilu * U) * gam * Ga + fabs(G * sg) * gam * Ua + 8.0 * u32 * fabs(a);
+            }
+            const uint16_t hb = oracle_double_to_bf16(a);
+            if (h_out) h_out[o] = hb;
+            hv[n] = oracle_bf16_to_double(hb);
+        }
+        #pragma omp parallel for schedule(static)
+        for (int m = 0; m < H; ++m) {
+            double acc = 0.0;
+            for (int n = 0; n < I; ++n)
+                acc += hv[n] * (MUT(22) ? fp8w(w2, s2, I, n % H, m % I) : fp8w(w2, s2, I, m, n));
+            y[(size_t)t * H + m] = acc;
+        }
+        free(hv);
+    }
+}
+
 /* Pre-normalisation of the layer stack: u = bf16(x / sqrt(mean(x^2) + eps)). */
 void oracle_prenorm(int T, int H, const float *x, double eps, uint16_t *u) {
     for (int t = 0; t < T; ++t) {

@@ -181,6 +181,26 @@ def gen_router(wl: Workload, layer: int = 0) -> np.ndarray:
     return f32_to_bf16_bits(w * np.float32(1.0 / np.sqrt(wl.H)))
 
 
+def gen_shared(wl: Workload, layer: int = 0) -> dict:
+    """Shared-expert tensors of one layer, intermediate size wl.I: E4M3 codes
+    uniform over the 254 non-NaN codes (w1, w3 [I, H], w2 [H, I]) and UE8M0
+    32 x 32 block scales uniform in [113, 115] (s1, s3 [I/32, H/32], s2
+    [H/32, I/32]), which keeps the projections of N(0,1) activations O(1)."""
+    rng = _rng(wl.weight_seed, 5, layer)
+    H, I = wl.H, wl.I
+
+    def codes(shape):
+        c = rng.integers(0, 254, shape, dtype=np.int32)
+        return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)
+
+    def scales(shape):
+        return rng.integers(113, 116, shape, dtype=np.int32).astype(np.uint8)
+
+    return {"w1": codes((I, H)), "s1": scales((I // 32, H // 32)),
+            "w3": codes((I, H)), "s3": scales((I // 32, H // 32)),
+            "w2": codes((H, I)), "s2": scales((H // 32, I // 32))}
+
+
 def gen_logits(wl: Workload, step: int = 0, layer: int = 0) -> np.ndarray:
     """Router logits for one step: [T, E] float32 = N(0,1) noise + per-expert bias."""
     noise = _rng(wl.input_seed, 0, step, layer).standard_normal((wl.T, wl.E), dtype=np.float32)

@@ -527,8 +527,42 @@ def pin_saliency_numpy(o):
     assert np.all(sal[np.setdiff1d(np.arange(E), out["idx"])] == 0.0)
 
 
+def random_shared(rng, H, I, lo=113, hi=115):
+    """Shared-expert tensors: E4M3 codes uniform over the 254 non-NaN codes,
+    UE8M0 block scales uniform in [lo, hi]."""
+    def codes(shape):
+        c = rng.integers(0, 254, shape)
+        return np.where(c >= 0x7F, c + 1, c).astype(np.uint8)
+    return {"w1": codes((I, H)), "s1": rng.integers(lo, hi + 1, (I // 32, H // 32)).astype(np.uint8),
+            "w3": codes((I, H)), "s3": rng.integers(lo, hi + 1, (I // 32, H // 32)).astype(np.uint8),
+            "w2": codes((H, I)), "s2": rng.integers(lo, hi + 1, (H // 32, I // 32)).astype(np.uint8)}
+
+
+def pin_shared_numpy(o):
+    """The shared expert against numpy float64: E4M3 values from the (pinned)
+    decode table, 32 x 32 block scales expanded with np.kron, matmuls, SwiGLU
+    and the oracle's (pinned) bf16 rounding of h.  Non-square block grids
+    (H = 96, I = 64) so that a transposed scale index shows."""
+    rng = np.random.default_rng(81)
+    H, I, T = 96, 64, 3
+    sw = random_shared(rng, H, I, 110, 118)
+    x = rand_bf16(rng, (T, H))
+    out = o.shared(x, sw, want_h=True)
+    tab = np.array([o.e4m3(c) if (c & 0x7F) != 0x7F else 0.0 for c in range(256)])
+    dq = lambda w, sc: tab[w] * np.kron(np.ldexp(1.0, sc.astype(np.int64) - 127), np.ones((32, 32)))
+    W1, W3, W2 = dq(sw["w1"], sw["s1"]), dq(sw["w3"], sw["s3"]), dq(sw["w2"], sw["s2"])
+    xf = bf16_to_f64(x)
+    G, U = xf @ W1.T, xf @ W3.T
+    a = G / (1.0 + np.exp(-G)) * U
+    assert np.allclose(out["hpre"], a, rtol=1e-12, atol=1e-300)
+    h = np.array([[o.to_bf16(v) for v in row] for row in a], np.uint16)
+    assert np.array_equal(out["h"], h)
+    y = bf16_to_f64(h) @ W2.T
+    assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
 ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pin_router_special,
             pin_permute, pin_probe_w1, pin_probe_w2, pin_closed_form_swiglu, pin_prenorm,
             pin_brute, pin_numpy_matmul, pin_e4m3_table, pin_mx8_quant, pin_mx8_special,
             pin_mx8_forward, pin_router_numpy, pin_router_onehot, pin_router_bound,
-            pin_saliency_single, pin_saliency_numpy]
+            pin_saliency_single, pin_saliency_numpy, pin_shared_numpy]

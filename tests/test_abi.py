@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
               "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string",
               "moe_fp4_quant_mxfp8", "moe_fp4_router_logits", "moe_fp4_forward_routed",
-              "moe_fp4_forward_saliency"):
+              "moe_fp4_forward_saliency", "moe_fp4_shared_expert", "moe_fp4_forward_shared"):
         assert n in names
 
 
@@ -269,3 +269,40 @@ def test_forward_saliency_validation(lib):
     assert call(FAKE, lib.MODE_DECODE, n_pre.value) == lib.EUNSUPPORTED
     assert call(FAKE + 2, lib.MODE_PREFILL, n_pre.value) == lib.EALIGN
     assert call(FAKE, lib.MODE_AUTO, n_dec.value) == lib.EWORKSPACE
+
+
+def _shared(lib, **over):
+    sw = lib.SharedWeightsStruct()
+    for i, n in enumerate(lib.TENSORS):
+        setattr(sw, n, over.get(n, FAKE + (i << 30)))
+    sw.I = over.get("I", 128)
+    return sw
+
+
+def test_shared_expert_validation(lib):
+    f = lib._lib.moe_fp4_shared_expert
+    d = ctypes.byref(lib.Dims(4, 256, 0, 0, 0))
+    call = lambda sw, x=FAKE, y=FAKE, flags=0, h=FAKE, dims=d: f(dims, x, ctypes.byref(sw), y, flags,
+                                                                 h, None)
+    assert call(_shared(lib), h=None) == lib.EINVAL
+    assert call(_shared(lib), x=None) == lib.EINVAL
+    assert call(_shared(lib, w2=None)) == lib.EINVAL
+    assert call(_shared(lib, I=100)) == lib.EUNSUPPORTED
+    assert call(_shared(lib), dims=ctypes.byref(lib.Dims(4, 250, 0, 0, 0))) == lib.EUNSUPPORTED
+    assert call(_shared(lib), flags=2) == lib.EUNSUPPORTED
+    assert call(_shared(lib, w3=FAKE + 8)) == lib.EALIGN
+    assert call(_shared(lib), h=FAKE + 2) == lib.EALIGN
+
+
+def test_forward_shared_validation(lib):
+    """The shared expert's h lives in the routed h section: I_s <= k * I."""
+    f = lib._lib.moe_fp4_forward_shared
+    d = lib.Dims(4, 256, 128, 16, 2)
+    w = _weights(lib)
+    n = ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == lib.OK
+    call = lambda sw, nb: f(ctypes.byref(d), FAKE, FAKE, ctypes.byref(w), ctypes.byref(sw), FAKE, 0,
+                            0, FAKE, nb, None)
+    assert call(_shared(lib, I=288), n.value) == lib.EUNSUPPORTED
+    assert call(_shared(lib, s1=None), n.value) == lib.EINVAL
+    assert call(_shared(lib, I=256), 0) == lib.EWORKSPACE

@@ -7,7 +7,8 @@ experts, no gate in the combine, w2 read transposed, h left unrounded, last inpu
 column dropped, wrong subnormal, sign bit ignored; for the MXFP8 mode: scale
 exponent off by one, no saturation, sign of FP8 dropped, ties away from zero;
 for the router logits: last input dropped, weight read transposed; for the
-saliency: a row missing from the norm, the gate left out)."""
+saliency: a row missing from the norm, the gate left out; for the shared
+expert: block-scale index transposed, w2 read transposed)."""
 import pytest
 
 import oracle
@@ -19,7 +20,8 @@ MUTANTS = {1: "nibble order", 2: "silu on w3", 3: "scale bias 126", 4: "one scal
            11: "subnormal = 1.0", 12: "sign ignored", 13: "mx8 scale exponent off by one",
            14: "fp8 not saturated", 15: "fp8 sign dropped", 16: "fp8 ties away from zero",
            17: "router last input dropped", 18: "router weight transposed",
-           19: "saliency norm misses a row", 20: "saliency without the gate"}
+           19: "saliency norm misses a row", 20: "saliency without the gate",
+           21: "shared block scale transposed", 22: "shared w2 transposed"}
 
 
 @pytest.mark.parametrize("n", sorted(MUTANTS), ids=lambda n: MUTANTS[n].replace(" ", "_"))
