@@ -258,10 +258,12 @@ __global__ void __launch_bounds__(kThreads) gemv2_combine_kernel(LayerArgs a) {
 
 // =========================================================================== one-token path
 // Lane l of a wave owns the 32-input groups g = l + 64 i (i < NXG) of the rows
-// it reads, and keeps the activations of those groups in registers for the
-// whole kernel: the weights are the only stream, and the inner loop is the FP4
-// decode (v_cvt_scalef32_pk_bf16_fp4) and the dot products (v_dot2c_f32_bf16,
-// bf16 products exact in fp32), with no LDS traffic and no per-chunk indexing.
+// it reads.  In the w1/w3 kernel the token's activations sit in LDS (read per
+// unit, 16 bytes per group and dword; in registers they would cost 48 VGPRs
+// and the kernel measured 0.7 us slower at H = 5120); in the w2 kernel each
+// lane keeps its 32 h values in registers.  The weights are the only HBM
+// stream, and the inner loop is the FP4 decode (v_cvt_scalef32_pk_bf16_fp4)
+// and the dot products (v_dot2c_f32_bf16, bf16 products exact in fp32).
 
 constexpr int kOneMaxXG = 4;      // x groups per lane: H <= 64 * 32 * 4
 constexpr int kOneMaxPL = 2;      // (slot, group) pairs per lane in the w2 kernel
@@ -348,16 +350,19 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = H / 32;
 
-  // this lane's x groups (clamped to the last group past the row end; their
-  // values are zeroed below, so the duplicate chunk adds exactly nothing)
-  int gc[NXG];
-  u32x4 xr[NXG][4];
+  // The token's x in LDS as 16-byte chunks (group g, dword q at 4 g + q),
+  // followed by one zero group.  A lane's groups past the row end load a
+  // duplicate weight chunk (clamped to the last group) and read the zero
+  // group of x, so they add exactly nothing.
+  __shared__ u32x4 xl[kOneMaxXG * kWave * 4 + 4];
+  for (int c = tid; c < CPR * 4; c += kThreads) xl[c] = ld16(a.x + 8 * c);
+  if (tid < 4) xl[4 * CPR + tid] = zero4();
+  int gc[NXG], xo[NXG];
 #pragma unroll
   for (int i = 0; i < NXG; ++i) {
     const int g = lane + kWave * i;
     gc[i] = g < CPR ? g : CPR - 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[i][q] = ld16(a.x + (size_t)gc[i] * 32 + 8 * q);
+    xo[i] = g < CPR ? 4 * g : 4 * CPR;
   }
   if (a.fused_route) {
     route_one(a, tb);
@@ -368,11 +373,6 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     }
     lds_barrier();
   }
-  bf16x8 X[NXG][4];
-#pragma unroll
-  for (int i = 0; i < NXG; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) X[i][q] = as_bf16x8(sel4(lane + kWave * i < CPR, xr[i][q]));
 
   const int nunits = a.k * I;
   const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
@@ -408,8 +408,9 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
       const float c1 = ue8m0_to_f32(B.s1[i]), c3 = ue8m0_to_f32(B.s3[i]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), X[i][q], G);
-        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), X[i][q], U);
+        const bf16x8 xq = as_bf16x8(xl[xo[i] + q]);
+        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), xq, G);
+        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), xq, U);
       }
     }
     G = wave_sum_f32(G);
