@@ -38,8 +38,8 @@ int sal_tiles(int H) { return (H + kSalRows - 1) / kSalRows; }
 
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
-  size_t logits, idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, h,
-      ypair, sal, xq, xqs, hq, hqs, total;
+  size_t logits, idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, perm,
+      h, ypair, sal, xq, xqs, hq, hqs, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
@@ -57,6 +57,8 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   L.slot_tok = o; o = align_up(o + P * 4);
   L.dinfo = o;    o = align_up(o + (size_t)d.E * 16);
   L.meta = o;     o = align_up(o + 64);
+  L.perm = o;     // per-block expert counts of the multi-block permutation
+  if (P > (size_t)kSmallRoutePairs) o = align_up(o + (size_t)kPermBlocksMax * d.E * 4);
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
   L.ypair = o;
   const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
@@ -144,6 +146,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   r.meta = at<int32_t>(ws, L.meta);
   r.slot_gate = at<float>(ws, L.slot_gate);
   r.slot_tok = at<int32_t>(ws, L.slot_tok);
+  if ((size_t)d.T * d.k > (size_t)kSmallRoutePairs) r.perm_scratch = at<int32_t>(ws, L.perm);
   // A one-token decode ranks the logits inside its first expert kernel.
   const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.I, d.E, d.k);
   r.ev = events;

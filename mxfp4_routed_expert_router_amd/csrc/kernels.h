@@ -46,7 +46,13 @@ struct RouteArgs {
   float* slot_gate;
   int32_t* slot_tok;
   const hipEvent_t* ev;  // optional stage timing (see ev_start)
+  // optional [kPermBlocksMax][E] scratch: with it (and dinfo, slot_gate) large
+  // batches are permuted by many workgroups instead of one
+  int32_t* perm_scratch;
 };
+
+constexpr int kPermBlocksMax = 256;  // workgroups of the multi-block permutation
+int perm_pairs_per_block(int P);     // pairs each of them owns (a multiple of 256)
 
 // Weights and routing state shared by the expert kernels.
 struct LayerArgs {

@@ -74,6 +74,11 @@ __device__ void block_excl_scan_e(int (&vals)[kMaxExperts / NTH], int* s_wsum, i
   lds_barrier();
 }
 
+template <int NTH>
+__device__ void scatter_range(const int32_t* idx, int p0, int p1, int E, int k,
+                              int32_t* sorted_pairs, int32_t* pair_slot, const float* gsrc,
+                              float* slot_gate, int32_t* slot_tok, PermSmem<NTH>& sm);
+
 // Histogram, scan and stable scatter of the P pairs of `idx` (LDS or global)
 // by one NTH-thread block.  Pairs are taken in chunks of NTH in pair order;
 // inside a chunk a pair's position is base[e] + (pairs of e in earlier waves of
@@ -130,9 +135,23 @@ __device__ void block_permute(const int32_t* idx, int P, int E, int k, int32_t* 
   if (dinfo)
     for (int x = nd + tid; x < (P < E ? P : E); x += NTH) dinfo[4 * x] = -1;
   lds_barrier();
-  for (int c0 = 0; c0 < P; c0 += NTH) {
+  scatter_range<NTH>(idx, 0, P, E, k, sorted_pairs, pair_slot, gsrc, slot_gate, slot_tok, sm);
+}
+
+// Stable scatter of pairs p0 .. p1-1 (sm.base[e] = the sorted position of the
+// first of them routed to expert e; sm.wcnt zero), in chunks of NTH in pair
+// order: inside a chunk a pair's position is base[e] + (pairs of e in earlier
+// waves of the chunk) + (pairs of e in earlier lanes of its wave), the lanes
+// holding the same expert found by 11 ballots on the expert id's bits.
+template <int NTH>
+__device__ void scatter_range(const int32_t* idx, int p0, int p1, int E, int k,
+                              int32_t* sorted_pairs, int32_t* pair_slot, const float* gsrc,
+                              float* slot_gate, int32_t* slot_tok, PermSmem<NTH>& sm) {
+  constexpr int NW = NTH / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  for (int c0 = p0; c0 < p1; c0 += NTH) {
     const int p = c0 + tid;
-    const bool valid = p < P;
+    const bool valid = p < p1;
     const int e = valid ? idx[p] : -1;
     // lanes of this wave holding the same expert
     uint64_t peers = ~0ull;
@@ -156,7 +175,7 @@ __device__ void block_permute(const int32_t* idx, int P, int E, int k, int32_t* 
       }
     }
     lds_barrier();
-    if (c0 + NTH < P) {  // advance the per-expert bases for the next chunk
+    if (c0 + NTH < p1) {  // advance the per-expert bases for the next chunk
       for (int x = tid; x < E; x += NTH) {
         int add = 0;
 #pragma unroll
@@ -188,6 +207,91 @@ permute_kernel(const int32_t* __restrict__ idx, const float* __restrict__ gates,
   }
   block_permute<kPermThreads>(src, P, E, k, counts, offsets, sorted_pairs, pair_slot, dinfo, meta,
                               gates, slot_gate, slot_tok, sm);
+}
+
+// Large batches inside the forward path (which has workspace for the per-block
+// counts): the permutation over many workgroups.  Block b owns the pairs
+// [b R, (b+1) R) in pair order.
+//   perm_hist_kernel     per-block expert histograms -> bcnt[b][e]
+//   perm_scan_kernel     counts, offsets, the distinct-expert records, and
+//                        bcnt[b][e] <- offsets[e] + pairs of e in blocks < b
+//   perm_scatter_kernel  each block scatters its pairs stably from bcnt[b][.]
+// The result is the same stable order as the single-block kernel's.
+constexpr int kPermBlockThreads = 256;
+
+__global__ void __launch_bounds__(kPermBlockThreads)
+perm_hist_kernel(const int32_t* __restrict__ idx, int P, int E, int R, int32_t* __restrict__ bcnt) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x, p0 = blockIdx.x * R, p1 = min(P, p0 + R);
+  for (int e = tid; e < E; e += kPermBlockThreads) cnt[e] = 0;
+  lds_barrier();
+  for (int p = p0 + tid; p < p1; p += kPermBlockThreads) atomicAdd(&cnt[idx[p]], 1);
+  lds_barrier();
+  for (int e = tid; e < E; e += kPermBlockThreads) bcnt[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+constexpr int kPermScanThreads = kMaxExperts;
+
+__global__ void __launch_bounds__(kPermScanThreads)
+perm_scan_kernel(int32_t* __restrict__ bcnt, int NB, int P, int E, int32_t* counts,
+                 int32_t* offsets, int32_t* dinfo, int32_t* meta) {
+  __shared__ PermSmem<kPermScanThreads> sm;
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 8 <= NB; b += 8) {  // eight independent loads in flight
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = bcnt[(size_t)(b + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bcnt[(size_t)(b + j) * E + e] = run;
+        run += c[j];
+      }
+    }
+    for (; b < NB; ++b) {
+      const int c = bcnt[(size_t)b * E + e];
+      bcnt[(size_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  int c[1] = {run}, f[1] = {run > 0 ? 1 : 0};
+  int total = 0, nd = 0;
+  block_excl_scan_e<kPermScanThreads>(c, sm.wsum, &total);
+  block_excl_scan_e<kPermScanThreads>(f, sm.wsum, &nd);
+  if (e < E) {
+    counts[e] = run;
+    offsets[e] = c[0];
+    if (run > 0) {
+      dinfo[4 * f[0] + 0] = e;
+      dinfo[4 * f[0] + 1] = c[0];
+      dinfo[4 * f[0] + 2] = run;
+      dinfo[4 * f[0] + 3] = 0;
+    }
+    for (int b = 0; b < NB; ++b) bcnt[(size_t)b * E + e] += c[0];
+  }
+  if (e == 0) {
+    offsets[E] = total;
+    meta[0] = nd;
+  }
+  for (int x = nd + e; x < (P < E ? P : E); x += kPermScanThreads) dinfo[4 * x] = -1;
+}
+
+__global__ void __launch_bounds__(kPermBlockThreads)
+perm_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ gates, int P, int E,
+                    int k, int R, const int32_t* __restrict__ bcnt, int32_t* sorted_pairs,
+                    int32_t* pair_slot, float* slot_gate, int32_t* slot_tok) {
+  __shared__ PermSmem<kPermBlockThreads> sm;
+  const int tid = threadIdx.x, p0 = blockIdx.x * R, p1 = min(P, p0 + R);
+  for (int e = tid; e < E; e += kPermBlockThreads) {
+    sm.base[e] = bcnt[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < kPermBlockThreads / kWave; ++q) sm.wcnt[q][e] = 0;
+  }
+  lds_barrier();
+  scatter_range<kPermBlockThreads>(idx, p0, p1, E, k, sorted_pairs, pair_slot, gates, slot_gate,
+                                   slot_tok, sm);
 }
 
 // Small batches: top-k and permutation in one launch of 256 threads.  The four
@@ -223,6 +327,12 @@ int vpl_for(int E) {
 
 }  // namespace
 
+int perm_pairs_per_block(int P) {
+  const int chunks = (P + kPermBlockThreads - 1) / kPermBlockThreads;
+  const int per = (chunks + kPermBlocksMax - 1) / kPermBlocksMax;  // chunks per block
+  return per * kPermBlockThreads;
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int P = a.T * a.k;
   const int vpl = vpl_for(a.E);
@@ -255,9 +365,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
       default: MOE_TOPK(16); break;
     }
 #undef MOE_TOPK
-    launch_k(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, (hipEvent_t) nullptr,
-             ev_stop(a.ev, 0), (const int32_t*)a.idx, (const float*)a.gates, P, a.E, a.k, a.counts,
-             a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok);
+    if (a.perm_scratch && a.dinfo && a.slot_gate) {
+      const int R = perm_pairs_per_block(P), NB = (P + R - 1) / R;
+      launch_k(perm_hist_kernel, dim3(NB), dim3(kPermBlockThreads), 0, stream,
+               (hipEvent_t) nullptr, (hipEvent_t) nullptr, (const int32_t*)a.idx, P, a.E, R,
+               a.perm_scratch);
+      launch_k(perm_scan_kernel, dim3(1), dim3(kPermScanThreads), 0, stream, (hipEvent_t) nullptr,
+               (hipEvent_t) nullptr, a.perm_scratch, NB, P, a.E, a.counts, a.offsets, a.dinfo,
+               a.meta);
+      launch_k(perm_scatter_kernel, dim3(NB), dim3(kPermBlockThreads), 0, stream,
+               (hipEvent_t) nullptr, ev_stop(a.ev, 0), (const int32_t*)a.idx,
+               (const float*)a.gates, P, a.E, a.k, R, (const int32_t*)a.perm_scratch,
+               a.sorted_pairs, a.pair_slot, a.slot_gate, a.slot_tok);
+    } else {
+      launch_k(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, (hipEvent_t) nullptr,
+               ev_stop(a.ev, 0), (const int32_t*)a.idx, (const float*)a.gates, P, a.E, a.k,
+               a.counts, a.offsets, a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate,
+               a.slot_tok);
+    }
   }
   return hipGetLastError();
 }

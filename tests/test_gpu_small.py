@@ -137,8 +137,10 @@ def test_forward_small(moe, orc, T, H, I, E, k, mode):
     _forward_case(moe, orc, T, H, I, E, k, seed=T * 7 + H + I, mode=mode)
 
 
-@pytest.mark.parametrize("T", [40, 130, 300])
+@pytest.mark.parametrize("T", [40, 130, 300, 700, 3000])
 def test_forward_prefill_many_tokens(moe, orc, T):
+    """Experts with more than 64 tokens (several passes); above 1024 pairs
+    (T = 700, 3000) the permutation runs on many workgroups."""
     say(f"forward prefill T={T}: experts with more than 64 tokens (several passes)")
     _forward_case(moe, orc, T, 128, 96, 3, 2, seed=T, mode=2)
 
