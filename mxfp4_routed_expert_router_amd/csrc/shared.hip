@@ -9,7 +9,7 @@
 // decoded to bf16 (v_cvt_scalef32_pk_bf16_fp8) and every product is exact in
 // fp32, as on the routed path.
 //
-//   shared_gemv_kernel<M>  T <= 4: one wave per output row; lane l takes the
+//   shared_gemv_kernel<M, C>  T <= 4: one wave per output row; lane l takes the
 //                          16-byte chunks l + 64 j of the row (16 codes each,
 //                          whole lines per load), the wave reduces with DPP.
 //   shared_gemm_kernel<M>  T > 4: 64 rows x 64 tokens per workgroup, four
@@ -48,9 +48,11 @@ struct SharedArgs {
 };
 
 constexpr int kGvMaxT = 4;
-constexpr int kGvChunks = 8;  // 16-byte chunks per lane and round: K <= 8192 in one round
+constexpr int kGvMaxChunks = 8;  // 16-byte chunks per lane and round (K <= 8192 in one round)
 
-template <int M>
+// kGvChunks: chunks per lane and round, the smallest that covers K in one
+// round (registers are sized by it, so the whole grid stays resident).
+template <int M, int kGvChunks>
 __global__ void __launch_bounds__(4 * kWave) shared_gemv_kernel(SharedArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -225,11 +227,27 @@ __global__ void __launch_bounds__(kSThreads) shared_gemm_kernel(SharedArgs a) {
   }
 }
 
+template <int M, int C>
+void launch_gemv(const SharedArgs& s, hipStream_t stream) {
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(shared_gemv_kernel<M, C>), dim3((s.N + 3) / 4), dim3(4 * kWave),
+                     0, stream, s);
+}
+
 template <int M>
 void launch_one_gemm(const SharedArgs& s, hipStream_t stream) {
-  if (s.T <= kGvMaxT)
-    hipLaunchKernelGGL(shared_gemv_kernel<M>, dim3((s.N + 3) / 4), dim3(4 * kWave), 0, stream, s);
-  else
+  if (s.T <= kGvMaxT) {
+    const int ncl = (s.K / 16 + kWave - 1) / kWave;  // chunks per lane
+    switch (ncl < kGvMaxChunks ? ncl : kGvMaxChunks) {
+      case 1: launch_gemv<M, 1>(s, stream); break;
+      case 2: launch_gemv<M, 2>(s, stream); break;
+      case 3: launch_gemv<M, 3>(s, stream); break;
+      case 4: launch_gemv<M, 4>(s, stream); break;
+      case 5: launch_gemv<M, 5>(s, stream); break;
+      case 6: launch_gemv<M, 6>(s, stream); break;
+      case 7: launch_gemv<M, 7>(s, stream); break;
+      default: launch_gemv<M, 8>(s, stream); break;
+    }
+  } else
     hipLaunchKernelGGL(shared_gemm_kernel<M>, dim3((s.N + kST - 1) / kST, (s.T + kST - 1) / kST),
                        dim3(kSThreads), 0, stream, s);
 }
