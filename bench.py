@@ -260,6 +260,77 @@ def main():
         f"{us_shared_only:.2f} us ({shared['shared_GBps']:.0f} GB/s)")
     del sw_d
 
+    # ---------------------------------------------------------------- speculative-verify batches
+    # T = 6 and T = 32 tokens per step on the same 384 resident experts.
+    from synth.configs import VERIFY6, VERIFY32, STACK1, STACK6
+    verify = {}
+    for vw in (VERIFY6, VERIFY32):
+        n_v = min(vw.steps, 64)
+        xv = torch.from_numpy(np.stack([synth.gen_x(vw, s) for s in range(n_v)]).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        lv_np = np.stack([synth.gen_logits(vw, s) for s in range(n_v)])
+        lv = torch.from_numpy(lv_np).to(dev)
+        yv = torch.empty((vw.T, vw.H), dtype=torch.float32, device=dev)
+        wsv = torch.empty(moe.moe_fp4_workspace_size(vw.T, vw.H, vw.I, vw.E, vw.k), dtype=torch.uint8,
+                          device=dev)
+
+        def step_v(i, xv=xv, lv=lv, yv=yv, wsv=wsv, vw=vw, n_v=n_v):
+            j = i % n_v
+            moe.moe_fp4_forward(xv[j], lv[j], w, vw.k, y=yv, workspace=wsv)
+
+        us_v = graph_us(step_v)
+        d_v = [len(np.unique(topk_sets(lv_np[s], vw.k))) for s in range(n_v)]
+        b_v = float(np.mean(d_v)) * expert_bytes(vw.H, vw.I)
+        verify[vw.name] = {"T": vw.T, "us_per_step": us_v, "us_per_token": us_v / vw.T,
+                           "distinct_experts": float(np.mean(d_v)), "bytes_per_step": b_v,
+                           "GBps": b_v / (us_v * 1e-6) / 1e9}
+        log(f"verify T={vw.T}: {us_v:.2f} us/step ({us_v / vw.T:.2f} us/token), "
+            f"{np.mean(d_v):.1f} distinct experts, {b_v / (us_v * 1e-6) / 1e9:.0f} GB/s")
+        del xv, lv, yv, wsv
+
+    # ---------------------------------------------------------------- pruned resident stack
+    # 40 layers x 138 experts (103.8 GB in HBM), x_{l+1} = x_l + moe_l(prenorm(x_l)),
+    # every layer of every token in one graph.
+    stack = {}
+    t0 = time.time()
+    layers = [moe.ExpertWeights.from_dict(synth.layer_device(STACK1, layer=l, device=dev))
+              for l in range(STACK1.layers)]
+    torch.cuda.synchronize()
+    log(f"stack: {STACK1.layers} x {STACK1.E} experts generated in HBM in {time.time() - t0:.1f} s")
+    for sw_ in (STACK1, STACK6):
+        n_s = min(sw_.steps, 16)
+        xs0 = torch.from_numpy(np.stack([synth.gen_x_f32(sw_, s) for s in range(n_s)])).to(dev)
+        lgs_np = [[synth.gen_logits(sw_, s, l) for l in range(sw_.layers)] for s in range(n_s)]
+        lgs_s = [[torch.from_numpy(a).to(dev) for a in row] for row in lgs_np]
+        xst = xs0.clone()
+        us_ = torch.empty((sw_.T, sw_.H), dtype=torch.bfloat16, device=dev)
+        wss = torch.empty(moe.moe_fp4_workspace_size(sw_.T, sw_.H, sw_.I, sw_.E, sw_.k),
+                          dtype=torch.uint8, device=dev)
+
+        def step_s(i, xst=xst, us_=us_, wss=wss, lgs_s=lgs_s, sw_=sw_, n_s=n_s):
+            j = i % n_s
+            for l in range(sw_.layers):
+                moe.moe_fp4_prenorm_bf16(xst[j], out=us_)
+                moe.moe_fp4_forward(us_, lgs_s[j][l], layers[l], sw_.k, y=xst[j], accumulate=True,
+                                    workspace=wss)
+
+        # a few steps per graph (each step is 40 layer calls)
+        saved = (args.warmup, args.steps)
+        args.warmup, args.steps = 2, n_s
+        us_step = graph_us(step_s)
+        args.warmup, args.steps = saved
+        d_s = [sum(len(np.unique(topk_sets(lgs_np[s][l], sw_.k))) for l in range(sw_.layers))
+               for s in range(n_s)]
+        b_s = float(np.mean(d_s)) * expert_bytes(sw_.H, sw_.I)
+        stack[sw_.name] = {"T": sw_.T, "layers": sw_.layers, "E": sw_.E,
+                           "us_per_step": us_step, "tokens_per_s": sw_.T / (us_step * 1e-6),
+                           "bytes_per_step": b_s, "GBps": b_s / (us_step * 1e-6) / 1e9}
+        log(f"stack T={sw_.T}: {us_step / 1e3:.3f} ms per pass of {sw_.layers} layers, "
+            f"{sw_.T / (us_step * 1e-6):.0f} tokens/s, {b_s / (us_step * 1e-6) / 1e9:.0f} GB/s")
+        del xs0, xst, us_, wss, lgs_s
+    del layers
+    torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- decode, cold caches
     # A read-only flush (summing a 1 GiB buffer) between steps evicts the
     # experts from L2 and the MALL without leaving dirty lines whose write-back
@@ -397,6 +468,8 @@ def main():
         "cold": cold,
         "decode_routed": routed,
         "decode_shared": shared,
+        "verify": verify,
+        "stack": stack,
         "prefill": prefill,
         "prefill_mxfp8": prefill_mx,
         "cpu_baseline": cpu,
