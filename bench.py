@@ -303,16 +303,13 @@ def main():
         lgs_np = [[synth.gen_logits(sw_, s, l) for l in range(sw_.layers)] for s in range(n_s)]
         lgs_s = [[torch.from_numpy(a).to(dev) for a in row] for row in lgs_np]
         xst = xs0.clone()
-        us_ = torch.empty((sw_.T, sw_.H), dtype=torch.bfloat16, device=dev)
         wss = torch.empty(moe.moe_fp4_workspace_size(sw_.T, sw_.H, sw_.I, sw_.E, sw_.k),
                           dtype=torch.uint8, device=dev)
 
-        def step_s(i, xst=xst, us_=us_, wss=wss, lgs_s=lgs_s, sw_=sw_, n_s=n_s):
+        def step_s(i, xst=xst, wss=wss, lgs_s=lgs_s, sw_=sw_, n_s=n_s):
             j = i % n_s
-            for l in range(sw_.layers):
-                moe.moe_fp4_prenorm_bf16(xst[j], out=us_)
-                moe.moe_fp4_forward(us_, lgs_s[j][l], layers[l], sw_.k, y=xst[j], accumulate=True,
-                                    workspace=wss)
+            for l in range(sw_.layers):  # x += moe_l(prenorm(x)), one call per layer
+                moe.moe_fp4_forward_residual(xst[j], lgs_s[j][l], layers[l], sw_.k, workspace=wss)
 
         # a few steps per graph (each step is 40 layer calls)
         saved = (args.warmup, args.steps)
@@ -327,7 +324,7 @@ def main():
                            "bytes_per_step": b_s, "GBps": b_s / (us_step * 1e-6) / 1e9}
         log(f"stack T={sw_.T}: {us_step / 1e3:.3f} ms per pass of {sw_.layers} layers, "
             f"{sw_.T / (us_step * 1e-6):.0f} tokens/s, {b_s / (us_step * 1e-6) / 1e9:.0f} GB/s")
-        del xs0, xst, us_, wss, lgs_s
+        del xs0, xst, wss, lgs_s
     del layers
     torch.cuda.empty_cache()
 

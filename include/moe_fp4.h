@@ -242,6 +242,19 @@ int moe_fp4_forward_shared(const moe_fp4_dims *dims, const uint16_t *x, const fl
                            const moe_fp4_weights *w, const moe_fp4_shared_weights *sw, float *y,
                            int mode, int flags, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* One layer of a residual stack, in place (the pre-norm of moe_fp4_prenorm_bf16
+ * with eps = 1e-6, then the layer, its output added to the residual stream):
+ *   x[t] += layer( bf16(x[t] / sqrt(mean_m x[t][m]^2 + 1e-6)) )
+ *   x       [T][H] fp32, 16-byte aligned, read and updated
+ *   logits, w, mode, ws, ws_bytes: as moe_fp4_forward (same workspace size)
+ * Same bits as moe_fp4_prenorm_bf16 into a bf16 buffer followed by
+ * moe_fp4_forward(..., y = x, MOE_FP4_ACCUMULATE).  On the one-token decode
+ * path the pre-norm runs inside the first expert kernel (no launch of its own).
+ * Errors: as moe_fp4_forward. */
+int moe_fp4_forward_residual(const moe_fp4_dims *dims, float *x, const float *logits,
+                             const moe_fp4_weights *w, int mode, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Pre-normalisation for a residual stack of layers:
  *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
  *   x [T][H] fp32, u [T][H] bf16 bits.

@@ -11,4 +11,5 @@ from ._lib import (ACCUMULATE, MODE_AUTO, MODE_DECODE, MODE_PREFILL,  # noqa: F4
                    moe_fp4_prenorm_bf16, moe_fp4_quant_mxfp8, moe_fp4_route,
                    moe_fp4_router_logits, moe_fp4_forward_routed, moe_fp4_forward_saliency,
                    SharedWeights, moe_fp4_shared_expert, moe_fp4_forward_shared,
+                   moe_fp4_forward_residual,
                    moe_fp4_workspace_size, status_string)

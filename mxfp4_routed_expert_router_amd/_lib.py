@@ -69,13 +69,15 @@ def _load():
                                           P, I32, P, P]
     lib.moe_fp4_forward_shared.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
                                            ctypes.POINTER(SharedWeightsStruct), P, I32, I32, P, SZ, P]
+    lib.moe_fp4_forward_residual.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
+                                             I32, P, SZ, P]
     lib.moe_fp4_forward_saliency.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
                                              P, P, I32, I32, P, SZ, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
               "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency",
-              "moe_fp4_shared_expert", "moe_fp4_forward_shared"):
+              "moe_fp4_shared_expert", "moe_fp4_forward_shared", "moe_fp4_forward_residual"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -439,6 +441,25 @@ def moe_fp4_forward_shared(x: torch.Tensor, logits: torch.Tensor, weights: Exper
                                        workspace.data_ptr(), workspace.numel(), _stream(x)),
            "moe_fp4_forward_shared")
     return y
+
+
+def moe_fp4_forward_residual(x: torch.Tensor, logits: torch.Tensor, weights: ExpertWeights, k: int,
+                             mode: int = MODE_AUTO, workspace: Optional[torch.Tensor] = None):
+    """One residual layer in place: x [T, H] fp32 += layer(bf16(x / rms(x)))."""
+    _need(x, "x", (torch.float32,), 2)
+    _need(logits, "logits", (torch.float32,), 2)
+    T, H = x.shape
+    E = logits.shape[1]
+    I = weights.intermediate()
+    need = moe_fp4_workspace_size(T, H, I, E, k, mode)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws = weights.as_struct()
+    _check(_lib.moe_fp4_forward_residual(ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(),
+                                         logits.data_ptr(), ctypes.byref(ws), mode,
+                                         workspace.data_ptr(), workspace.numel(), _stream(x)),
+           "moe_fp4_forward_residual")
+    return x
 
 
 def moe_fp4_quant_mxfp8(x: torch.Tensor):

@@ -12,6 +12,7 @@ using namespace moe_fp4;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr float kStackEps = 1e-6f;  // the residual stack's pre-norm epsilon
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -39,7 +40,7 @@ int sal_tiles(int H) { return (H + kSalRows - 1) / kSalRows; }
 // Workspace sections, each 256-byte aligned.
 struct WsLayout {
   size_t logits, idx, gates, counts, offsets, sorted, slot, slot_gate, slot_tok, dinfo, meta, perm,
-      h, ypair, sal, xq, xqs, hq, hqs, total;
+      h, ypair, sal, xq, xqs, hq, hqs, u, total;
 };
 
 WsLayout layout(const moe_fp4_dims& d, int rmode) {
@@ -61,6 +62,8 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   if (P > (size_t)kSmallRoutePairs) o = align_up(o + (size_t)kPermBlocksMax * d.E * 4);
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
   L.ypair = o;
+  L.u = o;  // pre-normed input of moe_fp4_forward_residual: ypair's space in the prefill modes
+  if (rmode == MOE_FP4_MODE_DECODE) o = align_up(o + (size_t)d.T * d.H * 2);
   const bool mx = rmode == MOE_FP4_MODE_PREFILL_MXFP8;
   if (rmode == MOE_FP4_MODE_PREFILL || mx) {
     o = align_up(o + P * (size_t)d.H * 4);
@@ -88,12 +91,19 @@ T* at(void* ws, size_t off) {
 // Exactly one of logits and w_router is given; with w_router the logits are
 // computed into the workspace first.
 // With saliency (prefill modes only) the per-expert saliency is added to it.
+// With x_resid (x null, y = x_resid) the layer's input is the pre-norm of
+// x_resid and its output is added to it.
 int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
                  const uint16_t* w_router, const moe_fp4_weights* w, float* y, int mode, int flags,
                  void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                  moe_fp4_route_out* route_out, const hipEvent_t* events,
-                 float* saliency = nullptr) {
-  if (!dims || !x || !(logits || w_router) || !w || !y || !ws) return MOE_FP4_EINVAL;
+                 float* saliency = nullptr, float* x_resid = nullptr) {
+  if (x_resid) {
+    if (x) return MOE_FP4_EINVAL;
+    y = x_resid;
+    flags |= MOE_FP4_ACCUMULATE;
+  }
+  if (!dims || !(x || x_resid) || !(logits || w_router) || !w || !y || !ws) return MOE_FP4_EINVAL;
   if (!w->w1 || !w->s1 || !w->w3 || !w->s3 || !w->w2 || !w->s2) return MOE_FP4_EINVAL;
   if (route_out && (!route_out->topk_idx || !route_out->gates || !route_out->counts ||
                     !route_out->offsets || !route_out->sorted_pairs || !route_out->pair_slot))
@@ -115,7 +125,8 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
                           (int64_t)d.H * d.I / 2, (int64_t)d.H * d.I / 32};
   int64_t stride[6];
   for (int i = 0; i < 6; ++i) stride[i] = w->expert_stride[i] ? w->expert_stride[i] : per[i];
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(w->w1, 16) ||
+  if (!aligned(x_resid ? (const void*)x_resid : (const void*)x, 16) || !aligned(y, 16) ||
+      !aligned(ws, kAlign) || !aligned(w->w1, 16) ||
       !aligned(w->w3, 16) || !aligned(w->w2, 16) || stride[0] % 16 || stride[2] % 16 ||
       stride[4] % 16 || (h_out && !aligned(h_out, 4)) || (w_router && !aligned(w_router, 16)))
     return MOE_FP4_EALIGN;
@@ -127,6 +138,15 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   const WsLayout L = layout(d, rmode);
   if (ws_bytes < L.total) return MOE_FP4_EWORKSPACE;
 
+  // the pre-norm: inside the w1/w3 kernel on the one-token path, else a
+  // kernel of its own into the workspace
+  const bool prenorm_fused =
+      x_resid && rmode == MOE_FP4_MODE_DECODE && decode_one_token(d.T, d.H, d.I, d.k);
+  if (x_resid && !prenorm_fused) {
+    uint16_t* const u = at<uint16_t>(ws, L.u);
+    if (launch_prenorm(x_resid, u, d.T, d.H, kStackEps, stream) != hipSuccess) return MOE_FP4_EHIP;
+    x = u;
+  }
   if (w_router) {
     float* const lg = at<float>(ws, L.logits);
     if (launch_router_logits(x, w_router, lg, d.T, d.H, d.E, stream) != hipSuccess)
@@ -178,6 +198,10 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   a.fused_route = fused ? 1 : 0;
   a.route = r;
   a.logits = logits;
+  if (prenorm_fused) {
+    a.xf = x_resid;
+    a.eps = kStackEps;
+  }
   if (saliency) {
     a.sal_part = at<float>(ws, L.sal);
     a.sal_tiles = sal_tiles(d.H);
@@ -269,6 +293,14 @@ int moe_fp4_forward_routed(const moe_fp4_dims* dims, const uint16_t* x, const ui
   if (!w_router) return MOE_FP4_EINVAL;
   return forward_impl(dims, x, nullptr, w_router, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
                       nullptr, nullptr);
+}
+
+int moe_fp4_forward_residual(const moe_fp4_dims* dims, float* x, const float* logits,
+                             const moe_fp4_weights* w, int mode, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (!x) return MOE_FP4_EINVAL;
+  return forward_impl(dims, nullptr, logits, nullptr, w, nullptr, mode, 0, ws, ws_bytes, stream,
+                      nullptr, nullptr, nullptr, nullptr, x);
 }
 
 int moe_fp4_forward_saliency(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,

@@ -355,7 +355,25 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   // duplicate weight chunk (clamped to the last group) and read the zero
   // group of x, so they add exactly nothing.
   __shared__ u32x4 xl[kOneMaxXG * kWave * 4 + 4];
-  for (int c = tid; c < CPR * 4; c += kThreads) xl[c] = ld16(a.x + 8 * c);
+  if (a.xf) {
+    // the layer's input is the pre-norm of the fp32 row xf (same bits as
+    // moe_fp4_prenorm_bf16: row_rms, then one division and rounding per value)
+    __shared__ float wsum[4];
+    const float r = row_rms(a.xf, H, a.eps, wsum);
+    for (int c = tid; c < CPR * 4; c += kThreads) {
+      const float4 v0 = *reinterpret_cast<const float4*>(a.xf + 8 * c);
+      const float4 v1 = *reinterpret_cast<const float4*>(a.xf + 8 * c + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] / r) |
+               ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] / r) << 16);
+      xl[c] = o;
+    }
+  } else {
+    for (int c = tid; c < CPR * 4; c += kThreads) xl[c] = ld16(a.x + 8 * c);
+  }
   if (tid < 4) xl[4 * CPR + tid] = zero4();
   int gc[NXG], xo[NXG];
 #pragma unroll
@@ -606,6 +624,8 @@ bool decode_fits(int T, int H, int I, int k) {
   return T <= kDecodeMaxTokens && I <= kWaves * kB2 * 128 && lds13_bytes(T, H) <= kDecodeLds &&
          lds2_bytes(P, I) <= kDecodeLds;
 }
+
+bool decode_one_token(int T, int H, int I, int k) { return T == 1 && one_token_fits(H, I, k); }
 
 bool decode_fuses_route(int T, int H, int I, int E, int k) {
   return T == 1 && one_token_fits(H, I, k) && E <= kFusedVPL * kWave;

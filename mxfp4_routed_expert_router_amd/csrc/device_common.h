@@ -142,6 +142,28 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return umin32(umin32(r0, r1), umin32(r2, r3));
 }
 
+// RMS of one row for the pre-normalisation u = bf16(x / rms), rms =
+// sqrt(mean(x^2) + eps): threads 0..255 of the workgroup sum the squares of
+// elements tid, tid + 256, ... in that order, each wave reduces with XOR
+// shuffles, and the four wave sums are added as ((w0 + w1) + w2) + w3.  Every
+// thread of the workgroup must call it (it has a barrier); all get the value.
+// wsum: 4 floats of LDS.  The standalone pre-norm and the fused one use it, so
+// both give the same bits.
+__device__ __forceinline__ float row_rms(const float* __restrict__ xr, int H, float eps,
+                                         float* wsum) {
+  const int tid = threadIdx.x;
+  if (tid < 256) {
+    float ss = 0.f;
+    for (int m = tid; m < H; m += 256) ss += xr[m] * xr[m];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  }
+  __syncthreads();
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  return sqrtf(tot / (float)H + eps);
+}
+
 template <int V>
 struct IntC {
   static constexpr int value = V;

@@ -81,11 +81,16 @@ struct LayerArgs {
   int fused_route;
   RouteArgs route;
   const float* logits;
+  // one-token decode with the pre-norm inside the w1/w3 kernel: x is then
+  // unused and the layer's input is bf16(xf / sqrt(mean(xf^2) + eps))
+  const float* xf;
+  float eps;
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 bool decode_fits(int T, int H, int I, int k);  // shapes the decode kernels take
 bool decode_fuses_route(int T, int H, int I, int E, int k);  // decode routes in its first kernel
+bool decode_one_token(int T, int H, int I, int k);           // the one-token decode kernels run
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream);

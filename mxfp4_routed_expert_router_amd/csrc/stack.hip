@@ -9,19 +9,12 @@ namespace moe_fp4 {
 namespace {
 
 // One workgroup per token row: u = bf16(x / sqrt(mean(x^2) + eps)).  The sum of
-// squares is reduced in a fixed order, so u is reproducible bit for bit.
+// squares is reduced in a fixed order (row_rms), so u is reproducible bit for bit.
 __global__ void __launch_bounds__(256) prenorm_kernel(const float* __restrict__ x,
                                                       uint16_t* __restrict__ u, int H, float eps) {
   __shared__ float wsum[4];
   const float* xr = x + (size_t)blockIdx.x * H;
-  float ss = 0.f;
-  for (int m = threadIdx.x; m < H; m += 256) ss += xr[m] * xr[m];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-  const float r = sqrtf(tot / (float)H + eps);
+  const float r = row_rms(xr, H, eps, wsum);
   uint16_t* ur = u + (size_t)blockIdx.x * H;
   for (int m = threadIdx.x; m < H; m += 256) ur[m] = f32_to_bf16_rne(xr[m] / r);
 }

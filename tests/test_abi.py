@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for n in ("moe_fp4_route", "moe_fp4_forward", "moe_fp4_forward_debug",
               "moe_fp4_workspace_size", "moe_fp4_prenorm_bf16", "moe_fp4_status_string",
               "moe_fp4_quant_mxfp8", "moe_fp4_router_logits", "moe_fp4_forward_routed",
-              "moe_fp4_forward_saliency", "moe_fp4_shared_expert", "moe_fp4_forward_shared"):
+              "moe_fp4_forward_saliency", "moe_fp4_shared_expert", "moe_fp4_forward_shared",
+              "moe_fp4_forward_residual"):
         assert n in names
 
 
@@ -306,3 +307,15 @@ def test_forward_shared_validation(lib):
     assert call(_shared(lib, I=288), n.value) == lib.EUNSUPPORTED
     assert call(_shared(lib, s1=None), n.value) == lib.EINVAL
     assert call(_shared(lib, I=256), 0) == lib.EWORKSPACE
+
+
+def test_forward_residual_validation(lib):
+    f = lib._lib.moe_fp4_forward_residual
+    d = lib.Dims(4, 256, 128, 16, 2)
+    w = _weights(lib)
+    n = ctypes.c_size_t()
+    assert lib._lib.moe_fp4_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == lib.OK
+    call = lambda x, nb: f(ctypes.byref(d), x, FAKE, ctypes.byref(w), 0, FAKE, nb, None)
+    assert call(None, n.value) == lib.EINVAL
+    assert call(FAKE + 8, n.value) == lib.EALIGN
+    assert call(FAKE, 0) == lib.EWORKSPACE

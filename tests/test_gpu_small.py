@@ -318,3 +318,38 @@ def test_device_generator_matches_host(moe):
         h = synth.expert_host(DECODE, 0, e)
         for n in h:
             assert np.array_equal(dev[n][e].cpu().numpy(), h[n]), (e, n)
+
+
+RESIDUAL_CASES = [  # (T, H, I, E, k, mode): one-token path (pre-norm fused), decode MFMA, prefill, MXFP8
+    (1, 256, 128, 16, 2, 0),
+    (1, 5120, 2304, 8, 6, 0),
+    (2, 256, 128, 16, 2, 1),
+    (40, 256, 128, 24, 6, 2),
+    (40, 256, 128, 24, 6, 3),
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,mode", RESIDUAL_CASES)
+def test_forward_residual(moe, orc, T, H, I, E, k, mode):
+    """x += layer(prenorm(x)) in one call: the same bits as the pre-norm entry
+    point followed by an accumulating forward, and the oracle's stack layer."""
+    import torch
+    say(f"forward_residual T={T} H={H} I={I} E={E} k={k} mode={mode}")
+    rng = np.random.default_rng(T * 3 + H + mode)
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
+    w = dev_weights(dense)
+    x0 = (rng.standard_normal((T, H)) * 3.0).astype(np.float32)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lgd = torch.from_numpy(lg).cuda()
+    x1 = torch.from_numpy(x0).cuda()
+    moe.moe_fp4_forward_residual(x1, lgd, w, k, mode=mode)
+    x2 = torch.from_numpy(x0).cuda()
+    u = moe.moe_fp4_prenorm_bf16(x2)
+    moe.moe_fp4_forward(u, lgd, w, k, y=x2, mode=mode, accumulate=True)
+    torch.cuda.synchronize()
+    x1, x2 = x1.cpu().numpy(), x2.cpu().numpy()
+    assert np.array_equal(x1.view(np.uint32), x2.view(np.uint32))
+    if mode != 3:
+        xr = orc.stack_layer(I, E, k, x0, lg, experts)
+        check_y(x1.astype(np.float64) - x0, xr.astype(np.float64) - x0, f"residual mode={mode}")
