@@ -125,6 +125,9 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (1, 352, 96, 7, 3),       # one token, ragged groups
     (1, 256, 2080, 10, 5),    # one token, 65 groups per w2 row
     (1, 256, 1024, 16, 16),   # one token, k = 16: k * I / 32 at the one-token path's limit
+    (100, 64, 32, 1024, 16),  # E = 1024, k = 16: the largest router tables, 1600 pairs
+    (1, 16384, 64, 4, 2),     # H at its limit: T = 1 on the MFMA decode kernels
+    (2, 64, 16384, 3, 2),     # I at its limit (prefill only)
 ]
 
 
