@@ -88,107 +88,9 @@ def profiled_traffic(kernel):
     return float(k["read_bytes"] + k["write_bytes"])
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--prefill-reps", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode figure")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the layer runs on a single MI355X and this build has "
-              "no multi-GPU path (--gpus must be 1).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import synth
-    import mxfp4_routed_expert_router_amd as moe
-    from synth.configs import DECODE as wl, PREFILL as pf
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"device: {torch.cuda.get_device_name(dev)}")
-
-    # ---------------------------------------------------------------- set-up
-    t0 = time.time()
-    w = moe.ExpertWeights.from_dict(synth.layer_device(wl, layer=0, device=dev))
-    torch.cuda.synchronize()
-    log(f"weights: {wl.E} experts x {expert_bytes(wl.H, wl.I)} B generated in HBM "
-        f"in {time.time() - t0:.1f} s")
-    n_tok = max(args.steps, 1)
-    n_gen = min(wl.steps, n_tok + args.warmup)
-    xs = np.stack([synth.gen_x(wl, s)[0] for s in range(n_gen)])
-    lgs = np.stack([synth.gen_logits(wl, s)[0] for s in range(n_gen)])
-    x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
-    lg_d = torch.from_numpy(lgs).to(dev)
-    y_d = torch.empty((n_gen, wl.H), dtype=torch.float32, device=dev)
-    ws = torch.empty(moe.moe_fp4_workspace_size(1, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8,
-                     device=dev)
-    idx_all = topk_sets(lgs, wl.k)
-
-    def step(i, events=None):
-        j = i % n_gen
-        xi, li, yi = x_d[j:j + 1], lg_d[j:j + 1], y_d[j:j + 1]
-        if events is None:
-            moe.moe_fp4_forward(xi, li, w, wl.k, y=yi, workspace=ws)
-        else:
-            moe.moe_fp4_forward_profiled(xi, li, w, wl.k, events, y=yi, workspace=ws)
-
-    # ---------------------------------------------------------------- decode, timed
-    # The steps are captured once into HIP graphs and replayed: a serving loop
-    # issues a layer call this way, and it keeps the host's per-call launch
-    # overhead (Python + ctypes, tens of microseconds) out of the GPU timeline.
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    g_plain = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_plain):
-        for i in range(args.steps):
-            step(args.warmup + i)
-    g_plain.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    g_plain.replay()
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
-
-    # Kernel durations: each kernel's dispatch records a start and an end event
-    # on the layer's stream (moe_fp4_forward_profiled).  The steps are enqueued
-    # behind a spin kernel so that they are all queued before the first one runs
-    # and execute back to back, as in the graph.
-    evs = [moe.StageEvents() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SPIN_CYCLES)
-    tp0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[-1]) / args.steps
-    stage = np.array([e.stage_ms() for e in evs])  # [steps, 4]: route, w13, w2, combine
-    k_ms = {"route": float(stage[:, 0].mean()), "w13": float(stage[:, 1].mean()),
-            "w2": float(stage[:, 2].mean())}
-    by = [decode_bytes(wl, idx_all[(args.warmup + i) % n_gen][None]) for i in range(args.steps)]
-    k_bytes = {n: float(np.mean([b[n] for b in by])) for n in ("route", "w13", "w2")}
-    step_bytes = k_bytes["route"] + k_bytes["w13"] + k_bytes["w2"]
-    us_tok = ms_per_step * 1e3 / wl.T
-    dom = max(("w13", "w2"), key=lambda n: k_ms[n])
-    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
-    log(f"decode: {us_tok:.2f} us/token graph replay ({step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s "
-        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us per step with timed dispatches); kernels route "
-        f"{k_ms['route'] * 1e3:.2f} us, w1/w3 {k_ms['w13'] * 1e3:.2f} us, "
-        f"w2+combine {k_ms['w2'] * 1e3:.2f} us")
-    eager_t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
-    log(f"decode eager (one Python call per step): {us_eager:.2f} us/token")
-
+def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, graph_us):
+    """Decode with the router step and with the shared expert, the
+    speculative-verify batches and the pruned 40-layer stack."""
     # ---------------------------------------------------------------- decode from the router step
     # The same steps with the logits computed on the GPU from x and a bf16
     # router weight [E, H] (moe_fp4_forward_routed), and the router kernel
@@ -203,21 +105,6 @@ def main():
     def step_router(i):
         j = i % n_gen
         moe.moe_fp4_router_logits(x_d[j:j + 1], wr_d, out=lg_out)
-
-    def graph_us(fn):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(args.steps):
-                fn(args.warmup + i)
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e6 / args.steps
 
     us_routed = graph_us(step_routed)
     us_router = graph_us(step_router)
@@ -327,6 +214,133 @@ def main():
         del xs0, xst, wss, lgs_s
     del layers
     torch.cuda.empty_cache()
+
+    return routed, shared, verify, stack
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode figure")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router, shared-expert, verify and stack figures (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X and this build has "
+              "no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import mxfp4_routed_expert_router_amd as moe
+    from synth.configs import DECODE as wl, PREFILL as pf
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device: {torch.cuda.get_device_name(dev)}")
+
+    # ---------------------------------------------------------------- set-up
+    t0 = time.time()
+    w = moe.ExpertWeights.from_dict(synth.layer_device(wl, layer=0, device=dev))
+    torch.cuda.synchronize()
+    log(f"weights: {wl.E} experts x {expert_bytes(wl.H, wl.I)} B generated in HBM "
+        f"in {time.time() - t0:.1f} s")
+    n_tok = max(args.steps, 1)
+    n_gen = min(wl.steps, n_tok + args.warmup)
+    xs = np.stack([synth.gen_x(wl, s)[0] for s in range(n_gen)])
+    lgs = np.stack([synth.gen_logits(wl, s)[0] for s in range(n_gen)])
+    x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+    lg_d = torch.from_numpy(lgs).to(dev)
+    y_d = torch.empty((n_gen, wl.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_fp4_workspace_size(1, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8,
+                     device=dev)
+    idx_all = topk_sets(lgs, wl.k)
+
+    def step(i, events=None):
+        j = i % n_gen
+        xi, li, yi = x_d[j:j + 1], lg_d[j:j + 1], y_d[j:j + 1]
+        if events is None:
+            moe.moe_fp4_forward(xi, li, w, wl.k, y=yi, workspace=ws)
+        else:
+            moe.moe_fp4_forward_profiled(xi, li, w, wl.k, events, y=yi, workspace=ws)
+
+    # ---------------------------------------------------------------- decode, timed
+    # The steps are captured once into HIP graphs and replayed: a serving loop
+    # issues a layer call this way, and it keeps the host's per-call launch
+    # overhead (Python + ctypes, tens of microseconds) out of the GPU timeline.
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g_plain = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_plain):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    g_plain.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g_plain.replay()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    # Kernel durations: each kernel's dispatch records a start and an end event
+    # on the layer's stream (moe_fp4_forward_profiled).  The steps are enqueued
+    # behind a spin kernel so that they are all queued before the first one runs
+    # and execute back to back, as in the graph.
+    evs = [moe.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    tp0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[-1]) / args.steps
+    stage = np.array([e.stage_ms() for e in evs])  # [steps, 4]: route, w13, w2, combine
+    k_ms = {"route": float(stage[:, 0].mean()), "w13": float(stage[:, 1].mean()),
+            "w2": float(stage[:, 2].mean())}
+    by = [decode_bytes(wl, idx_all[(args.warmup + i) % n_gen][None]) for i in range(args.steps)]
+    k_bytes = {n: float(np.mean([b[n] for b in by])) for n in ("route", "w13", "w2")}
+    step_bytes = k_bytes["route"] + k_bytes["w13"] + k_bytes["w2"]
+    us_tok = ms_per_step * 1e3 / wl.T
+    dom = max(("w13", "w2"), key=lambda n: k_ms[n])
+    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
+    log(f"decode: {us_tok:.2f} us/token graph replay ({step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s "
+        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us per step with timed dispatches); kernels route "
+        f"{k_ms['route'] * 1e3:.2f} us, w1/w3 {k_ms['w13'] * 1e3:.2f} us, "
+        f"w2+combine {k_ms['w2'] * 1e3:.2f} us")
+    eager_t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
+    log(f"decode eager (one Python call per step): {us_eager:.2f} us/token")
+
+    def graph_us(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(args.warmup + i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / args.steps
+
+    routed = shared = None
+    verify, stack = {}, {}
+    if not args.no_extras:
+        routed, shared, verify, stack = run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d,
+                                                   y_d, ws, n_gen, graph_us)
 
     # ---------------------------------------------------------------- decode, cold caches
     # A read-only flush (summing a 1 GiB buffer) between steps evicts the
