@@ -20,23 +20,34 @@
 namespace moe_fp4 {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kTok = 64;                // tokens per pass
 constexpr int kKB = 256;                // inputs per weight block
 constexpr int kHB = 128;                // inputs per activation half block
-constexpr int kRows13 = 16 * kWaves;    // w1/w3 rows per workgroup (one 16-row tile per wave)
-constexpr int kRows2 = 32 * kWaves;     // w2 rows per workgroup (two 16-row tiles per wave)
 constexpr int kTiles = 2;               // weight tiles per wave (w1 and w3, or two w2 tiles)
 constexpr int kWLoads = 3 * kTiles;     // per weight block: two 1 KB halves and the scales per tile
 constexpr int kXLoads = 2;              // per half block, waves whose tokens are read: two 1 KB quarters
 
+// Two shapes of the same kernels: 8 waves and 64 tokens per pass (one
+// workgroup per CU, 150 KB of LDS) for prefill chunks; 4 waves and 32 tokens
+// (two workgroups per CU, 75 KB) for small batches, where each expert has a
+// few tokens and a second resident workgroup hides the first one's pipeline
+// fill.  Wave w stages tokens 8 w .. 8 w + 7 of a pass in both.
+template <int W, int TOK>
+struct LdsCfg {
+  static constexpr int kWaves = W, kThreads = W * kWave, kTok = TOK, kMaxNT = TOK / 16;
+  static constexpr int kRows13 = 16 * W;  // w1/w3 rows per workgroup (one 16-row tile per wave)
+  static constexpr int kRows2 = 32 * W;   // w2 rows per workgroup (two 16-row tiles per wave)
+  static_assert(TOK == 8 * W, "each wave stages 8 tokens of a pass");
+};
+using CfgBig = LdsCfg<8, 64>;
+using CfgSmall = LdsCfg<4, 32>;
+
+template <class C>
 struct SmemL {
-  uint8_t w[3][kWaves][kTiles][2048];   // 16 rows x 128 bytes (see woff)
-  uint8_t x[3][kTok * kHB * 2];         // 64 tokens x 128 bf16 (see xoff_h)
-  uint32_t ws[3][kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
-  int row[kTok];                        // source row of each staged token
-  float sal[kWaves * 64];               // saliency reduction (saliency.h)
+  uint8_t w[3][C::kWaves][kTiles][2048];   // 16 rows x 128 bytes (see woff)
+  uint8_t x[3][C::kTok * kHB * 2];         // kTok tokens x 128 bf16 (see xoff_h)
+  uint32_t ws[3][C::kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
+  int row[C::kTok];                        // source row of each staged token
+  float sal[C::kWaves * 64];               // saliency reduction (saliency.h, 8 waves only)
 };
 
 // Byte offset in a half-block activation tile of token t's 16-byte chunk c (of
@@ -69,8 +80,8 @@ __device__ __forceinline__ void wait_step(int hb, int NHB, int NB, bool xw) {
 // wrow0[m][rt] points at row 0 of the wave's 16-row tile (inside the weights
 // even for a tile past the end, whose results are not stored), srow0 at that
 // row's scales.  Tokens past nc read token 0's row.
-template <int M, int kRT, int NT>
-__device__ __forceinline__ void gemm_pass_lds(SmemL& sm, const uint8_t* const (&wrow0)[M][kRT],
+template <class C, int M, int kRT, int NT>
+__device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
                                               const uint8_t* const (&srow0)[M][kRT], size_t wrow,
                                               size_t srow, const uint16_t* __restrict__ src, int nc,
                                               int K, f32x4 (&acc)[M][kRT][NT]) {
@@ -169,7 +180,9 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL& sm, const uint8_t* const (&
   __syncthreads();  // the LDS is free for the caller (and its row table may change)
 }
 
-__global__ void __launch_bounds__(kThreads, 1) gemm13_lds_kernel(LayerArgs a) {
+template <class C>
+__global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
+  constexpr int kRows13 = C::kRows13, kTok = C::kTok;
   const int tpe = (a.I + kRows13 - 1) / kRows13;
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
@@ -177,7 +190,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_lds_kernel(LayerArgs a) {
   const int ne = a.counts[e];
   if (ne == 0) return;
   const int off = a.offsets[e];
-  __shared__ SmemL sm;
+  __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c16 = lane & 15, kb = lane >> 4;
@@ -196,7 +209,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_lds_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[2][1][NT];
-      gemm_pass_lds<2, 1, NT>(sm, wr, sr, wrow, srow, a.x, nc, a.H, acc);
+      gemm_pass_lds<C, 2, 1, NT>(sm, wr, sr, wrow, srow, a.x, nc, a.H, acc);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = 16 * nt + c16;
@@ -210,16 +223,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_lds_kernel(LayerArgs a) {
         }
       }
     };
-    switch ((nc + 15) / 16) {
-      case 1: pass(IntC<1>{}); break;
-      case 2: pass(IntC<2>{}); break;
-      case 3: pass(IntC<3>{}); break;
-      default: pass(IntC<4>{}); break;
+    if constexpr (C::kMaxNT == 4) {
+      switch ((nc + 15) / 16) {
+        case 1: pass(IntC<1>{}); break;
+        case 2: pass(IntC<2>{}); break;
+        case 3: pass(IntC<3>{}); break;
+        default: pass(IntC<4>{}); break;
+      }
+    } else {
+      if (nc <= 16) pass(IntC<1>{}); else pass(IntC<2>{});
     }
   }
 }
 
-__global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
+template <class C>
+__global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
+  constexpr int kRows2 = C::kRows2, kTok = C::kTok;
   const int tpe = (a.H + kRows2 - 1) / kRows2;
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
@@ -227,7 +246,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
   const int ne = a.counts[e];
   if (ne == 0) return;
   const int off = a.offsets[e];
-  __shared__ SmemL sm;
+  __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c16 = lane & 15, kb = lane >> 4;
@@ -251,7 +270,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[1][2][NT];
-      gemm_pass_lds<1, 2, NT>(sm, wr, sr, wrow, srow, a.h, nc, a.I, acc);
+      gemm_pass_lds<C, 1, 2, NT>(sm, wr, sr, wrow, srow, a.h, nc, a.I, acc);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -265,18 +284,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_lds_kernel(LayerArgs a) {
             *reinterpret_cast<float4*>(a.ypair + (size_t)s * a.H + rw + 16 * rt + 4 * kb) = o;
           }
         }
-      if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
+      if constexpr (C::kWaves == 8)
+        if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
     };
-    switch ((nc + 15) / 16) {
-      case 1: pass(IntC<1>{}); break;
-      case 2: pass(IntC<2>{}); break;
-      case 3: pass(IntC<3>{}); break;
-      default: pass(IntC<4>{}); break;
+    if constexpr (C::kMaxNT == 4) {
+      switch ((nc + 15) / 16) {
+        case 1: pass(IntC<1>{}); break;
+        case 2: pass(IntC<2>{}); break;
+        case 3: pass(IntC<3>{}); break;
+        default: pass(IntC<4>{}); break;
+      }
+    } else {
+      if (nc <= 16) pass(IntC<1>{}); else pass(IntC<2>{});
     }
   }
 }
 
-static_assert(kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
+static_assert(CfgBig::kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
 
 }  // namespace
 
@@ -287,15 +311,36 @@ bool prefill_lds_takes(int K, const uint8_t* const* scales, const int64_t* strid
   return true;
 }
 
+namespace {
+// Small batches (at most 32 tokens, so at most 32 per expert: one pass) take
+// the 4-wave shape; saliency needs the 8-wave one's 256-row w2 tiles.
+bool small_batch(const LayerArgs& a) { return a.T <= CfgSmall::kTok && !a.sal_part; }
+
+template <class C>
+void launch13(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int t13 = a.E * ((a.I + C::kRows13 - 1) / C::kRows13);
+  launch_k(gemm13_lds_kernel<C>, dim3(xcd_grid(t13)), dim3(C::kThreads), 0, stream, start, stop, a);
+}
+template <class C>
+void launch2(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const int t2 = a.E * ((a.H + C::kRows2 - 1) / C::kRows2);
+  launch_k(gemm2_lds_kernel<C>, dim3(xcd_grid(t2)), dim3(C::kThreads), 0, stream, start, stop, a);
+}
+}  // namespace
+
 hipError_t launch_gemm13_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13);
-  launch_k(gemm13_lds_kernel, dim3(xcd_grid(t13)), dim3(kThreads), 0, stream, start, stop, a);
+  if (small_batch(a))
+    launch13<CfgSmall>(a, stream, start, stop);
+  else
+    launch13<CfgBig>(a, stream, start, stop);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const int t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
-  launch_k(gemm2_lds_kernel, dim3(xcd_grid(t2)), dim3(kThreads), 0, stream, start, stop, a);
+  if (small_batch(a))
+    launch2<CfgSmall>(a, stream, start, stop);
+  else
+    launch2<CfgBig>(a, stream, start, stop);
   return hipGetLastError();
 }
 
