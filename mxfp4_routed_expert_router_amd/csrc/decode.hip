@@ -284,57 +284,52 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Routing of the token in LDS: the k chosen experts by ascending id (slot d),
-// with their gates.
-struct OneTables {
-  int de[kMaxK];
-  float gate[kMaxK];
-};
-
-// Rank the logits in wave 0 (every workgroup does, redundantly).  Each chosen
-// expert holds exactly one pair, so the expert of rank j sits in sorted slot
-// (number of chosen ids below it).  Workgroup 0 publishes the routing result.
-__device__ void route_one(const LayerArgs& a, OneTables& tb) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int k = a.k, E = a.E;
-  if (tid < kWave) {
-    int my_e;
-    float my_g;
-    wave_topk_regs<kFusedVPL>(a.logits, E, k, lane, my_e, my_g);
-    const int key = lane < k ? my_e : 0x7FFFFFFF;
-    int rank = 0;
-    for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(key, i) < key ? 1 : 0;
-    if (lane < k) {
-      tb.de[rank] = my_e;
-      tb.gate[rank] = my_g;
-      if (blockIdx.x == 0) {
-        const RouteArgs& r = a.route;
-        r.idx[lane] = my_e;
-        r.gates[lane] = my_g;
-        r.sorted_pairs[rank] = lane;
-        r.pair_slot[lane] = rank;
-        r.slot_gate[rank] = my_g;
-        r.slot_tok[rank] = 0;
-        r.dinfo[4 * rank + 0] = my_e;
-        r.dinfo[4 * rank + 1] = rank;
-        r.dinfo[4 * rank + 2] = 1;
-        r.dinfo[4 * rank + 3] = 0;
-      }
-    }
-  }
-  lds_barrier();
-  if (blockIdx.x == 0) {
+// The k chosen experts of the token by ascending id (slot d), as wave w sees
+// them in its own row of the table.  With the routing fused, every wave ranks
+// the logits itself (the same computation, so the same result in every wave):
+// it can then issue its first unit's loads without waiting for any other wave.
+// Each chosen expert holds exactly one pair, so the expert of rank j sits in
+// sorted slot (number of chosen ids below it).  Wave 0 of workgroup 0
+// publishes the routing result.
+__device__ __forceinline__ void route_one_wave(const LayerArgs& a, const float (&lv)[kFusedVPL],
+                                               int (&de)[kMaxK]) {
+  const int lane = threadIdx.x & (kWave - 1), k = a.k;
+  int my_e;
+  float my_g;
+  wave_topk_vals<kFusedVPL>(lv, a.E, k, lane, my_e, my_g);
+  const int key = lane < k ? my_e : 0x7FFFFFFF;
+  int rank = 0;
+  for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(key, i) < key ? 1 : 0;
+  if (lane < k) de[rank] = my_e;
+  if (blockIdx.x == 0 && threadIdx.x < kWave && lane < k) {
     const RouteArgs& r = a.route;
-    for (int x = tid; x < E; x += kThreads) {
-      int below = 0;
-      while (below < k && tb.de[below] < x) ++below;
-      r.counts[x] = (below < k && tb.de[below] == x) ? 1 : 0;
-      r.offsets[x] = below;
-    }
-    if (tid == 0) {
-      r.offsets[E] = k;
-      r.meta[0] = k;
-    }
+    r.idx[lane] = my_e;
+    r.gates[lane] = my_g;
+    r.sorted_pairs[rank] = lane;
+    r.pair_slot[lane] = rank;
+    r.slot_gate[rank] = my_g;
+    r.slot_tok[rank] = 0;
+    r.dinfo[4 * rank + 0] = my_e;
+    r.dinfo[4 * rank + 1] = rank;
+    r.dinfo[4 * rank + 2] = 1;
+    r.dinfo[4 * rank + 3] = 0;
+  }
+}
+
+// Workgroup 0's counts and offsets of the fused routing (after a barrier that
+// makes wave 0's table visible).
+__device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&de)[kMaxK]) {
+  const RouteArgs& r = a.route;
+  const int k = a.k, E = a.E;
+  for (int x = threadIdx.x; x < E; x += kThreads) {
+    int below = 0;
+    while (below < k && de[below] < x) ++below;
+    r.counts[x] = (below < k && de[below] == x) ? 1 : 0;
+    r.offsets[x] = below;
+  }
+  if (threadIdx.x == 0) {
+    r.offsets[E] = k;
+    r.meta[0] = k;
   }
 }
 
@@ -345,7 +340,7 @@ __device__ void route_one(const LayerArgs& a, OneTables& tb) {
 // (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
 template <int NXG>
 __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
-  __shared__ OneTables tb;
+  __shared__ int de_w[kWaves][kMaxK];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = H / 32;
@@ -353,28 +348,27 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   // The token's x in LDS as 16-byte chunks (group g, dword q at 4 g + q),
   // followed by one zero group.  A lane's groups past the row end load a
   // duplicate weight chunk (clamped to the last group) and read the zero
-  // group of x, so they add exactly nothing.
+  // group of x, so they add exactly nothing.  The logits and a bf16 x are
+  // loaded together at entry; x is stored to LDS after the routing and the
+  // first unit's loads are issued.
   __shared__ u32x4 xl[kOneMaxXG * kWave * 4 + 4];
-  if (a.xf) {
-    // the layer's input is the pre-norm of the fp32 row xf (same bits as
-    // moe_fp4_prenorm_bf16: row_rms, then one division and rounding per value)
-    __shared__ float wsum[4];
-    const float r = row_rms(a.xf, H, a.eps, wsum);
-    for (int c = tid; c < CPR * 4; c += kThreads) {
-      const float4 v0 = *reinterpret_cast<const float4*>(a.xf + 8 * c);
-      const float4 v1 = *reinterpret_cast<const float4*>(a.xf + 8 * c + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] / r) |
-               ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] / r) << 16);
-      xl[c] = o;
-    }
-  } else {
-    for (int c = tid; c < CPR * 4; c += kThreads) xl[c] = ld16(a.x + 8 * c);
+  static_assert(kOneMaxXG * kWave * 4 <= 2 * kThreads, "x chunks per thread");
+  float lv[kFusedVPL];
+  if (a.fused_route) wave_load_logits<kFusedVPL>(a.logits, a.E, lane, lv);
+  const int nc = CPR * 4, c0 = tid, c1 = tid + kThreads;
+  u32x4 xv0 = zero4(), xv1 = zero4();
+  if (!a.xf) {
+    xv0 = ld16(a.x + 8 * (c0 < nc ? c0 : 0));
+    xv1 = ld16(a.x + 8 * (c1 < nc ? c1 : 0));
   }
-  if (tid < 4) xl[4 * CPR + tid] = zero4();
+  if (a.fused_route) {
+    route_one_wave(a, lv, de_w[w]);
+  } else if (lane < a.k) {
+    de_w[w][lane] = a.dinfo[4 * lane];
+  }
+  // de_w[w] is written and read by wave w only: LDS operations of one wave
+  // complete in order, so no barrier is needed before the first issue
+
   int gc[NXG], xo[NXG];
 #pragma unroll
   for (int i = 0; i < NXG; ++i) {
@@ -382,20 +376,9 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     gc[i] = g < CPR ? g : CPR - 1;
     xo[i] = g < CPR ? 4 * g : 4 * CPR;
   }
-  if (a.fused_route) {
-    route_one(a, tb);
-  } else {
-    if (tid < a.k) {
-      tb.de[tid] = a.dinfo[4 * tid];
-      tb.gate[tid] = a.slot_gate[tid];
-    }
-    lds_barrier();
-  }
-
   const int nunits = a.k * I;
   const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
   const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;  // units of this wave
-  if (F == 0) return;
   const int wbytes = I * (H / 2), sbytes = I * CPR;
 
   struct Unit {
@@ -404,7 +387,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   };
   auto issue = [&](int f, Unit& B) {
     const int u = wid + f * nw, d = u / I, r = u - d * I;
-    const int e = uniform(tb.de[d]);
+    const int e = uniform(de_w[w][d]);
     const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
     const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
     const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
@@ -436,12 +419,38 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     if (lane == 0) a.h[(size_t)d * I + r] = swiglu_bf16(G, U);
   };
 
+  Unit A, B;
+  if (F > 0) issue(0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  if (a.xf) {
+    // the layer's input is the pre-norm of the fp32 row xf (same bits as
+    // moe_fp4_prenorm_bf16: row_rms, then one division and rounding per value)
+    __shared__ float wsum[4];
+    const float r = row_rms(a.xf, H, a.eps, wsum);
+    for (int c = tid; c < nc; c += kThreads) {
+      const float4 v0 = *reinterpret_cast<const float4*>(a.xf + 8 * c);
+      const float4 v1 = *reinterpret_cast<const float4*>(a.xf + 8 * c + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] / r) |
+               ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] / r) << 16);
+      xl[c] = o;
+    }
+  } else {
+    if (c0 < nc) xl[c0] = xv0;
+    if (c1 < nc) xl[c1] = xv1;
+  }
+  if (tid < 4) xl[nc + tid] = zero4();
+  lds_barrier();
+  if (a.fused_route && blockIdx.x == 0) publish_counts(a, de_w[0]);
+  if (F == 0) return;
+
   // Two register buffers; the loop body has no conditional loads, so each wait
   // is for the older buffer only and the next unit stays in flight.  The
   // scheduling barriers keep the compiler from sinking a unit's loads below
   // the computation they are meant to overlap.
-  Unit A, B;
-  issue(0, A);
   int f = 0;
   for (; f + 2 < F; f += 2) {
     issue(f + 1, B);

@@ -159,7 +159,7 @@ __device__ __forceinline__ float row_rms(const float* __restrict__ xr, int H, fl
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
     if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   }
-  __syncthreads();
+  lds_barrier();  // wsum is the only data shared; loads in flight stay in flight
   const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   return sqrtf(tot / (float)H + eps);
 }

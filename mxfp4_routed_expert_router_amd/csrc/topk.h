@@ -12,10 +12,12 @@ namespace moe_fp4 {
 // the key of +0; NaN maps to 1, below the key of -inf (0x007FFFFF).  Key 0
 // marks a slot that is empty or already chosen.
 __device__ __forceinline__ uint32_t order_key(float v) {
+  // selects only: a branch here would let the compiler sink the logit loads
+  // into it, each then waited for before the next is issued
   uint32_t u = __float_as_uint(v);
-  if (v != v) return 1u;
-  if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = (u << 1) == 0u ? 0u : u;
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return v != v ? 1u : key;
 }
 
 __device__ __forceinline__ float key_value(uint32_t key) {
@@ -23,24 +25,30 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __uint_as_float(u);
 }
 
-// One wave ranks the E logits of one token; lane j < k receives the expert of
-// rank j and its gate.  Lane l holds experts l, l+64, ...  Each round takes the
-// wave-wide maximum key (DPP), and among lanes holding it the lowest expert id,
-// then clears that entry.  Requires k <= E and all 64 lanes active.
+// Lane l's logits l, l+64, ... of one token row.  The loads are unconditional
+// (a clamped index, the value discarded past E): inside a branch each one would
+// be waited for before the next is issued.
 template <int VPL>
-__device__ __forceinline__ void wave_topk_regs(const float* __restrict__ lrow, int E, int k,
-                                               int lane, int& e_out, float& g_out) {
-  // The loads are unconditional (a clamped index, the value discarded past E):
-  // inside a branch each one would be waited for before the next is issued.
-  float vals[VPL];
+__device__ __forceinline__ void wave_load_logits(const float* __restrict__ lrow, int E, int lane,
+                                                 float (&vals)[VPL]) {
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
     vals[i] = lrow[e < E ? e : E - 1];
   }
+}
+
+// One wave ranks the E logits of one token (vals as wave_load_logits leaves
+// them); lane j < k receives the expert of rank j and its gate.  Each round
+// takes the wave-wide maximum key (DPP), and among lanes holding it the lowest
+// expert id, then clears that entry.  Requires k <= E and all 64 lanes active.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_vals(const float (&vals)[VPL], int E, int k, int lane,
+                                               int& e_out, float& g_out) {
   uint32_t keys[VPL];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) keys[i] = (lane + kWave * i < E) ? order_key(vals[i]) : 0u;
+  for (int i = 0; i < VPL; ++i)  // a mask, not a select: see wave_load_logits
+    keys[i] = order_key(vals[i]) & (0u - (uint32_t)(lane + kWave * i < E));
   int my_e = 0;
   float my_v = 0.f, v0 = 0.f, s = 0.f;
   for (int j = 0; j < k; ++j) {
@@ -70,6 +78,15 @@ __device__ __forceinline__ void wave_topk_regs(const float* __restrict__ lrow, i
   }
   e_out = my_e;
   g_out = expf(my_v - v0) / s;
+}
+
+// As wave_topk_vals, loading the logits itself.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_regs(const float* __restrict__ lrow, int E, int k,
+                                               int lane, int& e_out, float& g_out) {
+  float vals[VPL];
+  wave_load_logits<VPL>(lrow, E, lane, vals);
+  wave_topk_vals<VPL>(vals, E, k, lane, e_out, g_out);
 }
 
 // As wave_topk_regs, writing the k experts and gates to idx_out / g_out.
