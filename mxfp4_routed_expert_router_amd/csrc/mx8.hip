@@ -122,14 +122,20 @@ constexpr int kRows13 = 16 * kWaves;     // w1/w3 rows per workgroup
 constexpr int kRows2 = 32 * kWaves;      // w2 rows per workgroup (two 16-row tiles per wave)
 constexpr int kStages = 3;               // K blocks resident in LDS (kStages - 1 in flight)
 constexpr int kTiles = 2;                // weight tiles per wave and block (M x row tiles)
-constexpr int kWLoads = 3 * kTiles;      // per tile: two 1 KB halves and the scales
-constexpr int kXLoads = 3;               // per wave holding tokens: two 1 KB quarters and scales
+// Loads a wave issues for one block.  The scale bytes of two blocks come in
+// one load, issued with the even block: a scale load gathers 8 bytes from
+// each of 16 rows (16 cache lines), so fetching them a block at a time made
+// the scales cost as much request traffic as the weights themselves.
+constexpr int kWLoads = 3 * kTiles;      // even block, per tile: two 1 KB halves and the scales
+constexpr int kXLoads = 3;               // even block, per wave holding tokens: two 1 KB quarters and scales
+constexpr int kWLoadsOdd = 2 * kTiles;   // odd block: the halves only
+constexpr int kXLoadsOdd = 2;
 
 struct SmemMx {
   uint8_t w[kStages][kWaves][kTiles][2048];   // 16 rows x 128 bytes, swizzled: see woff
   uint8_t x[kStages][kTok * kKB];             // E4M3 codes of 64 tokens, swizzled: see xoff
-  uint32_t ws[kStages][kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
-  uint32_t xs[kStages][kWaves][16];           // token 8 w + i: scale dword d at 8 d + i
+  uint32_t ws[2][kWaves][kTiles][64];   // blocks 2p, 2p+1 in slot p % 2: dword d of row r at 16 d + r
+  uint32_t xs[2][kWaves][32];           // token 8 w + i: scale dword d (blocks 2p, 2p+1) at 8 d + i
   int row[kTok];                              // source row of each staged token
   float sal[kWaves * 64];                     // saliency reduction (saliency.h)
 };
@@ -167,8 +173,7 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
 
   // weight lanes: half h covers rows 8 h + lane / 8 (see woff)
   const int wr_r = lane >> 3, wr_c0 = wtile_chunk(lane, 0), wr_c1 = wtile_chunk(lane, 1);
-  // scale lanes (lane < 32): tile row lane % 16, dword lane / 16
-  const int sc_r = c16, sc_d = kb & 1;
+  // scale lanes: tile row lane % 16, dword lane / 16 of a block pair
   // activation lanes: quarter h covers tokens 8 w + 4 h + lane / 16, LDS slot
   // lane % 16 holding chunk (lane % 16) ^ (t & 15)
   const bool xw = 8 * w < 16 * NT;         // this wave stages tokens that are read
@@ -179,13 +184,26 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
     xsrc[h] = q + (size_t)sm.row[t < nc ? t : 0] * Kp + ((c16 ^ (t & 15)) << 4);
   }
   const int st = 8 * w + (lane & 7);
-  const uint8_t* const ssrc = qs + (size_t)sm.row[st < nc ? st : 0] * KSp + 4 * ((lane >> 3) & 1);
+  const uint8_t* const ssrc = qs + (size_t)sm.row[st < nc ? st : 0] * KSp;
+
+  // Byte offset, from the row's scales, of scale dword dd (0..3) of the block
+  // pair starting at b: dwords 0, 1 belong to block b and 2, 3 to block b + 1.
+  // Past the last block the lane re-reads block b; in a half block only dword
+  // 0 exists, and dword 1 re-reads it (the inputs it scales are zeros).
+  auto pair_off = [&](int b, int dd) {
+    int blk = b + (dd >> 1), sub = dd & 1;
+    if (blk >= NB) blk = b;
+    if (half_tail && blk == NB - 1) sub = 0;
+    return blk * 8 + 4 * sub;
+  };
+  const int wdd = lane >> 4, xdd = (lane >> 3) & 3;
 
   auto issue = [&](int b, int s) {
     const bool tail = half_tail && b == NB - 1;
-    // in a half block, chunks 4..7 (and scale dword 1) re-read chunks 0..3 (dword 0)
+    const bool even = (b & 1) == 0;
+    // in a half block, chunks 4..7 re-read chunks 0..3
     const int c0 = tail ? wr_c0 & 3 : wr_c0, c1 = tail ? wr_c1 & 3 : wr_c1;
-    const int d = tail ? 0 : sc_d;
+    const int ps = (b >> 1) & 1;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -194,16 +212,17 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
         const uint8_t* const src = wrow0[m][rt] + (size_t)b * 128;
         lds_load16(lds_addr(dst), src + wr_r * wrow + 16 * c0);
         lds_load16(lds_addr(dst + 1024), src + (8 + wr_r) * wrow + 16 * c1);
-        if (lane < 32) lds_load4(lds_addr(&sm.ws[s][w][m * kRT + rt][0]),
-                                 srow0[m][rt] + sc_r * srow + (size_t)b * 8 + 4 * d);
+        if (even) lds_load4(lds_addr(&sm.ws[ps][w][m * kRT + rt][0]),
+                            srow0[m][rt] + c16 * srow + pair_off(b, wdd));
       }
     if (xw) {
       lds_load16(lds_addr(&sm.x[s][(8 * w) * kKB]), xsrc[0] + (size_t)b * kKB);
       lds_load16(lds_addr(&sm.x[s][(8 * w + 4) * kKB]), xsrc[1] + (size_t)b * kKB);
-      if (lane < 16) lds_load4(lds_addr(&sm.xs[s][w][0]), ssrc + (size_t)b * 8);
+      if (even && lane < 32) lds_load4(lds_addr(&sm.xs[ps][w][0]), ssrc + pair_off(b, xdd));
     }
   };
-  auto compute = [&](int s) {
+  auto compute = [&](int b) {
+    const int s = b % kStages, ps = (b >> 1) & 1, d0 = 2 * (b & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       u32x4 A[M][kRT];
@@ -213,7 +232,7 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
           A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * j + kb)]);
-          sa[m][rt] = (int)((sm.ws[s][w][m * kRT + rt][16 * j + c16] >> (8 * kb)) & 0xFFu);
+          sa[m][rt] = (int)((sm.ws[ps][w][m * kRT + rt][16 * (d0 + j) + c16] >> (8 * kb)) & 0xFFu);
         }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -222,7 +241,7 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
         const u32x4 hi = ld16(&sm.x[s][xoff(t, 8 * j + 4 + kb)]);
         const i32x8 B = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        const int sb = (int)((sm.xs[s][t / 8][8 * j + (t & 7)] >> (8 * kb)) & 0xFFu);
+        const int sb = (int)((sm.xs[ps][t / 8][8 * (d0 + j) + (t & 7)] >> (8 * kb)) & 0xFFu);
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -239,16 +258,18 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
   for (int b = 0; b < kStages - 1 && b < NB; ++b) issue(b, b);
   for (int b = 0; b < NB; ++b) {
     // block b's loads (this wave's) are done once at most the loads of the
-    // block issued after it are in flight; the barrier extends that to every
-    // wave's, and means every wave is done computing block b - 1
+    // block issued after it are in flight (fewer for an odd block, which has
+    // no scale loads); the barrier extends that to every wave's, and means
+    // every wave is done computing block b - 1 (so also with the scale pair
+    // slot that block b + 2 may load)
     if (b + 1 == NB)
       wait_then_barrier<0>();
-    else if (xw)
-      wait_then_barrier<kWLoads + kXLoads>();
+    else if ((b + 1) & 1)
+      xw ? wait_then_barrier<kWLoadsOdd + kXLoadsOdd>() : wait_then_barrier<kWLoadsOdd>();
     else
-      wait_then_barrier<kWLoads>();
+      xw ? wait_then_barrier<kWLoads + kXLoads>() : wait_then_barrier<kWLoads>();
     if (b + kStages - 1 < NB) issue(b + kStages - 1, (b + kStages - 1) % kStages);  // into b-1's slot
-    compute(b % kStages);
+    compute(b);
   }
   __syncthreads();  // the LDS is free for the caller (and its row table may change)
 }
