@@ -23,7 +23,12 @@ namespace {
 constexpr int kKB = 256;                // inputs per weight block
 constexpr int kHB = 128;                // inputs per activation half block
 constexpr int kTiles = 2;               // weight tiles per wave (w1 and w3, or two w2 tiles)
-constexpr int kWLoads = 3 * kTiles;     // per weight block: two 1 KB halves and the scales per tile
+// Loads a wave issues per weight block.  The scale bytes of two blocks come in
+// one load, issued with the even block (one scale load gathers 8 bytes from
+// each of 16 rows, so a load per block costs as much request traffic as the
+// weight halves).
+constexpr int kWLoads = 3 * kTiles;     // even weight block: two 1 KB halves and the scales per tile
+constexpr int kWLoadsOdd = 2 * kTiles;  // odd weight block: the halves only
 constexpr int kXLoads = 2;              // per half block, waves whose tokens are read: two 1 KB quarters
 
 // Two shapes of the same kernels: 8 waves and 64 tokens per pass (one
@@ -45,7 +50,7 @@ template <class C>
 struct SmemL {
   uint8_t w[3][C::kWaves][kTiles][2048];   // 16 rows x 128 bytes (see woff)
   uint8_t x[3][C::kTok * kHB * 2];         // kTok tokens x 128 bf16 (see xoff_h)
-  uint32_t ws[3][C::kWaves][kTiles][32];   // scale dword d of tile row r at 16 d + r
+  uint32_t ws[2][C::kWaves][kTiles][64];   // blocks 2p, 2p+1 in slot p % 2: dword d of row r at 16 d + r
   int row[C::kTok];                        // source row of each staged token
   float sal[C::kWaves * 64];               // saliency reduction (saliency.h, 8 waves only)
 };
@@ -63,12 +68,13 @@ __device__ __forceinline__ void wait_n() { wait_then_barrier<N>(); }
 // after them: one weight block and one half block (see the issue order in
 // gemm_pass_lds).  xw: whether this wave loads activations.
 __device__ __forceinline__ void wait_step(int hb, int NHB, int NB, bool xw) {
-  const bool w_after = (hb + 1) / 2 + 1 < NB;
+  const int wb = (hb + 1) / 2 + 1;  // the weight block issued after step hb's operands
+  const bool w_after = wb < NB, w_even = (wb & 1) == 0;
   const bool x_after = xw && hb + 1 < NHB;
   if (w_after && x_after)
-    wait_n<kWLoads + kXLoads>();
+    w_even ? wait_n<kWLoads + kXLoads>() : wait_n<kWLoadsOdd + kXLoads>();
   else if (w_after)
-    wait_n<kWLoads>();
+    w_even ? wait_n<kWLoads>() : wait_n<kWLoadsOdd>();
   else if (x_after)
     wait_n<kXLoads>();
   else
@@ -108,8 +114,13 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
               ((c16 ^ (t & 15)) << 4);
   }
 
+  // scale lanes: tile row lane % 16, dword lane / 16 of a block pair's 16
+  // bytes (dwords 2, 3 belong to the odd block; past the last block a lane
+  // re-reads the even block's)
   auto issue_w = [&](int b) {
     const int s = b % 3;
+    const bool even = (b & 1) == 0;
+    const int so = b * 8 + 4 * (b + 1 < NB ? kb : kb & 1);
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -118,9 +129,8 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
         const uint8_t* const g = wrow0[m][rt] + (size_t)b * 128;
         lds_load16(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
         lds_load16(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
-        if (lane < 32)  // tile row lane % 16, scale dword lane / 16 of the block's 8 bytes
-          lds_load4(lds_addr(&sm.ws[s][w][m * kRT + rt][0]),
-                    srow0[m][rt] + c16 * srow + (size_t)b * 8 + 4 * (kb & 1));
+        if (even)
+          lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
       }
   };
   auto issue_x = [&](int hb) {
@@ -130,7 +140,7 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
     lds_load16(lds_addr(dst + (8 * w + 4) * 256), xsrc[1] + (size_t)hb * (kHB * 2));
   };
   auto compute = [&](int hb) {
-    const int s = (hb >> 1) % 3, hh = hb & 1;
+    const int b = hb >> 1, s = b % 3, hh = hb & 1, ps = (b >> 1) & 1, d = 2 * (b & 1) + hh;
     const uint8_t* const xt = &sm.x[hb % 3][0];
     u32x4 A4[M][kRT];
     float sc[M][kRT];
@@ -139,7 +149,7 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         A4[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * hh + kb)]);
-        sc[m][rt] = ue8m0_to_f32((sm.ws[s][w][m * kRT + rt][16 * hh + c16] >> (8 * kb)) & 0xFFu);
+        sc[m][rt] = ue8m0_to_f32((sm.ws[ps][w][m * kRT + rt][16 * d + c16] >> (8 * kb)) & 0xFFu);
       }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -172,7 +182,8 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
   for (int hb = 0; hb < NHB; ++hb) {
     wait_step(hb, NHB, NB, xw);
     // every wave is past step hb - 1: its slots (x (hb - 1) % 3, and for hb
-    // even the weight slot of block hb/2 - 1) may be loaded again
+    // even the weight slot of block hb/2 - 1, and the scale pair slot of
+    // blocks hb/2 - 2 and hb/2 - 1) may be loaded again
     if (hb + 2 < NHB) issue_x(hb + 2);
     if (!(hb & 1) && hb / 2 + 2 < NB) issue_w(hb / 2 + 2);
     compute(hb);
