@@ -257,8 +257,11 @@ int moe_fp4_forward_residual(const moe_fp4_dims *dims, float *x, const float *lo
 
 /* Pre-normalisation for a residual stack of layers:
  *   u[t][m] = bf16_rne(x[t][m] / sqrt(mean_m x[t][m]^2 + eps))
- *   x [T][H] fp32, u [T][H] bf16 bits.
- * Errors: EINVAL, EUNSUPPORTED (H not a multiple of 32 or above 16384), EHIP. */
+ *   x [T][H] fp32, u [T][H] bf16 bits, both 16-byte aligned.
+ * The sum of squares runs in one fixed order (reproducible bit for bit), the
+ * order the fused pre-norm of moe_fp4_forward_residual uses.
+ * Errors: EINVAL, EUNSUPPORTED (H not a multiple of 32 or above 16384), EALIGN,
+ * EHIP. */
 int moe_fp4_prenorm_bf16(const float *x, uint16_t *u, int32_t T, int32_t H, float eps,
                          hipStream_t stream);
 

@@ -382,6 +382,7 @@ int moe_fp4_prenorm_bf16(const float* x, uint16_t* u, int32_t T, int32_t H, floa
                          hipStream_t stream) {
   if (!x || !u || T < 1 || H < 1) return MOE_FP4_EINVAL;
   if (H % 32 || H > 16384) return MOE_FP4_EUNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(u, 16)) return MOE_FP4_EALIGN;
   return launch_prenorm(x, u, T, H, eps, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
 }
 

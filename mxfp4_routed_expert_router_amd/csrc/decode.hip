@@ -356,10 +356,18 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   float lv[kFusedVPL];
   if (a.fused_route) wave_load_logits<kFusedVPL>(a.logits, a.E, lane, lv);
   const int nc = CPR * 4, c0 = tid, c1 = tid + kThreads;
+  const int cc0 = c0 < nc ? c0 : 0, cc1 = c1 < nc ? c1 : 0;
   u32x4 xv0 = zero4(), xv1 = zero4();
-  if (!a.xf) {
-    xv0 = ld16(a.x + 8 * (c0 < nc ? c0 : 0));
-    xv1 = ld16(a.x + 8 * (c1 < nc ? c1 : 0));
+  float4 xf[4];  // a fp32 input row: chunks c0 and c1 (the pre-norm's ownership)
+  static_assert(kThreads == kNormThreads, "pre-norm chunk ownership");
+  if (a.xf) {
+    xf[0] = *reinterpret_cast<const float4*>(a.xf + 8 * cc0);
+    xf[1] = *reinterpret_cast<const float4*>(a.xf + 8 * cc0 + 4);
+    xf[2] = *reinterpret_cast<const float4*>(a.xf + 8 * cc1);
+    xf[3] = *reinterpret_cast<const float4*>(a.xf + 8 * cc1 + 4);
+  } else {
+    xv0 = ld16(a.x + 8 * cc0);
+    xv1 = ld16(a.x + 8 * cc1);
   }
   if (a.fused_route) {
     route_one_wave(a, lv, de_w[w]);
@@ -423,25 +431,18 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   if (F > 0) issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
   if (a.xf) {
-    // the layer's input is the pre-norm of the fp32 row xf (same bits as
-    // moe_fp4_prenorm_bf16: row_rms, then one division and rounding per value)
-    __shared__ float wsum[4];
-    const float r = row_rms(a.xf, H, a.eps, wsum);
-    for (int c = tid; c < nc; c += kThreads) {
-      const float4 v0 = *reinterpret_cast<const float4*>(a.xf + 8 * c);
-      const float4 v1 = *reinterpret_cast<const float4*>(a.xf + 8 * c + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      u32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] / r) |
-               ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] / r) << 16);
-      xl[c] = o;
-    }
-  } else {
-    if (c0 < nc) xl[c0] = xv0;
-    if (c1 < nc) xl[c1] = xv1;
+    // the layer's input is the pre-norm of the fp32 row xf, computed as
+    // moe_fp4_prenorm_bf16 computes it (same ownership and order: same bits)
+    __shared__ float wsum[kNormThreads / 64];
+    float ss = 0.f;
+    if (c0 < nc) ss = chunk_sumsq(xf[0], xf[1], ss);
+    if (c1 < nc) ss = chunk_sumsq(xf[2], xf[3], ss);
+    const float r = block_rms(ss, H, a.eps, wsum);
+    xv0 = chunk_to_bf16(xf[0], xf[1], r);
+    xv1 = chunk_to_bf16(xf[2], xf[3], r);
   }
+  if (c0 < nc) xl[c0] = xv0;
+  if (c1 < nc) xl[c1] = xv1;
   if (tid < 4) xl[nc + tid] = zero4();
   lds_barrier();
   if (a.fused_route && blockIdx.x == 0) publish_counts(a, de_w[0]);

@@ -142,26 +142,48 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return umin32(umin32(r0, r1), umin32(r2, r3));
 }
 
-// RMS of one row for the pre-normalisation u = bf16(x / rms), rms =
-// sqrt(mean(x^2) + eps): threads 0..255 of the workgroup sum the squares of
-// elements tid, tid + 256, ... in that order, each wave reduces with XOR
-// shuffles, and the four wave sums are added as ((w0 + w1) + w2) + w3.  Every
-// thread of the workgroup must call it (it has a barrier); all get the value.
-// wsum: 4 floats of LDS.  The standalone pre-norm and the fused one use it, so
-// both give the same bits.
-__device__ __forceinline__ float row_rms(const float* __restrict__ xr, int H, float eps,
-                                         float* wsum) {
-  const int tid = threadIdx.x;
-  if (tid < 256) {
-    float ss = 0.f;
-    for (int m = tid; m < H; m += 256) ss += xr[m] * xr[m];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
-  }
+// Pre-normalisation u = bf16(x / rms) of one fp32 row, rms = sqrt(mean(x^2) +
+// eps), by a 512-thread workgroup.  Thread t owns the 8-value chunks t,
+// t + 512, t + 1024, ... (chunk c holds elements 8 c .. 8 c + 7) and keeps
+// them in registers, so the row is read once.  The sum of squares runs over
+// the thread's chunks in that order and each chunk's values in order; each
+// wave then reduces with the fixed DPP tree of wave_sum_f32, and the 8 wave
+// sums are added in wave order.  The standalone pre-norm and the one fused
+// into the one-token decode kernel both use these, so both give the same bits.
+constexpr int kNormThreads = 512;
+
+__device__ __forceinline__ float chunk_sumsq(const float4& a, const float4& b, float ss) {
+  ss += a.x * a.x;
+  ss += a.y * a.y;
+  ss += a.z * a.z;
+  ss += a.w * a.w;
+  ss += b.x * b.x;
+  ss += b.y * b.y;
+  ss += b.z * b.z;
+  ss += b.w * b.w;
+  return ss;
+}
+
+// The workgroup's rms from each thread's partial sum ss (every thread of the
+// 512 must call it: it has a barrier).  wsum: 8 floats of LDS.
+__device__ __forceinline__ float block_rms(float ss, int H, float eps, float* wsum) {
+  ss = wave_sum_f32(ss);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
   lds_barrier();  // wsum is the only data shared; loads in flight stay in flight
-  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  float tot = wsum[0];
+#pragma unroll
+  for (int i = 1; i < kNormThreads / 64; ++i) tot += wsum[i];
   return sqrtf(tot / (float)H + eps);
+}
+
+// Eight values times 1 / r, rounded to bf16 and packed in order.
+__device__ __forceinline__ u32x4 chunk_to_bf16(const float4& a, const float4& b, float r) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)f32_to_bf16_rne(v[2 * j] / r) | ((uint32_t)f32_to_bf16_rne(v[2 * j + 1] / r) << 16);
+  return o;
 }
 
 template <int V>

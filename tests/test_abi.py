@@ -179,6 +179,9 @@ def test_prenorm_validation(lib):
     assert f(None, FAKE, 1, 64, 1e-6, None) == lib.EINVAL
     assert f(FAKE, FAKE, 0, 64, 1e-6, None) == lib.EINVAL
     assert f(FAKE, FAKE, 1, 48, 1e-6, None) == lib.EUNSUPPORTED
+    assert f(FAKE, FAKE, 1, 16416, 1e-6, None) == lib.EUNSUPPORTED
+    assert f(FAKE + 4, FAKE, 1, 64, 1e-6, None) == lib.EALIGN
+    assert f(FAKE, FAKE + 8, 1, 64, 1e-6, None) == lib.EALIGN
 
 
 def test_profiled_needs_eight_events(lib):
