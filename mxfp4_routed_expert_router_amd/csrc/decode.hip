@@ -471,13 +471,143 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   }
 }
 
-// y rows [m0, m1) of this workgroup: every (slot, group) pair of the step's
-// k chosen experts is owned by one lane of one wave (its 32 h values held in
+// ---------------------------------------------------------------- a few tokens
+// The one-token kernels generalised to 2 <= T <= kFewMaxT tokens (routing by
+// the routing kernels, before).  w1/w3: a unit is one row r of w1 and w3 for
+// one sorted slot s (a (token, expert) pair); unit u = r P + s, so the slots
+// of an expert that several tokens chose are consecutive units, taken by
+// neighbouring waves of one workgroup at the same time: the row is read from
+// HBM once and from the caches for the other slots.  Every token's x row
+// sits in LDS (followed by a zero group, as in the one-token kernel).
+constexpr int kFewMaxT = 6;
+
+size_t few13_lds(int T, int H, int k) {
+  return (size_t)T * (H / 32 * 4 + 4) * 16 + (size_t)2 * T * k * 4;
+}
+
+template <int NXG>
+__global__ void __launch_bounds__(kThreads) gemv13_few_kernel(LayerArgs a) {
+  extern __shared__ __align__(16) uint8_t fsm[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = uniform(tid / kWave);
+  const int T = a.T, P = T * a.k, H = a.H, I = a.I, CPR = H / 32;
+  const int RS = CPR * 4 + 4;  // 16-byte chunks a token row, the zero group included
+  u32x4* xl = reinterpret_cast<u32x4*>(fsm);
+  int* tab_e = reinterpret_cast<int*>(fsm + (size_t)T * RS * 16);  // expert of each slot
+  int* tab_x = tab_e + P;                                           // its token's row in xl
+
+  // the slot table: record d (distinct expert) covers slots off .. off + ne - 1
+  const int nrec = P < a.E ? P : a.E;
+  if (tid < nrec) {
+    const u32x4 rec = ld16(a.dinfo + 4 * tid);
+    const int e = (int)rec[0], off = (int)rec[1], ne = (int)rec[2];
+    if (e >= 0)
+      for (int j = 0; j < ne; ++j) tab_e[off + j] = e;
+  }
+  if (tid < P) tab_x[tid] = a.slot_tok[tid] * RS;
+  // x rows, 8 chunks a thread in flight at a time
+  const int nx = T * CPR * 4;
+  for (int c0 = tid; c0 < nx; c0 += 8 * kThreads) {
+    u32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = min(c0 + q * kThreads, nx - 1), t = c / (CPR * 4);
+      v[q] = ld16(a.x + (size_t)t * H + 8 * (c - t * CPR * 4));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = c0 + q * kThreads, t = c / (CPR * 4);
+      if (c < nx) xl[t * RS + (c - t * CPR * 4)] = v[q];
+    }
+  }
+  if (tid < 4 * T) xl[(tid >> 2) * RS + CPR * 4 + (tid & 3)] = zero4();
+  lds_barrier();
+
+  int gc[NXG], xo[NXG];
+#pragma unroll
+  for (int i = 0; i < NXG; ++i) {
+    const int g = lane + kWave * i;
+    gc[i] = g < CPR ? g : CPR - 1;
+    xo[i] = g < CPR ? 4 * g : 4 * CPR;
+  }
+  const int nunits = P * I;
+  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
+  const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;
+  if (F == 0) return;
+  const int wbytes = I * (H / 2), sbytes = I * CPR;
+
+  struct Unit {
+    u32x4 q1[NXG], q3[NXG];
+    uint32_t s1[NXG], s3[NXG];
+  };
+  auto issue = [&](int f, Unit& B) {
+    const int u = wid + f * nw, r = u / P, sl = u - r * P;
+    const int e = uniform(tab_e[sl]);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
+    const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
+    const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
+    const __amdgpu_buffer_rsrc_t q3 = rsrc(a.s3 + (size_t)e * a.stride[3], sbytes);
+    const int ow = r * (H / 2), os = r * CPR;
+#pragma unroll
+    for (int i = 0; i < NXG; ++i) {
+      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, gc[i] * 16, ow, 0));
+      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, gc[i] * 16, ow, 0));
+      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, gc[i], os, 0);
+      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, gc[i], os, 0);
+    }
+  };
+  auto compute = [&](int f, const Unit& B) {
+    const int u = wid + f * nw, r = u / P, sl = u - r * P;
+    const u32x4* xr = xl + uniform(tab_x[sl]);
+    float G = 0.f, U = 0.f;
+#pragma unroll
+    for (int i = 0; i < NXG; ++i) {
+      const float c1 = ue8m0_to_f32(B.s1[i]), c3 = ue8m0_to_f32(B.s3[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 xq = as_bf16x8(xr[xo[i] + q]);
+        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), xq, G);
+        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), xq, U);
+      }
+    }
+    G = wave_sum_f32(G);
+    U = wave_sum_f32(U);
+    if (lane == 0) a.h[(size_t)sl * I + r] = swiglu_bf16(G, U);
+  };
+
+  // the two-buffer loop of the one-token kernel
+  Unit A, B;
+  issue(0, A);
+  int f = 0;
+  for (; f + 2 < F; f += 2) {
+    issue(f + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f, A);
+    issue(f + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f + 1, B);
+  }
+  if (F - f == 2) {
+    issue(f + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(f, A);
+    compute(f + 1, B);
+  } else {
+    compute(f, A);
+  }
+}
+
+// y rows [m0, m1) of this workgroup for one token: every (pair, group) of the
+// token's k pairs is owned by one lane of one wave (its 32 h values held in
 // registers), so each w2 row costs each wave NPL 16-byte loads per lane; the
 // lane sums gate * (chunk . h), the wave reduces with DPP, and the 8 wave
 // partials of a row are added in a fixed order.  No atomics: y is bitwise
-// reproducible.
-template <int NPL>
+// reproducible.  One token (FEW false): the pairs are the sorted slots of the
+// fused routing.  A few tokens (FEW true): workgroup (row block, token t), the
+// pairs t k .. t k + k - 1 through pair_slot; a row block's workgroups for all
+// tokens sit on one XCD (grid x a multiple of 8), so the w2 rows of an expert
+// that several tokens chose are read from HBM about once.
+template <int NPL, bool FEW>
 __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
   __shared__ float part[kWaves][kOneRowsMax];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -486,6 +616,7 @@ __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
   const int NP = a.k * CPR, PW = (NP + kWaves - 1) / kWaves;
   const int R = (H + gridDim.x - 1) / gridDim.x, m0 = blockIdx.x * R;
   const int m1 = min(H, m0 + R);
+  const int tok = FEW ? (int)blockIdx.y : 0;
   if (m0 >= H) return;  // whole workgroup
 
   const uint8_t* wp[NPL];
@@ -499,10 +630,18 @@ __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
     for (int j = 0; j < NPL; ++j) {
       const int p = w * PW + lane + kWave * j;
       const int pc = (lane + kWave * j < PW && p < NP) ? p : 0;
-      sl[j] = pc / CPR;
-      gg[j] = pc - sl[j] * CPR;
-      ev[j] = a.dinfo[4 * sl[j]];
-      gt[j] = a.slot_gate[sl[j]];
+      const int jj = pc / CPR;
+      gg[j] = pc - jj * CPR;
+      if (FEW) {
+        const int pr = tok * a.k + jj;
+        sl[j] = a.pair_slot[pr];
+        ev[j] = a.route.idx[pr];
+        gt[j] = a.gates[pr];
+      } else {
+        sl[j] = jj;
+        ev[j] = a.dinfo[4 * sl[j]];
+        gt[j] = a.slot_gate[sl[j]];
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) hr[j][q] = ld16(a.h + (size_t)sl[j] * I + gg[j] * 32 + 8 * q);
     }
@@ -559,7 +698,7 @@ __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) s += part[q][tid];
-    float* yp = a.y + m0 + tid;
+    float* yp = a.y + (size_t)tok * H + m0 + tid;
     *yp = a.accumulate ? *yp + s : s;
   }
 }
@@ -620,9 +759,45 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
   const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
   const dim3 g2(n2);
   if (npl == 1)
-    launch_k(gemv2_one_kernel<1>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+    launch_k(gemv2_one_kernel<1, false>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   else
-    launch_k(gemv2_one_kernel<2>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+    launch_k(gemv2_one_kernel<2, false>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+  return hipSuccess;
+}
+
+bool few_fits(int T, int H, int I, int k) {
+  return T >= 2 && T <= kFewMaxT && one_token_fits(H, I, k) && few13_lds(T, H, k) <= kDecodeLds;
+}
+
+template <int NXG>
+const void* k13_few() { return reinterpret_cast<const void*>(gemv13_few_kernel<NXG>); }
+
+hipError_t launch_few(const LayerArgs& a, hipStream_t stream) {
+  const hipEvent_t* ev = a.ev;
+  const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
+  const size_t lds = few13_lds(a.T, a.H, a.k);
+  const void* k13 = nxg == 1 ? k13_few<1>() : nxg == 2 ? k13_few<2>() : nxg == 3 ? k13_few<3>()
+                                                                             : k13_few<4>();
+  const Residency res = residency(k13, lds);
+  if (res.wgs <= 0) return hipErrorInvalidValue;
+  const int units = a.T * a.k * a.I;
+  const dim3 blk(kThreads), g13(std::min(res.wgs, (units + kWaves - 1) / kWaves));
+  const hipEvent_t e0 = ev_start(ev, 1), e1 = ev_stop(ev, 1);
+  switch (nxg) {
+    case 1: launch_k(gemv13_few_kernel<1>, g13, blk, lds, stream, e0, e1, a); break;
+    case 2: launch_k(gemv13_few_kernel<2>, g13, blk, lds, stream, e0, e1, a); break;
+    case 3: launch_k(gemv13_few_kernel<3>, g13, blk, lds, stream, e0, e1, a); break;
+    default: launch_k(gemv13_few_kernel<4>, g13, blk, lds, stream, e0, e1, a); break;
+  }
+  // w2: (row block, token) workgroups; the row-block count a multiple of 8 so
+  // that a row block's workgroups share an XCD
+  int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
+  n2 = (n2 + 7) / 8 * 8;
+  const dim3 g2(n2, a.T);
+  if (npl == 1)
+    launch_k(gemv2_one_kernel<1, true>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+  else
+    launch_k(gemv2_one_kernel<2, true>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   return hipSuccess;
 }
 
@@ -630,6 +805,7 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
 
 bool decode_fits(int T, int H, int I, int k) {
   if (T == 1 && one_token_fits(H, I, k)) return true;
+  if (few_fits(T, H, I, k)) return true;
   const int P = T * k;
   return T <= kDecodeMaxTokens && I <= kWaves * kB2 * 128 && lds13_bytes(T, H) <= kDecodeLds &&
          lds2_bytes(P, I) <= kDecodeLds;
@@ -646,6 +822,9 @@ hipError_t launch_decode(const LayerArgs& a, hipStream_t stream) {
   const hipEvent_t* ev = a.ev;
   if (a.T == 1 && one_token_fits(a.H, a.I, a.k)) {
     const hipError_t e = launch_one(a, stream);
+    if (e != hipSuccess) return e;
+  } else if (few_fits(a.T, a.H, a.I, a.k)) {
+    const hipError_t e = launch_few(a, stream);
     if (e != hipSuccess) return e;
   } else {
     const int dmax = P < a.E ? P : a.E;  // distinct experts can not exceed either

@@ -126,6 +126,10 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (1, 256, 2080, 10, 5),    # one token, 65 groups per w2 row
     (1, 256, 1024, 16, 16),   # one token, k = 16: k * I / 32 at the one-token path's limit
     (100, 64, 32, 1024, 16),  # E = 1024, k = 16: the largest router tables, 1600 pairs
+    (2, 8192, 256, 8, 4),     # few-token GEMV path, 4 groups a lane (H = 8192)
+    (6, 1024, 2304, 12, 8),   # few-token path at T = 6, two (pair, group)s a lane in w2
+    (4, 2080, 160, 5, 5),     # few-token path, k = E (every token on every expert), 65 groups a row
+    (6, 256, 128, 2, 2),      # few-token path, two experts shared by all six tokens
     (1, 16384, 64, 4, 2),     # H at its limit: T = 1 on the MFMA decode kernels
     (2, 64, 16384, 3, 2),     # I at its limit (prefill only)
 ]
