@@ -478,15 +478,19 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
 // of an expert that several tokens chose are consecutive units, taken by
 // neighbouring waves of one workgroup at the same time: the row is read from
 // HBM once and from the caches for the other slots.  Every token's x row
-// sits in LDS (followed by a zero group, as in the one-token kernel).
-constexpr int kFewMaxT = 6;
+// sits in LDS (followed by a zero group, as in the one-token kernel): with
+// 8-wave workgroups (two a CU) while that takes at most 64 KB, else 16-wave
+// workgroups (one a CU, up to 160 KB), so a CU holds 16 waves either way.
+constexpr int kFewMaxT = 15;
+constexpr size_t kFewLdsBig = 160 * 1024;
 
 size_t few13_lds(int T, int H, int k) {
   return (size_t)T * (H / 32 * 4 + 4) * 16 + (size_t)2 * T * k * 4;
 }
 
-template <int NXG>
-__global__ void __launch_bounds__(kThreads) gemv13_few_kernel(LayerArgs a) {
+template <int NXG, int NW>
+__global__ void __launch_bounds__(NW * kWave) gemv13_few_kernel(LayerArgs a) {
+  constexpr int kThreads = NW * kWave, kWaves = NW;
   extern __shared__ __align__(16) uint8_t fsm[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
@@ -703,17 +707,18 @@ __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
   }
 }
 
-// Workgroups of `kernel` (kThreads threads, `lds` bytes of dynamic LDS) that the
+// Workgroups of `kernel` (`threads` threads, `lds` bytes of dynamic LDS) that the
 // current device holds at once, and its compute units.  Cached per (device,
 // kernel, lds).
 struct Residency {
   int wgs, cus;
 };
-Residency residency(const void* kernel, size_t lds) {
+Residency residency(const void* kernel, size_t lds, int threads = kThreads) {
   struct Entry {
     int dev;
     const void* kernel;
     size_t lds;
+    int threads;
     Residency r;
   };
   static std::mutex mu;
@@ -723,16 +728,16 @@ Residency residency(const void* kernel, size_t lds) {
   {
     std::lock_guard<std::mutex> lock(mu);
     for (const Entry& x : cache)
-      if (x.dev == dev && x.kernel == kernel && x.lds == lds) return x.r;
+      if (x.dev == dev && x.kernel == kernel && x.lds == lds && x.threads == threads) return x.r;
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
       cus <= 0 || per_cu <= 0)
     return Residency{0, 0};
   const Residency r{cus * per_cu, cus};
   std::lock_guard<std::mutex> lock(mu);
-  cache.push_back(Entry{dev, kernel, lds, r});
+  cache.push_back(Entry{dev, kernel, lds, threads, r});
   return r;
 }
 
@@ -766,32 +771,56 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
 }
 
 bool few_fits(int T, int H, int I, int k) {
-  return T >= 2 && T <= kFewMaxT && one_token_fits(H, I, k) && few13_lds(T, H, k) <= kDecodeLds;
+  return T >= 2 && T <= kFewMaxT && one_token_fits(H, I, k) && few13_lds(T, H, k) <= kFewLdsBig;
 }
 
-template <int NXG>
-const void* k13_few() { return reinterpret_cast<const void*>(gemv13_few_kernel<NXG>); }
+// The few-token w1/w3 kernel for NXG and the workgroup size the LDS allows;
+// the dynamic LDS limit is raised once per (device, kernel).
+template <int NW>
+hipError_t launch_few13(const LayerArgs& a, int nxg, size_t lds, hipStream_t stream, int& cus) {
+  const void* k = nxg == 1   ? reinterpret_cast<const void*>(gemv13_few_kernel<1, NW>)
+                  : nxg == 2 ? reinterpret_cast<const void*>(gemv13_few_kernel<2, NW>)
+                  : nxg == 3 ? reinterpret_cast<const void*>(gemv13_few_kernel<3, NW>)
+                             : reinterpret_cast<const void*>(gemv13_few_kernel<4, NW>);
+  if (lds > kDecodeLds) {
+    static std::mutex mu;
+    static std::vector<std::pair<int, const void*>> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(mu);
+    if (std::find(done.begin(), done.end(), std::make_pair(dev, k)) == done.end()) {
+      const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFewLdsBig);
+      if (e != hipSuccess) return e;
+      done.emplace_back(dev, k);
+    }
+  }
+  const Residency res = residency(k, lds, NW * kWave);
+  if (res.wgs <= 0) return hipErrorInvalidValue;
+  cus = res.cus;
+  const int units = a.T * a.k * a.I;
+  const dim3 blk(NW * kWave), g(std::min(res.wgs, (units + NW - 1) / NW));
+  const hipEvent_t e0 = ev_start(a.ev, 1), e1 = ev_stop(a.ev, 1);
+  switch (nxg) {
+    case 1: launch_k(gemv13_few_kernel<1, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 2: launch_k(gemv13_few_kernel<2, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 3: launch_k(gemv13_few_kernel<3, NW>, g, blk, lds, stream, e0, e1, a); break;
+    default: launch_k(gemv13_few_kernel<4, NW>, g, blk, lds, stream, e0, e1, a); break;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_few(const LayerArgs& a, hipStream_t stream) {
   const hipEvent_t* ev = a.ev;
   const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
   const size_t lds = few13_lds(a.T, a.H, a.k);
-  const void* k13 = nxg == 1 ? k13_few<1>() : nxg == 2 ? k13_few<2>() : nxg == 3 ? k13_few<3>()
-                                                                             : k13_few<4>();
-  const Residency res = residency(k13, lds);
-  if (res.wgs <= 0) return hipErrorInvalidValue;
-  const int units = a.T * a.k * a.I;
-  const dim3 blk(kThreads), g13(std::min(res.wgs, (units + kWaves - 1) / kWaves));
-  const hipEvent_t e0 = ev_start(ev, 1), e1 = ev_stop(ev, 1);
-  switch (nxg) {
-    case 1: launch_k(gemv13_few_kernel<1>, g13, blk, lds, stream, e0, e1, a); break;
-    case 2: launch_k(gemv13_few_kernel<2>, g13, blk, lds, stream, e0, e1, a); break;
-    case 3: launch_k(gemv13_few_kernel<3>, g13, blk, lds, stream, e0, e1, a); break;
-    default: launch_k(gemv13_few_kernel<4>, g13, blk, lds, stream, e0, e1, a); break;
-  }
+  int cus = 0;
+  const hipError_t e13 = lds <= kDecodeLds ? launch_few13<kWaves>(a, nxg, lds, stream, cus)
+                                           : launch_few13<2 * kWaves>(a, nxg, lds, stream, cus);
+  if (e13 != hipSuccess) return e13;
+  const dim3 blk(kThreads);
   // w2: (row block, token) workgroups; the row-block count a multiple of 8 so
   // that a row block's workgroups share an XCD
-  int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
+  int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, cus));
   n2 = (n2 + 7) / 8 * 8;
   const dim3 g2(n2, a.T);
   if (npl == 1)

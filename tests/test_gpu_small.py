@@ -130,6 +130,8 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (6, 1024, 2304, 12, 8),   # few-token path at T = 6, two (pair, group)s a lane in w2
     (4, 2080, 160, 5, 5),     # few-token path, k = E (every token on every expert), 65 groups a row
     (6, 256, 128, 2, 2),      # few-token path, two experts shared by all six tokens
+    (8, 5120, 256, 16, 4),    # few-token path with 16-wave workgroups (x rows take 82 KB of LDS)
+    (15, 4096, 128, 32, 6),   # few-token path at its token limit (124 KB of LDS)
     (1, 16384, 64, 4, 2),     # H at its limit: T = 1 on the MFMA decode kernels
     (2, 64, 16384, 3, 2),     # I at its limit (prefill only)
 ]
