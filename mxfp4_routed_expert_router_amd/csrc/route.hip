@@ -320,6 +320,106 @@ route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_
                                meta, s_g, slot_gate, slot_tok, sm);
 }
 
+// Few tokens (T <= kFewRouteTokens, at most kFewRoutePairs pairs): one wave
+// per token ranks all tokens at once, and the permutation needs no histogram
+// or scan: pair p's sorted slot is the number of pairs with a lower expert
+// plus the pairs of its expert before p (the same stable order as
+// block_permute), counts and offsets are counts over the P pairs, and a slot
+// whose expert differs from the previous slot's starts a distinct-expert
+// record.
+constexpr int kFewRouteThreads = 1024;
+constexpr int kFewRouteTokens = kFewRouteThreads / kWave;
+constexpr int kFewRoutePairs = 256;
+
+// LDS reads of four consecutive ints (arrays padded to a multiple of 4)
+__device__ __forceinline__ int4 lds4(const int* p) { return *reinterpret_cast<const int4*>(p); }
+
+template <int VPL>
+__global__ void __launch_bounds__(kFewRouteThreads)
+route_few_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* idx, float* gates,
+                 int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot,
+                 int32_t* dinfo, int32_t* meta, float* slot_gate, int32_t* slot_tok) {
+  __shared__ __align__(16) int pe[kFewRoutePairs];  // expert of pair p (padding: INT_MAX)
+  __shared__ __align__(16) int se[kFewRoutePairs];  // expert of sorted slot s (padding: INT_MAX)
+  __shared__ float pg[kFewRoutePairs];              // gate of pair p
+  __shared__ int first[kFewRoutePairs + 1];         // first slot of distinct expert d
+  __shared__ int wstarts[kFewRouteThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int P = T * k, P4 = (P + 3) & ~3;
+  if (w < T) {
+    int e;
+    float g;
+    wave_topk_regs<VPL>(logits + (size_t)w * E, E, k, lane, e, g);
+    if (lane < k) {
+      pe[w * k + lane] = e;
+      pg[w * k + lane] = g;
+      idx[w * k + lane] = e;
+      gates[w * k + lane] = g;
+    }
+  }
+  if (tid >= P && tid < P4) {
+    pe[tid] = 0x7FFFFFFF;
+    se[tid] = 0x7FFFFFFF;
+  }
+  lds_barrier();
+  if (tid < P) {
+    const int e = pe[tid];
+    int sl = 0;
+    for (int q = 0; q < P4; q += 4) {
+      const int4 v = lds4(pe + q);
+      sl += (v.x < e || (v.x == e && q + 0 < tid)) ? 1 : 0;
+      sl += (v.y < e || (v.y == e && q + 1 < tid)) ? 1 : 0;
+      sl += (v.z < e || (v.z == e && q + 2 < tid)) ? 1 : 0;
+      sl += (v.w < e || (v.w == e && q + 3 < tid)) ? 1 : 0;
+    }
+    se[sl] = e;
+    pair_slot[tid] = sl;
+    sorted_pairs[sl] = tid;
+    if (slot_tok) slot_tok[sl] = tid / k;
+    if (slot_gate) slot_gate[sl] = pg[tid];
+  }
+  lds_barrier();
+  for (int x = tid; x < E; x += kFewRouteThreads) {
+    int below = 0, cnt = 0;
+    for (int q = 0; q < P4; q += 4) {
+      const int4 v = lds4(se + q);
+      below += (v.x < x ? 1 : 0) + (v.y < x ? 1 : 0) + (v.z < x ? 1 : 0) + (v.w < x ? 1 : 0);
+      cnt += (v.x == x ? 1 : 0) + (v.y == x ? 1 : 0) + (v.z == x ? 1 : 0) + (v.w == x ? 1 : 0);
+    }
+    counts[x] = cnt;
+    offsets[x] = below;
+  }
+  // distinct-expert records: slot s starts one when s == 0 or its expert
+  // differs from slot s - 1; the record index is the number of starts before it
+  const bool start = tid < P && (tid == 0 || se[tid] != se[tid - 1]);
+  const uint64_t bal = __ballot(start);
+  if (lane == 0) wstarts[w] = __popcll(bal);
+  lds_barrier();
+  int d = __popcll(bal & ((1ull << lane) - 1ull)), nd = 0;
+  for (int q = 0; q < kFewRouteThreads / kWave; ++q) {
+    const int c = wstarts[q];
+    d += q < w ? c : 0;
+    nd += c;
+  }
+  if (start) first[d] = tid;
+  if (tid == 0) first[nd] = P;
+  lds_barrier();
+  if (dinfo) {
+    if (start) {
+      dinfo[4 * d + 0] = se[tid];
+      dinfo[4 * d + 1] = tid;
+      dinfo[4 * d + 2] = first[d + 1] - tid;
+      dinfo[4 * d + 3] = 0;
+    }
+    // records past the last distinct expert (up to min(P, E)) say "no expert"
+    for (int x = nd + tid; x < (P < E ? P : E); x += kFewRouteThreads) dinfo[4 * x] = -1;
+  }
+  if (tid == 0) {
+    offsets[E] = P;
+    if (meta) meta[0] = nd;
+  }
+}
+
 int vpl_for(int E) {
   const int v = (E + kWave - 1) / kWave;
   return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 6 ? 6 : v <= 8 ? 8 : 16;
@@ -336,7 +436,21 @@ int perm_pairs_per_block(int P) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const int P = a.T * a.k;
   const int vpl = vpl_for(a.E);
-  if (a.T <= kSmallRouteTokens && P <= kSmallRoutePairs) {
+  if (a.T <= kFewRouteTokens && P <= kFewRoutePairs) {
+#define MOE_ROUTE_FEW(V)                                                                         \
+  launch_k(route_few_kernel<V>, dim3(1), dim3(kFewRouteThreads), 0, stream, ev_start(a.ev, 0),   \
+           ev_stop(a.ev, 0), a.logits, a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets,       \
+           a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok)
+    switch (vpl) {
+      case 1: MOE_ROUTE_FEW(1); break;
+      case 2: MOE_ROUTE_FEW(2); break;
+      case 4: MOE_ROUTE_FEW(4); break;
+      case 6: MOE_ROUTE_FEW(6); break;
+      case 8: MOE_ROUTE_FEW(8); break;
+      default: MOE_ROUTE_FEW(16); break;
+    }
+#undef MOE_ROUTE_FEW
+  } else if (a.T <= kSmallRouteTokens && P <= kSmallRoutePairs) {
 #define MOE_ROUTE_SMALL(V)                                                                       \
   launch_k(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, ev_start(a.ev, 0),    \
            ev_stop(a.ev, 0), a.logits, a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets,       \

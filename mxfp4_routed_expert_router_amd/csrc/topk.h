@@ -73,11 +73,14 @@ __device__ __forceinline__ void wave_topk_vals(const float (&vals)[VPL], int E, 
     }
     const float v = key_value(m);
     if (j == 0) v0 = v;
-    s += expf(v - v0);  // softmax denominator, summed in rank order
     if (j == lane) { my_e = (int)e_win; my_v = v; }
   }
+  // lane j < k holds the j-th chosen logit; one exp per lane, and the softmax
+  // denominator summed in rank order from the lanes' terms
+  const float ev = expf(my_v - v0);
+  for (int j = 0; j < k; ++j) s += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ev), j));
   e_out = my_e;
-  g_out = expf(my_v - v0) / s;
+  g_out = ev / s;
 }
 
 // As wave_topk_vals, loading the logits itself.
