@@ -68,9 +68,11 @@ extern "C" {
  * differ from PREFILL by the FP8 quantisation of the activations (about 5e-2
  * relative), not by rounding. */
 /* DECODE takes one token on a dedicated path (H <= 8192 and k * I / 32 <=
- * 1024), and 2 <= T <= 16 on MFMA kernels as far as the T
- * activation rows and the T*k h rows they stage in LDS fit 64 KiB each and
- * I <= 3072; at H = 5120, I = 2304, k = 6 that is T <= 2.
+ * 1024); 2 <= T <= 15 on the same GEMV design with the T activation rows staged
+ * in LDS, as far as they fit 160 KiB (T * (H / 32 + 1) * 64 bytes, plus
+ * 8 * T * k; at H = 5120 that is T <= 15); and other shapes with T <= 16 on
+ * MFMA kernels as far as the T activation rows and the T*k h rows they stage
+ * in LDS fit 64 KiB each and I <= 3072.
  * moe_fp4_workspace_size(dims, MOE_FP4_MODE_DECODE, ...) returns
  * MOE_FP4_EUNSUPPORTED outside that range. */
 
