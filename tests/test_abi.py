@@ -90,6 +90,12 @@ def test_workspace_size(lib):
     with pytest.raises(lib.MoeFp4Error) as e:
         lib.moe_fp4_workspace_size(33, 256, 128, 16, 2, lib.MODE_DECODE)
     assert e.value.status == lib.EUNSUPPORTED
+    # the real shape: the few-token kernels stage up to 15 activation rows
+    for T in (1, 2, 6, 15):
+        assert lib.moe_fp4_workspace_size(T, 5120, 2304, 384, 6, lib.MODE_DECODE) > 0
+    with pytest.raises(lib.MoeFp4Error) as e:
+        lib.moe_fp4_workspace_size(16, 5120, 2304, 384, 6, lib.MODE_DECODE)
+    assert e.value.status == lib.EUNSUPPORTED
     n = ctypes.c_size_t()
     assert lib._lib.moe_fp4_workspace_size(None, 0, ctypes.byref(n)) == lib.EINVAL
 
