@@ -59,7 +59,7 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   L.dinfo = o;    o = align_up(o + (size_t)d.E * 16);
   L.meta = o;     o = align_up(o + 64);
   L.perm = o;     // per-block expert counts of the multi-block permutation
-  if (P > (size_t)kSmallRoutePairs) o = align_up(o + (size_t)kPermBlocksMax * d.E * 4);
+  if (P > (size_t)kFewRoutePairs) o = align_up(o + (size_t)kPermBlocksMax * d.E * 4);
   L.h = o;        o = align_up(o + P * (size_t)d.I * 2);
   L.ypair = o;
   L.u = o;  // pre-normed input of moe_fp4_forward_residual: ypair's space in the prefill modes
@@ -166,7 +166,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
   r.meta = at<int32_t>(ws, L.meta);
   r.slot_gate = at<float>(ws, L.slot_gate);
   r.slot_tok = at<int32_t>(ws, L.slot_tok);
-  if ((size_t)d.T * d.k > (size_t)kSmallRoutePairs) r.perm_scratch = at<int32_t>(ws, L.perm);
+  if ((size_t)d.T * d.k > (size_t)kFewRoutePairs) r.perm_scratch = at<int32_t>(ws, L.perm);
   // A one-token decode ranks the logits inside its first expert kernel.
   const bool fused = rmode == MOE_FP4_MODE_DECODE && decode_fuses_route(d.T, d.H, d.I, d.E, d.k);
   r.ev = events;

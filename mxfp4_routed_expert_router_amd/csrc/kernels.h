@@ -9,8 +9,8 @@ namespace moe_fp4 {
 
 constexpr int kMaxExperts = 1024;      // router / permutation LDS tables
 constexpr int kMaxK = 16;
-constexpr int kSmallRouteTokens = 64;  // one-launch route for small batches
-constexpr int kSmallRoutePairs = 1024;
+constexpr int kFewRouteTokens = 64;    // one-launch route (route_few_kernel) up to these
+constexpr int kFewRoutePairs = 1024;
 constexpr int kDecodeMaxTokens = 16;   // decode GEMV: one 16-token MFMA tile per expert
 constexpr size_t kDecodeLds = 65536;   // LDS budget of each decode kernel (x / h rows staged whole)
 

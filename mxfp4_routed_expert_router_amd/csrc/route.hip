@@ -294,42 +294,15 @@ perm_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ g
                                    slot_tok, sm);
 }
 
-// Small batches: top-k and permutation in one launch of 256 threads.  The four
-// waves take the tokens in turn; the chosen ids go through LDS.
-constexpr int kSmallThreads = 256;
-
-template <int VPL>
-__global__ void __launch_bounds__(kSmallThreads)
-route_small_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* idx,
-                   float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
-                   int32_t* pair_slot, int32_t* dinfo, int32_t* meta, float* slot_gate,
-                   int32_t* slot_tok) {
-  __shared__ PermSmem<kSmallThreads> sm;
-  __shared__ int32_t s_idx[kSmallRoutePairs];
-  __shared__ float s_g[kSmallRoutePairs];
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  for (int t = w; t < T; t += kSmallThreads / kWave)
-    wave_topk<VPL>(logits + (size_t)t * E, E, k, lane, s_idx + t * k, s_g + t * k);
-  lds_barrier();
-  const int P = T * k;
-  for (int p = threadIdx.x; p < P; p += kSmallThreads) {
-    idx[p] = s_idx[p];
-    gates[p] = s_g[p];
-  }
-  block_permute<kSmallThreads>(s_idx, P, E, k, counts, offsets, sorted_pairs, pair_slot, dinfo,
-                               meta, s_g, slot_gate, slot_tok, sm);
-}
-
-// Few tokens (T <= kFewRouteTokens, at most kFewRoutePairs pairs): one wave
-// per token ranks all tokens at once, and the permutation needs no histogram
+// Few tokens (T <= kFewRouteTokens, at most kFewRoutePairs pairs): the 16 waves
+// rank the tokens (wave w: tokens w, w + 16, ...), and the permutation needs no histogram
 // or scan: pair p's sorted slot is the number of pairs with a lower expert
 // plus the pairs of its expert before p (the same stable order as
 // block_permute), counts and offsets are counts over the P pairs, and a slot
 // whose expert differs from the previous slot's starts a distinct-expert
 // record.
 constexpr int kFewRouteThreads = 1024;
-constexpr int kFewRouteTokens = kFewRouteThreads / kWave;
-constexpr int kFewRoutePairs = 256;
+static_assert(kFewRoutePairs <= kFewRouteThreads, "one pair a thread");
 
 // LDS reads of four consecutive ints (arrays padded to a multiple of 4)
 __device__ __forceinline__ int4 lds4(const int* p) { return *reinterpret_cast<const int4*>(p); }
@@ -346,15 +319,27 @@ route_few_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t*
   __shared__ int wstarts[kFewRouteThreads / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int P = T * k, P4 = (P + 3) & ~3;
-  if (w < T) {
-    int e;
-    float g;
-    wave_topk_regs<VPL>(logits + (size_t)w * E, E, k, lane, e, g);
-    if (lane < k) {
-      pe[w * k + lane] = e;
-      pg[w * k + lane] = g;
-      idx[w * k + lane] = e;
-      gates[w * k + lane] = g;
+  // every logit row of the wave's tokens is loaded before the first is ranked
+  constexpr int NW = kFewRouteThreads / kWave, kTPW = (kFewRouteTokens + NW - 1) / NW;
+  float lv[kTPW][VPL];
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int t = w + NW * j;
+    wave_load_logits<VPL>(logits + (size_t)(t < T ? t : 0) * E, E, lane, lv[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int t = w + NW * j;
+    if (t < T) {
+      int e;
+      float g;
+      wave_topk_vals<VPL>(lv[j], E, k, lane, e, g);
+      if (lane < k) {
+        pe[t * k + lane] = e;
+        pg[t * k + lane] = g;
+        idx[t * k + lane] = e;
+        gates[t * k + lane] = g;
+      }
     }
   }
   if (tid >= P && tid < P4) {
@@ -362,7 +347,7 @@ route_few_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t*
     se[tid] = 0x7FFFFFFF;
   }
   lds_barrier();
-  if (tid < P) {
+  if (tid < P) {  // P <= kFewRoutePairs = kFewRouteThreads: one pair a thread
     const int e = pe[tid];
     int sl = 0;
     for (int q = 0; q < P4; q += 4) {
@@ -450,21 +435,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
       default: MOE_ROUTE_FEW(16); break;
     }
 #undef MOE_ROUTE_FEW
-  } else if (a.T <= kSmallRouteTokens && P <= kSmallRoutePairs) {
-#define MOE_ROUTE_SMALL(V)                                                                       \
-  launch_k(route_small_kernel<V>, dim3(1), dim3(kSmallThreads), 0, stream, ev_start(a.ev, 0),    \
-           ev_stop(a.ev, 0), a.logits, a.T, a.E, a.k, a.idx, a.gates, a.counts, a.offsets,       \
-           a.sorted_pairs, a.pair_slot, a.dinfo, a.meta, a.slot_gate, a.slot_tok)
-    switch (vpl) {
-      case 1: MOE_ROUTE_SMALL(1); break;
-      case 2: MOE_ROUTE_SMALL(2); break;
-      case 4: MOE_ROUTE_SMALL(4); break;
-      case 6: MOE_ROUTE_SMALL(6); break;
-      case 8: MOE_ROUTE_SMALL(8); break;
-      default: MOE_ROUTE_SMALL(16); break;
-    }
-#undef MOE_ROUTE_SMALL
   } else {
+    // more than 64 tokens or 1024 pairs: one wave per token, then the
+    // permutation (several workgroups with the forward path's scratch, else one)
     const int wpb = 4;
     const dim3 grid((a.T + wpb - 1) / wpb), block(wpb * kWave);
 #define MOE_TOPK(V) \
