@@ -132,6 +132,7 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (6, 256, 128, 2, 2),      # few-token path, two experts shared by all six tokens
     (8, 5120, 256, 16, 4),    # few-token path with 16-wave workgroups (x rows take 82 KB of LDS)
     (15, 4096, 128, 32, 6),   # few-token path at its token limit (124 KB of LDS)
+    (15, 256, 512, 32, 16),   # few-token path with k = 16: 240 pairs
     (1, 16384, 64, 4, 2),     # H at its limit: T = 1 on the MFMA decode kernels
     (2, 64, 16384, 3, 2),     # I at its limit (prefill only)
 ]
