@@ -130,11 +130,21 @@ constexpr int kWLoads = 3 * kTiles;      // even block, per tile: two 1 KB halve
 constexpr int kXLoads = 3;               // even block, per wave holding tokens: two 1 KB quarters and scales
 constexpr int kWLoadsOdd = 2 * kTiles;   // odd block: the halves only
 constexpr int kXLoadsOdd = 2;
+// Where K is a whole number of blocks (K % 256 == 0, K >= 512) the weight
+// scales come four blocks at a time instead (QS below): one 16-byte load a
+// lane, 32 lanes (16 rows x two block pairs), so half the cache lines of the
+// block-pair loads, into one slot a tile.  A row's last pair may hold one
+// block (K % 512 == 256): its load starts 8 bytes earlier, inside the row.  The loads of group g
+// (blocks 4 g .. 4 g + 3) go out right after block 4 g - 1 has read its
+// scale bytes, ahead of that iteration's block loads, so the wait for block
+// 4 g (at most the next block's loads in flight) covers them.
 
 struct SmemMx {
   uint8_t w[kStages][kWaves][kTiles][2048];   // 16 rows x 128 bytes, swizzled: see woff
   uint8_t x[kStages][kTok * kKB];             // E4M3 codes of 64 tokens, swizzled: see xoff
-  uint32_t ws[2][kWaves][kTiles][64];   // blocks 2p, 2p+1 in slot p % 2: dword d of row r at 16 d + r
+  // blocks 2p, 2p+1 in slot p % 2: dword d of row r at 16 d + r; or (QS) blocks
+  // 4g .. 4g+3 in both slots: dword d of row r, block pair q at 4 (16 q + r) + d
+  uint32_t ws[2][kWaves][kTiles][64];
   uint32_t xs[2][kWaves][32];           // token 8 w + i: scale dword d (blocks 2p, 2p+1) at 8 d + i
   int row[kTok];                              // source row of each staged token
   float sal[kWaves * 64];                     // saliency reduction (saliency.h)
@@ -152,7 +162,8 @@ static_assert(kStages == 3, "the loop below waits for all but at most one block"
 // M * kRT == kTiles.  wrow0[m][rt] points at row 0 of the wave's 16-row tile
 // (inside the weights even for rows past the end, whose results are not
 // stored); srow0 at that row's scales.  Tokens past nc load token 0's row.
-template <int M, int kRT, int NT>
+// QS: weight scales four blocks to a load (K % 256 == 0, K >= 512), else two.
+template <bool QS, int M, int kRT, int NT>
 __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&wrow0)[M][kRT],
                                              const uint8_t* const (&srow0)[M][kRT], size_t wrow,
                                              size_t srow, const uint8_t* __restrict__ q,
@@ -198,6 +209,21 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
   };
   const int wdd = lane >> 4, xdd = (lane >> 3) & 3;
 
+  // QS scale loads of group g: lane l < 32 reads row l % 16, block pair
+  // 2 g + l / 16 -- its 16 bytes, moved back to end at the row's end where
+  // they pass it (a one-block last pair; pairs past the end are never used)
+  uint32_t* const qslot = &sm.ws[0][0][0][0] + (size_t)w * kTiles * 128;
+  auto issue_scales = [&](int g) {
+    if (lane < 32) {
+      const int off = min(32 * g + 16 * (lane >> 4), (int)srow - 16);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          lds_load16(lds_addr(qslot + (m * kRT + rt) * 128), srow0[m][rt] + c16 * srow + off);
+    }
+  };
+
   auto issue = [&](int b, int s) {
     const bool tail = half_tail && b == NB - 1;
     const bool even = (b & 1) == 0;
@@ -212,8 +238,8 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
         const uint8_t* const src = wrow0[m][rt] + (size_t)b * 128;
         lds_load16(lds_addr(dst), src + wr_r * wrow + 16 * c0);
         lds_load16(lds_addr(dst + 1024), src + (8 + wr_r) * wrow + 16 * c1);
-        if (even) lds_load4(lds_addr(&sm.ws[ps][w][m * kRT + rt][0]),
-                            srow0[m][rt] + c16 * srow + pair_off(b, wdd));
+        if (!QS && even)
+          lds_load4(lds_addr(&sm.ws[ps][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + pair_off(b, wdd));
       }
     if (xw) {
       lds_load16(lds_addr(&sm.x[s][(8 * w) * kKB]), xsrc[0] + (size_t)b * kKB);
@@ -221,19 +247,32 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
       if (even && lane < 32) lds_load4(lds_addr(&sm.xs[ps][w][0]), ssrc + pair_off(b, xdd));
     }
   };
-  auto compute = [&](int b) {
-    const int s = b % kStages, ps = (b >> 1) & 1, d0 = 2 * (b & 1);
+  // this lane's weight scale bytes of block b, both halves
+  auto read_scales = [&](int b, int (&sa)[2][M][kRT]) {
+    const int ps = (b >> 1) & 1, d0 = 2 * (b & 1);
+    // QS: dword of the block's first half in its 16 bytes, after the shift
+    // of a load moved back (a one-block last pair: by 8 bytes)
+    const int qd = d0 + max(0, 16 * (b >> 1) + 16 - (int)srow) / 4;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      u32x4 A[M][kRT];
-      int sa[M][kRT];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
-          A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * j + kb)]);
-          sa[m][rt] = (int)((sm.ws[ps][w][m * kRT + rt][16 * (d0 + j) + c16] >> (8 * kb)) & 0xFFu);
+          const uint32_t v = QS ? qslot[(m * kRT + rt) * 128 + 4 * (16 * ps + c16) + qd + j]
+                                : sm.ws[ps][w][m * kRT + rt][16 * (d0 + j) + c16];
+          sa[j][m][rt] = (int)((v >> (8 * kb)) & 0xFFu);
         }
+  };
+  auto compute = [&](int b, const int (&sa)[2][M][kRT]) {
+    const int s = b % kStages, ps = (b >> 1) & 1, d0 = 2 * (b & 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 A[M][kRT];
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) A[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * j + kb)]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int t = 16 * nt + c16;
@@ -249,12 +288,14 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
             const u32x4 a4 = A[m][rt];
             const i32x8 Av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
             acc[m][rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                Av, B, acc[m][rt][nt], 4 /* A: E2M1 */, 0 /* B: E4M3 */, 0, sa[m][rt], 0, sb);
+                Av, B, acc[m][rt][nt], 4 /* A: E2M1 */, 0 /* B: E4M3 */, 0, sa[j][m][rt], 0, sb);
           }
       }
     }
   };
 
+  constexpr int kWEven = QS ? kWLoadsOdd : kWLoads;
+  if constexpr (QS) issue_scales(0);
   for (int b = 0; b < kStages - 1 && b < NB; ++b) issue(b, b);
   for (int b = 0; b < NB; ++b) {
     // block b's loads (this wave's) are done once at most the loads of the
@@ -267,13 +308,20 @@ __device__ __forceinline__ void gemm_pass_mx(SmemMx& sm, const uint8_t* const (&
     else if ((b + 1) & 1)
       xw ? wait_then_barrier<kWLoadsOdd + kXLoadsOdd>() : wait_then_barrier<kWLoadsOdd>();
     else
-      xw ? wait_then_barrier<kWLoads + kXLoads>() : wait_then_barrier<kWLoads>();
+      xw ? wait_then_barrier<kWEven + kXLoads>() : wait_then_barrier<kWEven>();
+    int sa[2][M][kRT];
+    read_scales(b, sa);
+    if (QS && (b & 3) == 3 && b + 1 < NB) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads above are done with the slot
+      issue_scales((b + 1) / 4);
+    }
     if (b + kStages - 1 < NB) issue(b + kStages - 1, (b + kStages - 1) % kStages);  // into b-1's slot
-    compute(b);
+    compute(b, sa);
   }
   __syncthreads();  // the LDS is free for the caller (and its row table may change)
 }
 
+template <bool QS>
 __global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
   const int tpe = (a.I + kRows13 - 1) / kRows13;
   int logical;
@@ -301,7 +349,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[2][1][NT];
-      gemm_pass_mx<2, 1, NT>(sm, wr, sr, wrow, srow, a.xq, a.xqs, nc, a.H, acc);
+      gemm_pass_mx<QS, 2, 1, NT>(sm, wr, sr, wrow, srow, a.xq, a.xqs, nc, a.H, acc);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = 16 * nt + c16;
@@ -324,6 +372,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_mx_kernel(LayerArgs a) {
   }
 }
 
+template <bool QS>
 __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
   const int tpe = (a.H + kRows2 - 1) / kRows2;
   int logical;
@@ -356,7 +405,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_mx_kernel(LayerArgs a) {
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[1][2][NT];
-      gemm_pass_mx<1, 2, NT>(sm, wr, sr, wrow, srow, a.hq, a.hqs, nc, a.I, acc);
+      gemm_pass_mx<QS, 1, 2, NT>(sm, wr, sr, wrow, srow, a.hq, a.hqs, nc, a.I, acc);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -410,12 +459,18 @@ hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream) {
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
   launch_k(quant_mx8_kernel, dim3(quant_blocks(a.T, Hp)), dim3(256), 0, stream, ev_start(ev, 1),
            (hipEvent_t) nullptr, (const uint16_t*)a.x, a.T, a.H, Hp, a.xq, a.xqs);
-  launch_k(gemm13_mx_kernel, dim3(xcd_grid(t13)), blk, 0, stream, (hipEvent_t) nullptr,
-           ev_stop(ev, 1), a);
+  // four-block scale loads where K is whole blocks (at least two) and the scales 16-byte aligned
+  auto qs = [](int K, const uint8_t* p, int64_t st) {
+    return K % 256 == 0 && K >= 512 && (uintptr_t)p % 16 == 0 && st % 16 == 0;
+  };
+  const bool qs13 = qs(a.H, a.s1, a.stride[1]) && qs(a.H, a.s3, a.stride[3]);
+  const bool qs2 = qs(a.I, a.s2, a.stride[5]);
+  launch_k(qs13 ? gemm13_mx_kernel<true> : gemm13_mx_kernel<false>, dim3(xcd_grid(t13)), blk, 0,
+           stream, (hipEvent_t) nullptr, ev_stop(ev, 1), a);
   launch_k(quant_mx8_kernel, dim3(quant_blocks(P, Ip)), dim3(256), 0, stream, ev_start(ev, 2),
            (hipEvent_t) nullptr, (const uint16_t*)a.h, P, a.I, Ip, a.hq, a.hqs);
-  launch_k(gemm2_mx_kernel, dim3(xcd_grid(t2)), blk, 0, stream, (hipEvent_t) nullptr, ev_stop(ev, 2),
-           a);
+  launch_k(qs2 ? gemm2_mx_kernel<true> : gemm2_mx_kernel<false>, dim3(xcd_grid(t2)), blk, 0, stream,
+           (hipEvent_t) nullptr, ev_stop(ev, 2), a);
   return launch_combine(a, stream);
 }
 

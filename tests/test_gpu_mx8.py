@@ -121,6 +121,11 @@ MX_CASES = [  # (T, H, I, E, k): H and I multiples of 128
     (37, 384, 256, 9, 3),      # ragged token tiles
     (70, 256, 128, 4, 4),      # k = E, more than 64 tokens per expert (two passes)
     (16, 512, 256, 24, 6),
+    # K % 256 == 0, K >= 512: weight scales four blocks to a load, the last group short
+    (20, 1536, 1024, 6, 3),    # 6 blocks on w1/w3 (last group of 2), 4 on w2 (one group)
+    (12, 2560, 512, 4, 2),     # 10 blocks on w1/w3, 2 on w2
+    (24, 768, 2304, 6, 2),     # 3 and 9 blocks: a one-block last pair
+    (40, 5248, 384, 8, 2),     # K % 512 != 0 at large K: block-pair scale loads, half tail block
 ]
 
 
