@@ -126,6 +126,7 @@ MX_CASES = [  # (T, H, I, E, k): H and I multiples of 128
     (12, 2560, 512, 4, 2),     # 10 blocks on w1/w3, 2 on w2
     (24, 768, 2304, 6, 2),     # 3 and 9 blocks: a one-block last pair
     (40, 5248, 384, 8, 2),     # K % 512 != 0 at large K: block-pair scale loads, half tail block
+    (700, 512, 256, 20, 2),    # 1400 pairs: many-workgroup permutation, experts with two passes
 ]
 
 

@@ -155,6 +155,14 @@ def test_forward_prefill_many_tokens(moe, orc, T):
     _forward_case(moe, orc, T, 128, 96, 3, 2, seed=T, mode=2)
 
 
+def test_forward_prefill_many_pairs_lds(moe, orc):
+    """1400 pairs (the many-workgroup permutation) over E = 20 experts, about
+    half of them with more than 64 tokens (two passes), K a multiple of 256
+    (the LDS-fed GEMMs)."""
+    say("forward prefill T=700 E=20: many-workgroup permutation, LDS-fed GEMMs")
+    _forward_case(moe, orc, 700, 256, 256, 20, 2, seed=7, mode=2)
+
+
 @pytest.mark.parametrize("mode", [1, 2])
 def test_forward_accumulate(moe, orc, mode):
     say(f"forward accumulate mode={mode}")
