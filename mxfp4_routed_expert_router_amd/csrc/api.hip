@@ -97,7 +97,8 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
                  const uint16_t* w_router, const moe_fp4_weights* w, float* y, int mode, int flags,
                  void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                  moe_fp4_route_out* route_out, const hipEvent_t* events,
-                 float* saliency = nullptr, float* x_resid = nullptr) {
+                 float* saliency = nullptr, float* x_resid = nullptr,
+                 const SharedArgs* shared13 = nullptr) {
   if (x_resid) {
     if (x) return MOE_FP4_EINVAL;
     y = x_resid;
@@ -202,6 +203,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
     a.xf = x_resid;
     a.eps = kStackEps;
   }
+  a.shared13 = shared13;
   if (saliency) {
     a.sal_part = at<float>(ws, L.sal);
     a.sal_tiles = sal_tiles(d.H);
@@ -334,10 +336,28 @@ int moe_fp4_forward_shared(const moe_fp4_dims* dims, const uint16_t* x, const fl
   if (rc != MOE_FP4_OK) return rc;
   // the shared expert's h reuses the routed h section once the routed path is done
   if (sw->I > dims->k * dims->I) return MOE_FP4_EUNSUPPORTED;
+  const int rmode = resolve_mode(*dims, mode);
+  const moe_fp4_dims& d = *dims;
+  if (rmode == MOE_FP4_MODE_DECODE && d.T == 1 && decode_one_token(d.T, d.H, d.I, d.k) &&
+      sw->I <= d.H && ws && ws_bytes >= layout(d, rmode).total) {
+    // One token: the shared w1/w3 rows run in the routed w2 launch, their h in
+    // the pre-norm input's section (unused without a residual); then the
+    // shared w2 adds to y.  Same kernels' arithmetic, same bits.
+    SharedArgs s13{};
+    s13.act = x;
+    s13.w[0] = sw->w1; s13.s[0] = sw->s1; s13.w[1] = sw->w3; s13.s[1] = sw->s3;
+    s13.N = sw->I; s13.K = d.H; s13.T = 1;
+    s13.h = at<uint16_t>(ws, layout(d, rmode).u);
+    rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, &s13);
+    if (rc != MOE_FP4_OK) return rc;
+    return launch_shared_w2(s13.h, sw->w2, sw->s2, 1, d.H, sw->I, y, 1, stream) == hipSuccess
+               ? MOE_FP4_OK
+               : MOE_FP4_EHIP;
+  }
   rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
                     nullptr, nullptr);
   if (rc != MOE_FP4_OK) return rc;
-  const int rmode = resolve_mode(*dims, mode);
   uint16_t* const h = at<uint16_t>(ws, layout(*dims, rmode).h);
   const uint8_t* t[6];
   return launch_shared(x, shared_tensors(sw, t), dims->T, dims->H, sw->I, y, 1, h, stream) ==

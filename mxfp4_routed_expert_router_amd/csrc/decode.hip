@@ -28,6 +28,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "shared_gemv.h"
 #include "topk.h"
 
 namespace moe_fp4 {
@@ -612,15 +613,14 @@ __global__ void __launch_bounds__(NW * kWave) gemv13_few_kernel(LayerArgs a) {
 // tokens sit on one XCD (grid x a multiple of 8), so the w2 rows of an expert
 // that several tokens chose are read from HBM about once.
 template <int NPL, bool FEW>
-__global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
+__device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int nblk, int tok) {
   __shared__ float part[kWaves][kOneRowsMax];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = I / 32;
   const int NP = a.k * CPR, PW = (NP + kWaves - 1) / kWaves;
-  const int R = (H + gridDim.x - 1) / gridDim.x, m0 = blockIdx.x * R;
+  const int R = (H + nblk - 1) / nblk, m0 = bid * R;
   const int m1 = min(H, m0 + R);
-  const int tok = FEW ? (int)blockIdx.y : 0;
   if (m0 >= H) return;  // whole workgroup
 
   const uint8_t* wp[NPL];
@@ -707,6 +707,27 @@ __global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
   }
 }
 
+// Workgroup b of nb takes rows b R .. (b + 1) R - 1 of y (R = H / nb rounded up).
+template <int NPL, bool FEW>
+__global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
+  gemv2_one_body<NPL, FEW>(a, blockIdx.x, gridDim.x, FEW ? (int)blockIdx.y : 0);
+}
+
+// The one-token w2 (workgroups below n2, as gemv2_one_kernel) and, in the same
+// launch, the shared expert's w1/w3 rows, one wave a row (the rest): those need
+// only x, and the w2 workgroups, one a compute unit, leave most of each CU's
+// waves free while their row loads are in flight.
+template <int NPL, int SC>
+__global__ void __launch_bounds__(kThreads) gemv2_one_shared_kernel(LayerArgs a, SharedArgs s,
+                                                                     int n2) {
+  if ((int)blockIdx.x < n2) {
+    gemv2_one_body<NPL, false>(a, blockIdx.x, n2, 0);
+    return;
+  }
+  const int n = ((int)blockIdx.x - n2) * kWaves + (int)(threadIdx.x / kWave);
+  if (n < s.N) shared_gemv_row<2, SC>(s, n, threadIdx.x & (kWave - 1));
+}
+
 // Workgroups of `kernel` (`threads` threads, `lds` bytes of dynamic LDS) that the
 // current device holds at once, and its compute units.  Cached per (device,
 // kernel, lds).
@@ -763,6 +784,34 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
   // w2: one workgroup per compute unit, at most kOneRowsMax rows each
   const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
   const dim3 g2(n2);
+  if (a.shared13) {
+    // the shared expert's w1/w3 rows ride along: one wave a row after the n2
+    // w2 workgroups, with the chunk count its own kernel would take
+    const SharedArgs& s = *a.shared13;
+    const int ncl = std::min((s.K / 16 + kWave - 1) / kWave, kGvMaxChunks);
+    const dim3 gs(n2 + (s.N + kWaves - 1) / kWaves);
+#define MOE_W2S(NPL, SC) \
+  launch_k(gemv2_one_shared_kernel<NPL, SC>, gs, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a, s, n2)
+#define MOE_W2S_NPL(NPL)                                                              \
+  switch (ncl) {                                                                     \
+    case 1: MOE_W2S(NPL, 1); break;                                                  \
+    case 2: MOE_W2S(NPL, 2); break;                                                  \
+    case 3: MOE_W2S(NPL, 3); break;                                                  \
+    case 4: MOE_W2S(NPL, 4); break;                                                  \
+    case 5: MOE_W2S(NPL, 5); break;                                                  \
+    case 6: MOE_W2S(NPL, 6); break;                                                  \
+    case 7: MOE_W2S(NPL, 7); break;                                                  \
+    default: MOE_W2S(NPL, 8); break;                                                 \
+  }
+    if (npl == 1) {
+      MOE_W2S_NPL(1)
+    } else {
+      MOE_W2S_NPL(2)
+    }
+#undef MOE_W2S_NPL
+#undef MOE_W2S
+    return hipSuccess;
+  }
   if (npl == 1)
     launch_k(gemv2_one_kernel<1, false>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   else

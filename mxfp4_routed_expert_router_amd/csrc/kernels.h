@@ -54,6 +54,18 @@ struct RouteArgs {
 constexpr int kPermBlocksMax = 256;  // workgroups of the multi-block permutation
 int perm_pairs_per_block(int P);     // pairs each of them owns (a multiple of 256)
 
+// One matrix product of the shared expert (FP8 E4M3 codes, one UE8M0 scale per
+// 32 x 32 block): M = 2 takes w[0], w[1] (w1, w3) into h with the SwiGLU
+// epilogue, M = 1 takes w[0] (w2) into y.
+struct SharedArgs {
+  const uint16_t* act;   // M = 2: x [T][K]; M = 1: h [T][K] (bf16 bits)
+  const uint8_t *w[2], *s[2];
+  int N, K, T;           // output rows, inputs per row, tokens
+  uint16_t* h;           // M = 2 output [T][N]
+  float* y;              // M = 1 output [T][N]
+  int accumulate;
+};
+
 // Weights and routing state shared by the expert kernels.
 struct LayerArgs {
   int T, H, I, E, k;
@@ -85,6 +97,9 @@ struct LayerArgs {
   // unused and the layer's input is bf16(xf / sqrt(mean(xf^2) + eps))
   const float* xf;
   float eps;
+  // one-token decode: the shared expert's w1/w3 (M = 2, T = 1), run in the
+  // routed w2 launch; host memory, read when launching (null: none)
+  const SharedArgs* shared13;
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
@@ -112,6 +127,9 @@ constexpr int kSalRows = 256;  // w2 rows per workgroup tile in every prefill w2
 
 // The shared expert: h = bf16(silu(W1 x) * (W3 x)) [T][I], y (+)= W2 h.
 // w = {w1, s1, w3, s3, w2, s2}: E4M3 codes with 32 x 32 UE8M0 block scales.
+// the shared expert's w2 alone: y (+)= W2 h
+hipError_t launch_shared_w2(const uint16_t* h, const uint8_t* w2, const uint8_t* s2, int T, int H,
+                            int I, float* y, int accumulate, hipStream_t stream);
 hipError_t launch_shared(const uint16_t* x, const uint8_t* const w[6], int T, int H, int I,
                          float* y, int accumulate, uint16_t* h, hipStream_t stream);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,

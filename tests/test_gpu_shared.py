@@ -62,12 +62,14 @@ def test_shared_expert(moe, orc, T, H, I):
     check_y(ya.cpu().numpy(), y0.astype(np.float64) + ref["y"], what + " accumulate")
 
 
-@pytest.mark.parametrize("mode", [1, 2, 3], ids=["decode", "prefill", "mxfp8"])
-def test_forward_shared(moe, orc, mode):
+@pytest.mark.parametrize("mode,T", [(1, 1), (1, 2), (2, 40), (3, 40)],
+                         ids=["decode1", "decode2", "prefill", "mxfp8"])
+def test_forward_shared(moe, orc, mode, T):
     """forward_shared is forward followed by the shared expert added to y (bit
-    for bit), and matches the oracle's routed layer plus its shared expert."""
+    for bit), and matches the oracle's routed layer plus its shared expert.
+    One token runs the shared w1/w3 rows inside the routed w2 launch."""
     import torch
-    T, H, I, E, k = (2, 256, 128, 16, 2) if mode == 1 else (40, 256, 128, 24, 6)
+    H, I, E, k = (256, 128, 16, 2) if mode == 1 else (256, 128, 24, 6)
     say(f"forward_shared T={T} mode={mode}")
     rng = np.random.default_rng(5 + mode)
     experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
