@@ -238,7 +238,10 @@ int moe_fp4_shared_expert(const moe_fp4_dims *dims, const uint16_t *x,
  *   y[t] (+)= sum_j gates[t][j] * Y_(t,j) + W2s h_s[t]
  * The shared expert's h uses the routed path's workspace, so sw->I <=
  * dims->k * dims->I is required (EUNSUPPORTED otherwise); same workspace size
- * as moe_fp4_forward.
+ * as moe_fp4_forward.  For one token in MOE_FP4_MODE_DECODE (the one-token
+ * kernels) with sw->I <= dims->H, the shared w1/w3 rows run in the routed w2
+ * launch and their h sits in the workspace's pre-norm section; y is the same,
+ * bit for bit, as moe_fp4_forward followed by moe_fp4_shared_expert.
  * Errors: as moe_fp4_forward and moe_fp4_shared_expert. */
 int moe_fp4_forward_shared(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
                            const moe_fp4_weights *w, const moe_fp4_shared_weights *sw, float *y,
