@@ -91,6 +91,36 @@ def test_forward_shared(moe, orc, mode, T):
         check_y(y, ref, f"forward_shared mode={mode}")
 
 
+def test_forward_shared_one_token_accumulate(moe, orc):
+    """One token with MOE_FP4_ACCUMULATE (the shared w1/w3 rows inside the
+    routed w2 launch): y0 + layer + shared expert, bit for bit the separate
+    calls', and the oracle's sum to the layer tolerance."""
+    import torch
+    T, H, I, E, k = 1, 512, 256, 12, 3
+    say("forward_shared T=1 accumulate")
+    rng = np.random.default_rng(31)
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
+    w = dev_weights(dense)
+    sw = pins.random_shared(rng, H, I)
+    dsw = _dev_shared(moe, sw)
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    y0 = rng.standard_normal((T, H)).astype(np.float32)
+    xd, lgd = dev_bits(x), torch.from_numpy(lg).cuda()
+    ya = torch.from_numpy(y0).cuda()
+    moe.moe_fp4_forward_shared(xd, lgd, w, dsw, k, y=ya, mode=1, accumulate=True)
+    yb = torch.from_numpy(y0).cuda()
+    moe.moe_fp4_forward(xd, lgd, w, k, y=yb, mode=1, accumulate=True)
+    moe.moe_fp4_shared_expert(xd, dsw, y=yb, accumulate=True)
+    torch.cuda.synchronize()
+    ya, yb = ya.cpu().numpy(), yb.cpu().numpy()
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    ref = (y0.astype(np.float64) + orc.forward(H, I, E, k, x, lg, experts)["y"].astype(np.float64)
+           + orc.shared(x, sw)["y"])
+    check_y(ya, ref, "forward_shared T=1 accumulate")
+
+
 def test_forward_shared_decode_real_shape(moe, orc):
     """One token at the real shape: 6 of 384 routed experts plus the shared expert."""
     import torch
