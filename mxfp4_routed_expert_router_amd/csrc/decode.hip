@@ -341,7 +341,7 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 // (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
 template <int NXG>
 __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
-  __shared__ int de_w[kWaves][kMaxK];
+  __shared__ int de_w[kMaxK];  // the chosen experts in ascending order
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = H / 32;
@@ -350,12 +350,12 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   // followed by one zero group.  A lane's groups past the row end load a
   // duplicate weight chunk (clamped to the last group) and read the zero
   // group of x, so they add exactly nothing.  The logits and a bf16 x are
-  // loaded together at entry; x is stored to LDS after the routing and the
-  // first unit's loads are issued.
+  // loaded together at entry (the logits by wave 0 alone), and x is stored
+  // to LDS while wave 0 ranks.
   __shared__ u32x4 xl[kOneMaxXG * kWave * 4 + 4];
   static_assert(kOneMaxXG * kWave * 4 <= 2 * kThreads, "x chunks per thread");
   float lv[kFusedVPL];
-  if (a.fused_route) wave_load_logits<kFusedVPL>(a.logits, a.E, lane, lv);
+  if (a.fused_route && w == 0) wave_load_logits<kFusedVPL>(a.logits, a.E, lane, lv);
   const int nc = CPR * 4, c0 = tid, c1 = tid + kThreads;
   const int cc0 = c0 < nc ? c0 : 0, cc1 = c1 < nc ? c1 : 0;
   u32x4 xv0 = zero4(), xv1 = zero4();
@@ -370,13 +370,16 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     xv0 = ld16(a.x + 8 * cc0);
     xv1 = ld16(a.x + 8 * cc1);
   }
-  if (a.fused_route) {
-    route_one_wave(a, lv, de_w[w]);
-  } else if (lane < a.k) {
-    de_w[w][lane] = a.dinfo[4 * lane];
+  // Wave 0 ranks the logits while the other waves stage x; the barrier
+  // below publishes both.  (Every wave ranking for itself, which needs no
+  // barrier before its first loads, kept the SIMDs busy for 3-4 us: 16 waves
+  // a CU running the same six wave-wide reductions.)
+  if (w == 0) {
+    if (a.fused_route)
+      route_one_wave(a, lv, de_w);
+    else if (lane < a.k)
+      de_w[lane] = a.dinfo[4 * lane];
   }
-  // de_w[w] is written and read by wave w only: LDS operations of one wave
-  // complete in order, so no barrier is needed before the first issue
 
   int gc[NXG], xo[NXG];
 #pragma unroll
@@ -396,7 +399,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   };
   auto issue = [&](int f, Unit& B) {
     const int u = wid + f * nw, d = u / I, r = u - d * I;
-    const int e = uniform(de_w[w][d]);
+    const int e = uniform(de_w[d]);
     const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
     const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
     const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
@@ -429,8 +432,6 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   };
 
   Unit A, B;
-  if (F > 0) issue(0, A);
-  __builtin_amdgcn_sched_barrier(0);
   if (a.xf) {
     // the layer's input is the pre-norm of the fp32 row xf, computed as
     // moe_fp4_prenorm_bf16 computes it (same ownership and order: same bits)
@@ -446,8 +447,10 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   if (c1 < nc) xl[c1] = xv1;
   if (tid < 4) xl[nc + tid] = zero4();
   lds_barrier();
-  if (a.fused_route && blockIdx.x == 0) publish_counts(a, de_w[0]);
+  if (a.fused_route && blockIdx.x == 0) publish_counts(a, de_w);
   if (F == 0) return;
+  issue(0, A);
+  __builtin_amdgcn_sched_barrier(0);
 
   // Two register buffers; the loop body has no conditional loads, so each wait
   // is for the older buffer only and the next unit stays in flight.  The
