@@ -70,6 +70,54 @@ def test_route_ties_zero_nan(moe, orc):
     assert np.max(np.abs(gg[ok] - g[ok])) <= 1e-6
 
 
+def _one_token_rows(rng, E):
+    """Logit rows for the one-token kernel's in-kernel ranking: exact ties,
+    neighbouring floats at the top (keys equal but for their lowest bits),
+    signed zeros, NaN and infinities, and plain rows."""
+    rows = [rng.standard_normal(E).astype(np.float32) for _ in range(3)]
+    r = np.round(rng.standard_normal(E), 1).astype(np.float32)  # many exact ties
+    rows.append(r)
+    r = rng.standard_normal(E).astype(np.float32)
+    top = np.float32(3.0)
+    for j, e in enumerate((17, 250, 3, 99, 300, 64, 128)):  # 3.0 and its neighbours
+        v = top
+        for _ in range(j % 4):
+            v = np.nextafter(v, np.float32(np.inf) if j % 2 else np.float32(-np.inf))
+        r[e] = v
+    rows.append(r)
+    r = np.zeros(E, np.float32)
+    r[::2] = -0.0
+    rows.append(r)
+    r = rng.standard_normal(E).astype(np.float32)
+    r[5], r[7], r[9], r[200] = np.nan, np.inf, -np.inf, np.inf
+    rows.append(r)
+    return rows
+
+
+def test_one_token_routing_ties(moe, orc):
+    """The one-token kernel ranks the logits itself: bit-exact against the
+    oracle on ties, near-ties, signed zeros, NaN and infinities."""
+    import torch
+    say("one-token in-kernel routing: ties and near-ties")
+    rng = np.random.default_rng(77)
+    H, I, E, k = 256, 128, 384, 6
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
+    w = dev_weights(dense)
+    x = pins.rand_bf16(rng, (1, H))
+    for i, row in enumerate(_one_token_rows(rng, E)):
+        lg = row[None, :]
+        idx, g, perm = _route_ref(orc, lg, k, E)
+        _, _, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k,
+                                                mode=moe.MODE_DECODE)
+        torch.cuda.synchronize()
+        assert np.array_equal(route.topk_idx.cpu().numpy(), idx), f"row {i}"
+        for name, ref in zip(("counts", "offsets", "sorted_pairs", "pair_slot"), perm):
+            assert np.array_equal(getattr(route, name).cpu().numpy(), ref), f"row {i} {name}"
+        if np.isfinite(row).all():
+            assert np.max(np.abs(route.gates.cpu().numpy() - g)) <= 1e-6, f"row {i}"
+
+
 def test_route_repeatable(moe):
     say("route twice, bitwise")
     rng = np.random.default_rng(3)
