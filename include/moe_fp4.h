@@ -79,7 +79,7 @@ extern "C" {
 /* ---- forward flags */
 #define MOE_FP4_ACCUMULATE    1  /* y += layer output (default: y = layer output)    */
 
-/* Supported range: 1 <= T <= 65536, 1 <= E <= 1024, 1 <= k <= min(E, 16),
+/* Supported range: 1 <= T <= 65535, 1 <= E <= 1024, 1 <= k <= min(E, 16),
  * H and I multiples of 32 with 32 <= H, I <= 16384. */
 typedef struct {
   int32_t T;  /* tokens in the call                  */
@@ -125,13 +125,38 @@ typedef struct {
  * Errors: EINVAL (null), EUNSUPPORTED (dims out of range or mode unknown). */
 int moe_fp4_workspace_size(const moe_fp4_dims *dims, int mode, size_t *bytes);
 
+/* ---- kernel paths (moe_fp4_plan) */
+#define MOE_FP4_PATH_DECODE_ONE     1  /* one token: GEMV kernels, routing in the first  */
+#define MOE_FP4_PATH_DECODE_FEW     2  /* 2..15 tokens: the same GEMV design, x in LDS   */
+#define MOE_FP4_PATH_DECODE_MFMA    3  /* other small shapes: MFMA GEMV kernels          */
+#define MOE_FP4_PATH_PREFILL        4  /* grouped GEMMs, bf16 activations                */
+#define MOE_FP4_PATH_PREFILL_MXFP8  5  /* grouped GEMMs, MXFP8 activations               */
+
+/* Which kernels moe_fp4_forward takes for these dims and mode (for profiling
+ * and for checks that depend on the kernels' accumulation order): *path is one
+ * of MOE_FP4_PATH_*.  Host only, enqueues nothing.
+ * Errors: EINVAL (null), EUNSUPPORTED (as moe_fp4_workspace_size). */
+int moe_fp4_plan(const moe_fp4_dims *dims, int mode, int *path);
+
+/* Bytes of workspace moe_fp4_route needs: 0 up to 64 tokens and 1024 pairs
+ * (one workgroup ranks and permutes them), else the per-workgroup expert
+ * counts and per-slot records of the permutation spread over many workgroups.
+ * dims->H and dims->I are not used.
+ * Errors: EINVAL (null or a non-positive size), EUNSUPPORTED (T > 65535,
+ * E > 1024, k > 16). */
+int moe_fp4_route_workspace_size(const moe_fp4_dims *dims, size_t *bytes);
+
 /* Router and token permutation (top-k + softmax over the chosen logits, then a
  * histogram, scan and stable scatter of the T*k pairs grouped by expert).
  *   logits  [T][E] fp32, row-major, 4-byte aligned.
+ *   ws      device workspace of at least moe_fp4_route_workspace_size bytes,
+ *           256-byte aligned (may be NULL when that size is 0); its contents
+ *           need no initialisation.
  * Results are bit-exact functions of the logits (no atomics-order dependence).
- * Errors: EINVAL (a null pointer), EUNSUPPORTED (dims), EHIP. */
+ * Errors: EINVAL (a null pointer), EUNSUPPORTED (dims), EALIGN, EWORKSPACE,
+ * EHIP. */
 int moe_fp4_route(const moe_fp4_dims *dims, const float *logits, moe_fp4_route_out *out,
-                  hipStream_t stream);
+                  void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Whole layer: route, experts, combine.
  *   x       [T][H] bf16 bit patterns, 16-byte aligned

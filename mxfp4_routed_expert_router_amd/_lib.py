@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_fp4.so")
 
 OK, EINVAL, EUNSUPPORTED, EALIGN, EWORKSPACE, EHIP = range(6)
 MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_PREFILL_MXFP8 = 0, 1, 2, 3
+(PATH_DECODE_ONE, PATH_DECODE_FEW, PATH_DECODE_MFMA, PATH_PREFILL,
+ PATH_PREFILL_MXFP8) = 1, 2, 3, 4, 5
 ACCUMULATE = 1
 TENSORS = ("w1", "s1", "w3", "s3", "w2", "s2")
 
@@ -54,7 +56,9 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_fp4_workspace_size.argtypes = [ctypes.POINTER(Dims), I32, ctypes.POINTER(SZ)]
-    lib.moe_fp4_route.argtypes = [ctypes.POINTER(Dims), P, ctypes.POINTER(RouteOut), P]
+    lib.moe_fp4_route.argtypes = [ctypes.POINTER(Dims), P, ctypes.POINTER(RouteOut), P, SZ, P]
+    lib.moe_fp4_route_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(SZ)]
+    lib.moe_fp4_plan.argtypes = [ctypes.POINTER(Dims), I32, ctypes.POINTER(I32)]
     lib.moe_fp4_forward.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights), P, I32,
                                     I32, P, SZ, P]
     lib.moe_fp4_forward_debug.argtypes = lib.moe_fp4_forward.argtypes + [P, ctypes.POINTER(RouteOut)]
@@ -74,7 +78,8 @@ def _load():
     lib.moe_fp4_forward_saliency.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights),
                                              P, P, I32, I32, P, SZ, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
-    for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward",
+    for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward", "moe_fp4_plan",
+              "moe_fp4_route_workspace_size",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
               "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency",
               "moe_fp4_shared_expert", "moe_fp4_forward_shared", "moe_fp4_forward_residual"):
@@ -183,13 +188,33 @@ def moe_fp4_workspace_size(T: int, H: int, I: int, E: int, k: int, mode: int = M
     return n.value
 
 
-def moe_fp4_route(logits: torch.Tensor, k: int) -> Route:
+def moe_fp4_plan(T: int, H: int, I: int, E: int, k: int, mode: int = MODE_AUTO) -> int:
+    """The kernel path (PATH_*) moe_fp4_forward takes for these sizes and mode."""
+    path = ctypes.c_int()
+    _check(_lib.moe_fp4_plan(ctypes.byref(Dims(T, H, I, E, k)), mode, ctypes.byref(path)),
+           "moe_fp4_plan")
+    return path.value
+
+
+def moe_fp4_route_workspace_size(T: int, E: int, k: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.moe_fp4_route_workspace_size(ctypes.byref(Dims(T, 0, 0, E, k)), ctypes.byref(n)),
+           "moe_fp4_route_workspace_size")
+    return n.value
+
+
+def moe_fp4_route(logits: torch.Tensor, k: int, workspace: Optional[torch.Tensor] = None) -> Route:
     _need(logits, "logits", (torch.float32,), 2)
     T, E = logits.shape
     out = Route.empty(T, E, k, logits.device)
     rs = out.as_struct()
+    nws = moe_fp4_route_workspace_size(T, E, k)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=logits.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.moe_fp4_route(ctypes.byref(Dims(T, 0, 0, E, k)), logits.data_ptr(),
-                              ctypes.byref(rs), _stream(logits)), "moe_fp4_route")
+                              ctypes.byref(rs), ws_ptr, ws_n, _stream(logits)), "moe_fp4_route")
     return out
 
 

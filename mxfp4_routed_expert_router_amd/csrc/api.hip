@@ -81,6 +81,25 @@ WsLayout layout(const moe_fp4_dims& d, int rmode) {
   return L;
 }
 
+// Workspace of moe_fp4_route: the records the many-workgroup permutation
+// writes besides the caller's outputs; none up to kFewRoutePairs pairs.
+struct RouteWs {
+  size_t dinfo, meta, slot_gate, slot_tok, perm, total;
+};
+RouteWs route_layout(const moe_fp4_dims& d) {
+  RouteWs L{};
+  const size_t P = (size_t)d.T * d.k;
+  if (d.T <= kFewRouteTokens && P <= (size_t)kFewRoutePairs) return L;
+  size_t o = 0;
+  L.dinfo = o;     o = align_up(o + (size_t)d.E * 16);
+  L.meta = o;      o = align_up(o + 64);
+  L.slot_gate = o; o = align_up(o + P * 4);
+  L.slot_tok = o;  o = align_up(o + P * 4);
+  L.perm = o;      o = align_up(o + (size_t)kPermBlocksMax * d.E * 4);
+  L.total = o;
+  return L;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 template <typename T>
@@ -262,23 +281,65 @@ int moe_fp4_workspace_size(const moe_fp4_dims* dims, int mode, size_t* bytes) {
   return MOE_FP4_OK;
 }
 
-int moe_fp4_route(const moe_fp4_dims* dims, const float* logits, moe_fp4_route_out* out,
-                  hipStream_t stream) {
-  if (!dims || !logits || !out || !out->topk_idx || !out->gates || !out->counts ||
-      !out->offsets || !out->sorted_pairs || !out->pair_slot)
-    return MOE_FP4_EINVAL;
+int moe_fp4_plan(const moe_fp4_dims* dims, int mode, int* path) {
+  if (!dims || !path) return MOE_FP4_EINVAL;
+  const moe_fp4_dims d = *dims;
+  if (!dims_ok(d)) return MOE_FP4_EUNSUPPORTED;
+  const int rmode = resolve_mode(d, mode);
+  if (rmode < 0) return MOE_FP4_EUNSUPPORTED;
+  if (rmode == MOE_FP4_MODE_DECODE) {
+    const int fam = decode_family(d.T, d.H, d.I, d.k);
+    *path = fam == 1 ? MOE_FP4_PATH_DECODE_ONE : fam == 2 ? MOE_FP4_PATH_DECODE_FEW
+                                                          : MOE_FP4_PATH_DECODE_MFMA;
+  } else {
+    *path = rmode == MOE_FP4_MODE_PREFILL_MXFP8 ? MOE_FP4_PATH_PREFILL_MXFP8 : MOE_FP4_PATH_PREFILL;
+  }
+  return MOE_FP4_OK;
+}
+
+namespace {
+int route_dims(const moe_fp4_dims* dims) {
+  if (!dims) return MOE_FP4_EINVAL;
   const moe_fp4_dims d = *dims;
   if (d.T < 1 || d.E < 1 || d.k < 1 || d.k > d.E) return MOE_FP4_EINVAL;
   if (d.T > 65535 || d.E > kMaxExperts || d.k > kMaxK) return MOE_FP4_EUNSUPPORTED;
-  if (!aligned(logits, 4)) return MOE_FP4_EALIGN;
-  // The per-distinct-expert records are internal to the forward path; with null
-  // pointers the permutation skips it.
+  return MOE_FP4_OK;
+}
+}  // namespace
+
+int moe_fp4_route_workspace_size(const moe_fp4_dims* dims, size_t* bytes) {
+  if (!bytes) return MOE_FP4_EINVAL;
+  const int rc = route_dims(dims);
+  if (rc != MOE_FP4_OK) return rc;
+  *bytes = route_layout(*dims).total;
+  return MOE_FP4_OK;
+}
+
+int moe_fp4_route(const moe_fp4_dims* dims, const float* logits, moe_fp4_route_out* out,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dims || !logits || !out || !out->topk_idx || !out->gates || !out->counts ||
+      !out->offsets || !out->sorted_pairs || !out->pair_slot)
+    return MOE_FP4_EINVAL;
+  const int rc = route_dims(dims);
+  if (rc != MOE_FP4_OK) return rc;
+  const moe_fp4_dims d = *dims;
+  if (!aligned(logits, 4) || (ws && !aligned(ws, kAlign))) return MOE_FP4_EALIGN;
+  const RouteWs L = route_layout(d);
+  if (L.total > 0 && (!ws || ws_bytes < L.total)) return MOE_FP4_EWORKSPACE;
   RouteArgs r{};
   r.logits = logits;
   r.T = d.T; r.E = d.E; r.k = d.k;
   r.idx = out->topk_idx; r.gates = out->gates; r.counts = out->counts; r.offsets = out->offsets;
   r.sorted_pairs = out->sorted_pairs; r.pair_slot = out->pair_slot;
-  r.dinfo = nullptr; r.meta = nullptr; r.slot_gate = nullptr; r.slot_tok = nullptr;
+  if (L.total > 0) {
+    // large batches: the permutation spread over many workgroups, with its
+    // per-workgroup counts and per-slot records in the workspace
+    r.dinfo = at<int32_t>(ws, L.dinfo);
+    r.meta = at<int32_t>(ws, L.meta);
+    r.slot_gate = at<float>(ws, L.slot_gate);
+    r.slot_tok = at<int32_t>(ws, L.slot_tok);
+    r.perm_scratch = at<int32_t>(ws, L.perm);
+  }
   return launch_route(r, stream) == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP;
 }
 

@@ -285,13 +285,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// The k chosen experts of the token by ascending id (slot d), as wave w sees
-// them in its own row of the table.  With the routing fused, every wave ranks
-// the logits itself (the same computation, so the same result in every wave):
-// it can then issue its first unit's loads without waiting for any other wave.
-// Each chosen expert holds exactly one pair, so the expert of rank j sits in
-// sorted slot (number of chosen ids below it).  Wave 0 of workgroup 0
-// publishes the routing result.
+// The k chosen experts of the token by ascending id (slot d), ranked by the one
+// wave that calls this (wave 0 of each workgroup) into the workgroup's table;
+// the other waves wait for it at the barrier that also publishes x.  Each
+// chosen expert holds exactly one pair, so the expert of rank j sits in sorted
+// slot (number of chosen ids below it).  Wave 0 of workgroup 0 publishes the
+// routing result.
 __device__ __forceinline__ void route_one_wave(const LayerArgs& a, const float (&lv)[kFusedVPL],
                                                int (&de)[kMaxK]) {
   const int lane = threadIdx.x & (kWave - 1), k = a.k;
@@ -893,6 +892,11 @@ bool decode_fits(int T, int H, int I, int k) {
 }
 
 bool decode_one_token(int T, int H, int I, int k) { return T == 1 && one_token_fits(H, I, k); }
+
+int decode_family(int T, int H, int I, int k) {
+  if (T == 1 && one_token_fits(H, I, k)) return 1;
+  return few_fits(T, H, I, k) ? 2 : 3;
+}
 
 bool decode_fuses_route(int T, int H, int I, int E, int k) {
   return T == 1 && one_token_fits(H, I, k) && E <= kFusedVPL * kWave;

@@ -106,6 +106,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 bool decode_fits(int T, int H, int I, int k);  // shapes the decode kernels take
 bool decode_fuses_route(int T, int H, int I, int E, int k);  // decode routes in its first kernel
 bool decode_one_token(int T, int H, int I, int k);           // the one-token decode kernels run
+int decode_family(int T, int H, int I, int k);  // 1 one-token, 2 few-token GEMV, 3 MFMA GEMV
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream);
 hipError_t launch_prefill_mx8(const LayerArgs& a, hipStream_t stream);

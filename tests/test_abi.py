@@ -172,12 +172,48 @@ def test_route_validation(lib):
     for n in ("topk_idx", "gates", "counts", "offsets", "sorted_pairs", "pair_slot"):
         setattr(r, n, FAKE)
     f = lib._lib.moe_fp4_route
-    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), None, ctypes.byref(r), None) == lib.EINVAL
-    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 20)), FAKE, ctypes.byref(r), None) == lib.EINVAL
-    assert f(ctypes.byref(lib.Dims(4, 0, 0, 2000, 2)), FAKE, ctypes.byref(r), None) == lib.EUNSUPPORTED
-    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), FAKE + 2, ctypes.byref(r), None) == lib.EALIGN
+    d4 = ctypes.byref(lib.Dims(4, 0, 0, 16, 2))
+    assert f(d4, None, ctypes.byref(r), None, 0, None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 20)), FAKE, ctypes.byref(r), None, 0, None) == lib.EINVAL
+    assert f(ctypes.byref(lib.Dims(4, 0, 0, 2000, 2)), FAKE, ctypes.byref(r), None, 0,
+             None) == lib.EUNSUPPORTED
+    assert f(d4, FAKE + 2, ctypes.byref(r), None, 0, None) == lib.EALIGN
     r.gates = 0
-    assert f(ctypes.byref(lib.Dims(4, 0, 0, 16, 2)), FAKE, ctypes.byref(r), None) == lib.EINVAL
+    assert f(d4, FAKE, ctypes.byref(r), None, 0, None) == lib.EINVAL
+
+
+def test_route_workspace(lib):
+    """Up to 64 tokens and 1024 pairs routing needs no workspace; the 2048-token
+    chunk (12,288 pairs) needs one for the many-workgroup permutation, and a
+    missing, short or misaligned one is refused before anything is enqueued."""
+    r = lib.RouteOut()
+    for n in ("topk_idx", "gates", "counts", "offsets", "sorted_pairs", "pair_slot"):
+        setattr(r, n, FAKE)
+    assert lib.moe_fp4_route_workspace_size(64, 384, 16) == 0
+    assert lib.moe_fp4_route_workspace_size(6, 384, 6) == 0
+    n = lib.moe_fp4_route_workspace_size(2048, 384, 6)
+    assert n >= 256 * 384 * 4 + 2 * 12288 * 4 + 384 * 16
+    f = lib._lib.moe_fp4_route
+    d = ctypes.byref(lib.Dims(2048, 0, 0, 384, 6))
+    assert f(d, FAKE, ctypes.byref(r), None, 0, None) == lib.EWORKSPACE
+    assert f(d, FAKE, ctypes.byref(r), FAKE, n - 1, None) == lib.EWORKSPACE
+    assert f(d, FAKE, ctypes.byref(r), FAKE + 16, n, None) == lib.EALIGN
+    with pytest.raises(lib.MoeFp4Error):
+        lib.moe_fp4_route_workspace_size(0, 384, 6)
+
+
+def test_plan(lib):
+    """The kernel path a forward call takes, by size and mode."""
+    assert lib.moe_fp4_plan(1, 5120, 2304, 384, 6) == lib.PATH_DECODE_ONE
+    assert lib.moe_fp4_plan(6, 5120, 2304, 384, 6) == lib.PATH_DECODE_FEW
+    assert lib.moe_fp4_plan(15, 5120, 2304, 384, 6) == lib.PATH_DECODE_FEW
+    assert lib.moe_fp4_plan(16, 5120, 2304, 384, 6) == lib.PATH_PREFILL
+    assert lib.moe_fp4_plan(2048, 5120, 2304, 384, 6) == lib.PATH_PREFILL
+    assert lib.moe_fp4_plan(1, 5120, 2304, 384, 6, lib.MODE_PREFILL) == lib.PATH_PREFILL
+    assert lib.moe_fp4_plan(32, 5120, 2304, 384, 6, lib.MODE_PREFILL_MXFP8) == lib.PATH_PREFILL_MXFP8
+    assert lib.moe_fp4_plan(16, 256, 128, 16, 2, lib.MODE_DECODE) == lib.PATH_DECODE_MFMA
+    with pytest.raises(lib.MoeFp4Error):
+        lib.moe_fp4_plan(32, 5120, 2304, 384, 6, lib.MODE_DECODE)
 
 
 def test_prenorm_validation(lib):
