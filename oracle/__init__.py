@@ -28,15 +28,27 @@ _i32p = np.ctypeslib.ndpointer(np.int32, flags="C")
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C")
 
 
-def build(out: str = SO, mutant: int = 0) -> str:
-    """Compile oracle.c (optionally with one planted mistake) into a shared library."""
-    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-o", out, SRC, "-lm"]
-    if mutant:
-        cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
+def build(out: str = SO, src: str = SRC) -> str:
+    """Compile oracle.c (or `src`, a copy of it: the mutation tests build copies
+    with one planted mistake) into a shared library."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-o", out, src, "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"oracle build failed: {' '.join(cmd)}\n{r.stderr}")
     return out
+
+
+class _ACC(ctypes.Structure):
+    """oracle_acc: the accumulation model an h bound is for (see oracle.c)."""
+    _fields_ = [("sum", ctypes.c_double), ("prefix", ctypes.c_double), ("block", ctypes.c_int)]
+
+
+def _acc(acc):
+    """None (gamma_H), or (sum, prefix, block)."""
+    if acc is None:
+        return None
+    s, p, b = acc
+    return ctypes.byref(_ACC(float(s), float(p), int(b)))
 
 
 class _OW(ctypes.Structure):
@@ -67,15 +79,15 @@ class Oracle:
                                                               ctypes.c_void_p, ctypes.c_void_p,
                                                               ctypes.c_int]
         lib.oracle_saliency.restype = ctypes.c_int
-        lib.oracle_shared.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 11
+        lib.oracle_shared.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 12
         lib.oracle_shared.restype = None
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p, _f32p,
                                       ctypes.POINTER(_OW), ctypes.c_int, ctypes.c_void_p,
                                       _f32p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_forward_mx8.restype = ctypes.c_int
-        lib.oracle_forward_mx8.argtypes = lib.oracle_forward.argtypes + [ctypes.c_double]
+        lib.oracle_forward_mx8.argtypes = lib.oracle_forward.argtypes
         lib.oracle_e4m3.restype = ctypes.c_double
         lib.oracle_e4m3.argtypes = [ctypes.c_int]
         lib.oracle_mx8_quant.restype = None
@@ -88,10 +100,16 @@ class Oracle:
         lib.oracle_stack_layer.argtypes = [ctypes.c_int] * 5 + [_f32p, _f32p, ctypes.POINTER(_OW)]
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         self.lib = lib
 
     def threads(self) -> int:
         return int(self.lib.oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads of the oracle's parallel loops from now on."""
+        self.lib.oracle_set_threads(int(n))
 
     # ---------------------------------------------------------------- formats
     def e2m1(self, code: int) -> float:
@@ -165,11 +183,13 @@ class Oracle:
 
     def forward(self, H: int, I: int, E: int, k: int, x_bits: np.ndarray, logits: np.ndarray,
                 experts: Dict[int, Dict[str, np.ndarray]], tokens: Optional[Sequence[int]] = None,
-                want_h: bool = False, mx8: bool = False, gamma: float = 0.0):
+                want_h: bool = False, mx8: bool = False, acc=None):
         """y for the listed tokens (default all).  `experts` maps expert id -> its six
         byte tensors; only experts the router selects for the listed tokens are needed.
         With mx8, x and the bf16 h are quantised to MXFP8 before the matrices that
-        read them, and hbound uses `gamma` as the relative accumulation bound.
+        read them.  hbound bounds an fp32 evaluation of G and U under the
+        accumulation model `acc` = (sum, prefix, block) (None: gamma_H, the
+        products summed one by one in any order); see oracle_acc in oracle.c.
         Returns dict(y, idx, gates[, h, hpre, hbound])."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         logits = np.ascontiguousarray(logits, dtype=np.float32)
@@ -188,8 +208,7 @@ class Oracle:
                 None if tok is None else tok.ctypes.data, y,
                 None if h is None else h.ctypes.data, None if hpre is None else hpre.ctypes.data,
                 None if hbound is None else hbound.ctypes.data, idx.ctypes.data, g.ctypes.data)
-        rc = (self.lib.oracle_forward_mx8(*args, float(gamma)) if mx8
-              else self.lib.oracle_forward(*args))
+        rc = (self.lib.oracle_forward_mx8 if mx8 else self.lib.oracle_forward)(*args, _acc(acc))
         del keep
         if rc != 0:
             raise KeyError("the router selected an expert whose weights were not given")
@@ -219,11 +238,12 @@ class Oracle:
             raise KeyError("a listed expert's weights were not given")
         return sal
 
-    def shared(self, x_bits: np.ndarray, sw: Dict[str, np.ndarray], want_h: bool = False):
+    def shared(self, x_bits: np.ndarray, sw: Dict[str, np.ndarray], want_h: bool = False,
+               acc=None):
         """The shared expert's output y_s [T, H] (double) for bf16 bits x [T, H];
         sw holds w1, w3 [I, H] and w2 [H, I] E4M3 bytes with s1, s3 [I/32, H/32]
         and s2 [H/32, I/32] UE8M0 block scales.  With want_h also h (bf16 bits),
-        hpre and hbound [T, I]."""
+        hpre and hbound [T, I] (hbound under the accumulation model `acc`, as in forward)."""
         x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
         T, H = x_bits.shape
         I = sw["w1"].shape[0]
@@ -237,7 +257,7 @@ class Oracle:
         ptr = lambda a: None if a is None else a.ctypes.data
         self.lib.oracle_shared(T, H, I, x_bits.ctypes.data, *(t[n].ctypes.data for n in
                                ("w1", "s1", "w3", "s3", "w2", "s2")), y.ctypes.data, ptr(h),
-                               ptr(hp), ptr(hb))
+                               ptr(hp), ptr(hb), _acc(acc))
         out = {"y": y}
         if want_h:
             out["h"], out["hpre"], out["hbound"] = h, hp, hb

@@ -36,27 +36,19 @@
 #include <omp.h>
 #endif
 
-/* ORACLE_MUTANT plants one deliberate mistake (tests only: the mutation tests
- * build a copy with -DORACLE_MUTANT=n and check that some pin catches it).
- * The default, 0, is the oracle. */
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-#define MUT(n) (ORACLE_MUTANT == (n))
-
 /* ------------------------------------------------------------------ formats */
 
 /* E2M1 code -> value, from the bit fields of the format. */
 double oracle_e2m1(int code) {
     int s = (code >> 3) & 1, E = (code >> 1) & 3, m = code & 1;
-    double mag = (E == 0) ? (MUT(11) ? 1.0 : 0.5) * m : ldexp(1.0 + 0.5 * m, E - 1);
-    return (s && !MUT(12)) ? -mag : mag;
+    double mag = (E == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, E - 1);
+    return s ? -mag : mag;
 }
 
 /* UE8M0 byte -> scale 2^(e-127); 255 is NaN in the OCP MX format. */
 double oracle_ue8m0(int e) {
     if (e == 255) return NAN;
-    return ldexp(1.0, e - (MUT(3) ? 126 : 127));
+    return ldexp(1.0, e - 127);
 }
 
 /* bf16 bit pattern -> value */
@@ -108,17 +100,17 @@ double oracle_e4m3(int code) {
 
 /* r -> E4M3 code: round to nearest, ties to even, saturate to 448. */
 static int e4m3_code(double r) {
-    int s = (signbit(r) && MUT(15) == 0) ? 1 : 0;
+    int s = signbit(r) ? 1 : 0;
     double a = fabs(r), q;
     if (a >= ldexp(1.0, -6)) {
         int e;
         frexp(a, &e);                          /* a in [2^(e-1), 2^e) */
         double quantum = ldexp(1.0, e - 1 - 3); /* 3 mantissa bits */
-        q = (MUT(16) ? round(a / quantum) : nearbyint(a / quantum)) * quantum;
+        q = nearbyint(a / quantum) * quantum;
     } else {
-        q = (MUT(16) ? round(a / ldexp(1.0, -9)) : nearbyint(a / ldexp(1.0, -9))) * ldexp(1.0, -9);
+        q = nearbyint(a / ldexp(1.0, -9)) * ldexp(1.0, -9);
     }
-    if (q > 448.0 && MUT(14) == 0) q = 448.0;
+    if (q > 448.0) q = 448.0;
     int code;
     if (q == 0.0) {
         code = 0;
@@ -144,7 +136,7 @@ void oracle_mx8_quant(int n, const double *v, uint8_t *codes, uint8_t *scales) {
         if (amax > 0.0) {
             int e;
             frexp(amax, &e);                   /* amax in [2^(e-1), 2^e) */
-            se = (e - 1) - 8 + MUT(13) + 127;
+            se = (e - 1) - 8 + 127;
             if (se < 0) se = 0;
             if (se > 254) se = 254;
         }
@@ -168,14 +160,6 @@ static void mx8_round_trip(int n, double *v) {
 
 /* ------------------------------------------------------------------ weights */
 
-/* Decoded weight element: row r, input column c of a [rows][cols/2] nibble
- * tensor with a [rows][cols/32] scale tensor. */
-static inline double wval(const uint8_t *w, const uint8_t *s, int cols, int r, int c) {
-    uint8_t byte = w[(size_t)r * (cols / 2) + (c >> 1)];
-    int code = ((c & 1) != MUT(1)) ? (byte >> 4) : (byte & 0xF);
-    return oracle_e2m1(code) * oracle_ue8m0(s[(size_t)r * (cols / 32) + (MUT(4) ? 0 : (c >> 5))]);
-}
-
 /* ------------------------------------------------------------------ router */
 
 typedef struct { float v; int e; } okey;
@@ -190,7 +174,6 @@ static int key_cmp(const void *a, const void *b) {
         if (x->v > y->v) return -1;
         if (x->v < y->v) return 1;
     }
-    if (MUT(5)) return (x->e > y->e) ? -1 : (x->e < y->e);
     return (x->e < y->e) ? -1 : (x->e > y->e);
 }
 
@@ -208,8 +191,6 @@ void oracle_route(int T, int E, int k, const float *logits, int32_t *idx, float 
             ex[j] = exp((double)keys[j].v - l0);
             den += ex[j];
         }
-        if (MUT(6))
-            for (int j = k; j < E; ++j) den += exp((double)keys[j].v - l0);
         for (int j = 0; j < k; ++j) gates[(size_t)t * k + j] = (float)(ex[j] / den);
     }
     free(ex);
@@ -230,11 +211,9 @@ void oracle_router_logits(int T, int H, int E, const uint16_t *x, const uint16_t
     for (int t = 0; t < T; ++t)
         for (int e = 0; e < E; ++e) {
             double s = 0.0, a = 0.0;
-            const int n = MUT(17) ? H - 1 : H;
-            for (int c = 0; c < n; ++c) {
+            for (int c = 0; c < H; ++c) {
                 const double xv = oracle_bf16_to_double(x[(size_t)t * H + c]);
-                const double wv = oracle_bf16_to_double(
-                    MUT(18) ? wr[((size_t)c * E + e) % ((size_t)E * H)] : wr[(size_t)e * H + c]);
+                const double wv = oracle_bf16_to_double(wr[(size_t)e * H + c]);
                 s += xv * wv;
                 a += fabs(xv * wv);
             }
@@ -269,18 +248,90 @@ typedef struct {
 
 /* Row r of a matrix with `cols` inputs per row, decoded to doubles:
  * out[c] = E2M1(nibble c of row r) * 2^(scale of group c/32 - 127).
- * Same values as wval(), one scale decode per group of 32. */
+ * The element of row r, input c of a [rows][cols/2] nibble tensor with a
+ * [rows][cols/32] scale tensor. */
 static void decode_row(const uint8_t *w, const uint8_t *s, int cols, int r, double *out) {
     double table[16];
     for (int c = 0; c < 16; ++c) table[c] = oracle_e2m1(c);
     for (int g = 0; g < cols / 32; ++g) {
-        double sc = oracle_ue8m0(s[(size_t)r * (cols / 32) + (MUT(4) ? 0 : g)]);
+        double sc = oracle_ue8m0(s[(size_t)r * (cols / 32) + g]);
         for (int c = 32 * g; c < 32 * g + 32; ++c) {
             uint8_t byte = w[(size_t)r * (cols / 2) + (c >> 1)];
-            int code = ((c & 1) != MUT(1)) ? (byte >> 4) : (byte & 0xF);
+            int code = (c & 1) ? (byte >> 4) : (byte & 0xF);
             out[c] = table[code] * sc;
         }
     }
+}
+
+/* silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z). */
+static double dsilu(double z) {
+    const double s = 1.0 / (1.0 + exp(-z));
+    return s * (1.0 + z * (1.0 - s));
+}
+
+/* How far an fp32 evaluation of h = silu(G) * U can stray from the exact
+ * value, when the evaluation's G' and U' are within dG and dU of G and U
+ * (acc_bound below).  Then
+ *   |silu(G') U' - silu(G) U| <= |silu(G') - silu(G)| |U'| + |silu(G)| |U' - U|
+ *                             <= M dG (|U| + dU) + |silu(G)| dU
+ * with M the largest |silu'| on [G - dG, G + dG] (mean value theorem).
+ * silu' is monotone between its two extremes, at z = +-2.3994 (where
+ * z tanh(z/2) = 2), with values 1.0998 and -0.0998; so M is the larger of
+ * |silu'| at the two ends, or 1.1 (0.1) if the interval reaches the extreme
+ * near +2.4 (-2.4).  The fp32 evaluation of silu(G') U' itself (an
+ * exponential within 2 ulps, a division within 2.5 ulps and three more
+ * roundings) adds a relative 16 u, u = 2^-24, and an fp32 subnormal result an
+ * absolute 2^-149. */
+static double h_bound(double G, double U, double dG, double dU) {
+    const double u32 = ldexp(1.0, -24);
+    const double lo = G - dG, hi = G + dG;
+    double M = fmax(fabs(dsilu(lo)), fabs(dsilu(hi)));
+    if (lo <= 2.41 && hi >= 2.39) M = fmax(M, 1.1);
+    if (lo <= -2.39 && hi >= -2.41) M = fmax(M, 0.1);
+    const double silu = G / (1.0 + exp(-G));
+    const double e = M * dG * (fabs(U) + dU) + fabs(silu) * dU;
+    return e + 16.0 * u32 * (fabs(silu * U) + e) + ldexp(1.0, -149);
+}
+
+/* The accumulation model of the fp32 evaluation that an h bound is for:
+ * an evaluation of a sum S of exact products p_c (c ascending, as the oracle
+ * sums them) is within
+ *     sum * A + prefix * P,   A = sum_c |p_c|,
+ *                             P = sum_{j >= 1} |p_0 + ... + p_{jB-1}|
+ * of S, B = block (P: the magnitudes of the exact partial sums at the block
+ * boundaries jB inside the row).  The plain worst case of any summation order
+ * is sum = gamma_K = K u / (1 - K u), prefix = 0; an evaluation that takes
+ * the inputs in ascending blocks of B, each block through m instructions that
+ * err by at most eps relative to the absolute sum of their terms (the
+ * accumulator included), satisfies sum = (m + 1) e, prefix = m e with
+ * e = eps / (1 - N eps), N instructions in all (the accumulator before an
+ * instruction of block j is at most |P_j| + the block's absolute sum away
+ * from zero). */
+typedef struct {
+    double sum, prefix;
+    int block;
+} oracle_acc;
+
+/* The bound of an evaluation of G (U likewise) under `acc` (NULL, or sum <= 0
+ * with prefix <= 0: gamma_K).  A: sum of |terms|; P: prefix mass as above. */
+static double acc_bound(const oracle_acc *am, int K, double A, double P) {
+    const double u32 = ldexp(1.0, -24);
+    if (!am || (am->sum <= 0.0 && am->prefix <= 0.0)) return K * u32 / (1.0 - K * u32) * A;
+    return am->sum * A + am->prefix * P;
+}
+
+/* Sums of one row: S = sum_c p_c, A = sum_c |p_c| and the prefix mass P for
+ * blocks of B (B <= 0: P = 0), all in ascending c, p_c = x_c * w_c. */
+static void row_sums(int K, const double *x, const double *w, int B, double *S, double *A, double *P) {
+    double s = 0.0, a = 0.0, pm = 0.0;
+    for (int c = 0; c < K; ++c) {
+        if (B > 0 && c > 0 && c % B == 0) pm += fabs(s);
+        s += x[c] * w[c];
+        a += fabs(x[c] * w[c]);
+    }
+    *S = s;
+    *A = a;
+    *P = pm;
 }
 
 /* One token through one expert.
@@ -288,15 +339,13 @@ static void decode_row(const uint8_t *w, const uint8_t *s, int cols, int r, doub
  *   h_n = bf16(silu(G_n) * U_n)                                    (one rounding)
  *   Y_m = sum_n h_n W2[m][n]                                       (double)
  * Sums run over ascending c (resp. n).  hpre (optional) receives silu(G)*U
- * before rounding.  hbound (optional) receives a first-order bound on how far
- * an fp32 evaluation of silu(G)*U can stray from it when G and U are sums of
- * H fp32 products accumulated in any order (Higham's gamma_H times the sum of
- * absolute products), plus 8 fp32 ulps for the epilogue. */
+ * before rounding.  hbound (optional) receives h_bound() of each element, G
+ * and U evaluated under the accumulation model `acc` (see oracle_acc). */
 static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const uint8_t *s1,
                        const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
-                       int mx8, double gamma, uint16_t *h, double *hpre, double *hbound, double *Y) {
-    const double u32 = ldexp(1.0, -24);
-    const double gam = gamma > 0.0 ? gamma : H * u32 / (1.0 - H * u32);
+                       int mx8, const oracle_acc *am, uint16_t *h, double *hpre, double *hbound,
+                       double *Y) {
+    const int B = am ? am->block : 0;
     double *hv = (double *)malloc(sizeof(double) * (size_t)I);
     #pragma omp parallel
     {
@@ -306,22 +355,14 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
         for (int n = 0; n < I; ++n) {
             decode_row(w1, s1, H, n, r1);
             decode_row(w3, s3, H, n, r3);
-            double G = 0.0, U = 0.0, Ga = 0.0, Ua = 0.0;
-            for (int c = 0; c < H - MUT(10); ++c) {
-                G += x[c] * r1[c];
-                U += x[c] * r3[c];
-                Ga += fabs(x[c] * r1[c]);
-                Ua += fabs(x[c] * r3[c]);
-            }
-            double a = MUT(2) ? U / (1.0 + exp(-U)) * G : G / (1.0 + exp(-G)) * U;
+            double G, U, Ga, Ua, Gp, Up;
+            row_sums(H, x, r1, B, &G, &Ga, &Gp);
+            row_sums(H, x, r3, B, &U, &Ua, &Up);
+            double a = G / (1.0 + exp(-G)) * U;
             if (hpre) hpre[n] = a;
-            if (hbound) {
-                double sg = 1.0 / (1.0 + exp(-G));
-                double dsilu = sg * (1.0 + G * (1.0 - sg));
-                hbound[n] = fabs(dsilu * U) * gam * Ga + fabs(G * sg) * gam * Ua + 8.0 * u32 * fabs(a);
-            }
+            if (hbound) hbound[n] = h_bound(G, U, acc_bound(am, H, Ga, Gp), acc_bound(am, H, Ua, Up));
             h[n] = oracle_double_to_bf16(a);
-            hv[n] = MUT(9) ? a : oracle_bf16_to_double(h[n]);
+            hv[n] = oracle_bf16_to_double(h[n]);
         }
         free(r3);
         free(r1);
@@ -333,12 +374,8 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
         #pragma omp for schedule(static)
         for (int m = 0; m < H; ++m) {
             double acc = 0.0;
-            if (MUT(8)) {
-                for (int n = 0; n < I; ++n) acc += hv[n] * wval(w2, s2, H, n, m);
-            } else {
-                decode_row(w2, s2, I, m, r2);
-                for (int n = 0; n < I; ++n) acc += hv[n] * r2[n];
-            }
+            decode_row(w2, s2, I, m, r2);
+            for (int n = 0; n < I; ++n) acc += hv[n] * r2[n];
             Y[m] = acc;
         }
         free(r2);
@@ -358,7 +395,7 @@ static void expert_ffn(int H, int I, const double *x, const uint8_t *w1, const u
 static int forward_impl(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
                         const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
                         uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
-                        float *gates_out, int mx8, double gamma) {
+                        float *gates_out, int mx8, const oracle_acc *am) {
     int P = T * k;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
     float *g = (float *)malloc(sizeof(float) * (size_t)P);
@@ -385,12 +422,12 @@ static int forward_impl(int T, int H, int I, int E, int k, const uint16_t *x, co
                 break;
             }
             expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], mx8,
-                       gamma, h, hp, hbound ? hb : NULL, Y);
+                       am, h, hp, hbound ? hb : NULL, Y);
             size_t p = (size_t)t * k + j;
             if (h_out) memcpy(h_out + p * I, h, sizeof(uint16_t) * (size_t)I);
             if (hpre) memcpy(hpre + p * I, hp, sizeof(double) * (size_t)I);
             if (hbound) memcpy(hbound + p * I, hb, sizeof(double) * (size_t)I);
-            double gj = MUT(7) ? 1.0 : (double)g[p];
+            double gj = (double)g[p];
             for (int m = 0; m < H; ++m) acc[m] += gj * Y[m];
         }
         for (int m = 0; m < H; ++m) y[(size_t)i * H + m] = (float)acc[m];
@@ -399,24 +436,25 @@ static int forward_impl(int T, int H, int I, int E, int k, const uint16_t *x, co
     return rc;
 }
 
+/* The layer.  hbound (optional) bounds an evaluation of G and U under the
+ * accumulation model `acc` (NULL: gamma_H, see oracle_acc). */
 int oracle_forward(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
                    const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
                    uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
-                   float *gates_out) {
+                   float *gates_out, const oracle_acc *am) {
     return forward_impl(T, H, I, E, k, x, logits, W, n_tok, tok, y, h_out, hpre, hbound, idx_out,
-                        gates_out, 0, 0.0);
+                        gates_out, 0, am);
 }
 
 /* The MXFP8 mode: as oracle_forward, with x quantised to MXFP8 along H before
- * w1/w3 and the bf16 h quantised to MXFP8 along I before w2.  hbound uses
- * `gamma` as the relative accumulation bound of G and U (the summation error
- * is at most gamma times the sum of absolute products). */
+ * w1/w3 and the bf16 h quantised to MXFP8 along I before w2.  hbound as in
+ * oracle_forward. */
 int oracle_forward_mx8(int T, int H, int I, int E, int k, const uint16_t *x, const float *logits,
                        const oracle_weights *W, int n_tok, const int32_t *tok, float *y,
                        uint16_t *h_out, double *hpre, double *hbound, int32_t *idx_out,
-                       float *gates_out, double gamma) {
+                       float *gates_out, const oracle_acc *am) {
     return forward_impl(T, H, I, E, k, x, logits, W, n_tok, tok, y, h_out, hpre, hbound, idx_out,
-                        gates_out, 1, gamma);
+                        gates_out, 1, am);
 }
 
 /* Expert saliency, the pruning signal of the 10100.com page (section on
@@ -452,10 +490,10 @@ int oracle_saliency(int T, int H, int I, int E, int k, const uint16_t *x, const 
             for (int c = 0; c < H; ++c) xd[c] = oracle_bf16_to_double(x[(size_t)t * H + c]);
             if (mx8) mx8_round_trip(H, xd);
             expert_ffn(H, I, xd, W->w1[e], W->s1[e], W->w3[e], W->s3[e], W->w2[e], W->s2[e], mx8,
-                       0.0, h, hp, NULL, Y);
+                       NULL, h, hp, NULL, Y);
             double ss = 0.0;
-            for (int m = 0; m < H - MUT(19); ++m) ss += Y[m] * Y[m];
-            sal[i] += (MUT(20) ? 1.0 : (double)g[p]) * sqrt(ss);
+            for (int m = 0; m < H; ++m) ss += Y[m] * Y[m];
+            sal[i] += (double)g[p] * sqrt(ss);
         }
     }
     free(hp); free(h); free(Y); free(xd); free(g); free(idx);
@@ -472,43 +510,51 @@ int oracle_saliency(int T, int H, int I, int E, int k, const uint16_t *x, const 
  *   W2[m][n] = E4M3(w2[m][n]) * 2^(s2[m/32][n/32] - 127)   w2 [H][I], s2 [H/32][I/32]
  * h = bf16(silu(W1 x) * (W3 x)) rounded once, y_s = W2 h, added to the
  * layer's output without a gate.  y [T][H] double; h, hpre, hbound [T][I]
- * optional, as in expert_ffn. */
+ * optional, as in expert_ffn, hbound under the accumulation model `acc`
+ * (NULL: gamma_H). */
 static double fp8w(const uint8_t *w, const uint8_t *s, int cols, int r, int c) {
-    const int si = MUT(21) ? (c / 32) * (cols / 32) + r / 32 : (r / 32) * (cols / 32) + c / 32;
+    const int si = (r / 32) * (cols / 32) + c / 32;
     return oracle_e4m3(w[(size_t)r * cols + c]) * oracle_ue8m0(s[si]);
 }
 
 void oracle_shared(int T, int H, int I, const uint16_t *x, const uint8_t *w1, const uint8_t *s1,
                    const uint8_t *w3, const uint8_t *s3, const uint8_t *w2, const uint8_t *s2,
-                   double *y, uint16_t *h_out, double *hpre, double *hbound) {
-    const double u32 = ldexp(1.0, -24), gam = H * u32 / (1.0 - H * u32);
+                   double *y, uint16_t *h_out, double *hpre, double *hbound, const oracle_acc *am) {
+    const int B = am ? am->block : 0;
     for (int t = 0; t < T; ++t) {
         double *hv = (double *)malloc(sizeof(double) * (size_t)I);
-        #pragma omp parallel for schedule(static)
+        #pragma omp parallel
+        {
+        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+        double *r1 = (double *)malloc(sizeof(double) * (size_t)H);
+        double *r3 = (double *)malloc(sizeof(double) * (size_t)H);
+        for (int c = 0; c < H; ++c) xr[c] = oracle_bf16_to_double(x[(size_t)t * H + c]);
+        #pragma omp for schedule(static)
         for (int n = 0; n < I; ++n) {
-            double G = 0.0, U = 0.0, Ga = 0.0, Ua = 0.0;
             for (int c = 0; c < H; ++c) {
-                const double xv = oracle_bf16_to_double(x[(size_t)t * H + c]);
-                const double a1 = xv * fp8w(w1, s1, H, n, c), a3 = xv * fp8w(w3, s3, H, n, c);
-                G += a1; U += a3; Ga += fabs(a1); Ua += fabs(a3);
+                r1[c] = fp8w(w1, s1, H, n, c);
+                r3[c] = fp8w(w3, s3, H, n, c);
             }
+            double G, U, Ga, Ua, Gp, Up;
+            row_sums(H, xr, r1, B, &G, &Ga, &Gp);
+            row_sums(H, xr, r3, B, &U, &Ua, &Up);
             const double a = G / (1.0 + exp(-G)) * U;
             const size_t o = (size_t)t * I + n;
             if (hpre) hpre[o] = a;
-            if (hbound) {
-                const double sg = 1.0 / (1.0 + exp(-G));
-                const double dsilu = sg * (1.0 + G * (1.0 - sg));
-                hbound[o] = fabs(dsilu * U) * gam * Ga + fabs(G * sg) * gam * Ua + 8.0 * u32 * fabs(a);
-            }
+            if (hbound) hbound[o] = h_bound(G, U, acc_bound(am, H, Ga, Gp), acc_bound(am, H, Ua, Up));
             const uint16_t hb = oracle_double_to_bf16(a);
             if (h_out) h_out[o] = hb;
             hv[n] = oracle_bf16_to_double(hb);
+        }
+        free(r3);
+        free(r1);
+        free(xr);
         }
         #pragma omp parallel for schedule(static)
         for (int m = 0; m < H; ++m) {
             double acc = 0.0;
             for (int n = 0; n < I; ++n)
-                acc += hv[n] * (MUT(22) ? fp8w(w2, s2, I, n % H, m % I) : fp8w(w2, s2, I, m, n));
+                acc += hv[n] * fp8w(w2, s2, I, m, n);
             y[(size_t)t * H + m] = acc;
         }
         free(hv);
@@ -532,7 +578,7 @@ int oracle_stack_layer(int T, int H, int I, int E, int k, float *x, const float 
     uint16_t *u = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)T * H);
     float *y = (float *)malloc(sizeof(float) * (size_t)T * H);
     oracle_prenorm(T, H, x, 1e-6, u);
-    int rc = oracle_forward(T, H, I, E, k, u, logits, W, T, NULL, y, NULL, NULL, NULL, NULL, NULL);
+    int rc = oracle_forward(T, H, I, E, k, u, logits, W, T, NULL, y, NULL, NULL, NULL, NULL, NULL, NULL);
     if (rc == 0)
         for (size_t i = 0; i < (size_t)T * H; ++i) x[i] = (float)((double)x[i] + (double)y[i]);
     free(y);
@@ -546,5 +592,14 @@ int oracle_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Set the threads of the oracle's parallel loops (n >= 1). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

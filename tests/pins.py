@@ -566,3 +566,194 @@ ALL_PINS = [pin_e2m1_table, pin_ue8m0, pin_bf16_rounding, pin_router_vs_sort, pi
             pin_brute, pin_numpy_matmul, pin_e4m3_table, pin_mx8_quant, pin_mx8_special,
             pin_mx8_forward, pin_router_numpy, pin_router_onehot, pin_router_bound,
             pin_saliency_single, pin_saliency_numpy, pin_shared_numpy]
+
+
+# ---------------------------------------------------------------- h bound and the stack layer
+def _f32_bf16_bits(v32):
+    """float32 -> bf16 bit patterns, round to nearest, ties to even."""
+    u = np.asarray(v32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _h32(G32, U32):
+    """An fp32 evaluation's h: silu(G') U' from the fp32 sums, rounded once to
+    fp32 (then to bf16).  One rounding after exact arithmetic is within the
+    bound's allowance for the epilogue."""
+    G, U = np.asarray(G32, np.float64), np.asarray(U32, np.float64)
+    return _f32_bf16_bits((G / (1.0 + np.exp(-G)) * U).astype(np.float32))
+
+
+def _in_interval(o, hbits, hpre, hbound):
+    """Indices where the bf16 value hbits is outside [bf16(hpre - b), bf16(hpre + b)]."""
+    lo = bf16_to_f64(np.array([o.to_bf16(v) for v in (hpre - hbound).ravel()], np.uint16))
+    hi = bf16_to_f64(np.array([o.to_bf16(v) for v in (hpre + hbound).ravel()], np.uint16))
+    got = bf16_to_f64(hbits.ravel())
+    return np.nonzero((got < lo) | (got > hi))[0]
+
+
+def _f32_sum(terms, order):
+    """fp32 evaluation of sum(terms) (exact float64 products, last axis) in a
+    given order: 'forward' / 'reverse' one by one, 'pairwise' (numpy's float32
+    sum), 'sorted' by decreasing magnitude, 'lanes' (lane l of 64 chains its
+    32-input groups l, l + 64, ... one product at a time, then a 6-level tree of
+    the 64 lane sums, as a wave's DPP reduction), 'blocks' (the inputs in
+    ascending groups of 32 whose exact sum is added to an fp32 accumulator with
+    one rounding, as an MFMA instruction at best)."""
+    t = np.asarray(terms, np.float64)
+    t32 = t.astype(np.float32)
+    assert np.array_equal(t32.astype(np.float64), t)          # products exact in fp32
+    if order == "forward":
+        return np.add.accumulate(t32, axis=-1)[..., -1]
+    if order == "reverse":
+        return np.add.accumulate(t32[..., ::-1], axis=-1)[..., -1]
+    if order == "pairwise":
+        return t32.sum(axis=-1, dtype=np.float32)
+    if order == "sorted":
+        idx = np.argsort(-np.abs(t), axis=-1, kind="stable")
+        return np.add.accumulate(np.take_along_axis(t32, idx, -1), axis=-1)[..., -1]
+    K = t.shape[-1]
+    if order == "lanes":
+        G = K // 32
+        lanes = np.zeros(t.shape[:-1] + (64,), np.float32)
+        for g in range(G):
+            for j in range(32):
+                lanes[..., g % 64] = lanes[..., g % 64] + t32[..., 32 * g + j]
+        while lanes.shape[-1] > 1:
+            lanes = lanes[..., 0::2] + lanes[..., 1::2]
+        return lanes[..., 0]
+    if order == "blocks":
+        acc = np.zeros(t.shape[:-1], np.float32)
+        for g in range(0, K, 32):
+            acc = (acc.astype(np.float64) + t[..., g:g + 32].sum(-1)).astype(np.float32)
+        return acc
+    raise ValueError(order)
+
+
+_U24 = 2.0 ** -24
+
+
+def _acc_worst(D):
+    return (D * _U24 / (1 - D * _U24), 0.0, 0)
+
+
+def _acc_blocks(K):
+    """The 'blocks' order: N = K/32 additions, each within u of its terms'
+    absolute sum; four of them per 128-input block."""
+    e = _U24 / (1 - (K // 32) * _U24)
+    return (5 * e, 4 * e, 128)
+
+
+def pin_hbound_sound(o):
+    """Soundness of the oracle's h bound: fp32 evaluations of G and U in several
+    summation orders, then h rounded to bf16, must lie in [bf16(hpre - b),
+    bf16(hpre + b)] with b the oracle's bound for that order's accumulation
+    model (gamma_K for any order; the lane-tree depth for 'lanes'; the blocked
+    model for 'blocks').  Random rows at H = 2048, half of them with U made
+    small by cancellation, so that both terms of the bound matter."""
+    rng = np.random.default_rng(91)
+    H, I, T = 2048, 48, 3
+    ex = random_expert(rng, H, I)
+    x = rand_bf16(rng, (T, H))
+    W1, W3 = _dequant(ex["w1"], ex["s1"]), _dequant(ex["w3"], ex["s3"])
+    xd = bf16_to_f64(x)
+    P1 = xd[:, None, :] * W1[None]          # [T, I, H] exact products
+    P3 = xd[:, None, :] * W3[None]
+    models = {"forward": None, "reverse": None, "pairwise": None, "sorted": None,
+              "lanes": _acc_worst(32 * (H // 2048) + 6), "blocks": _acc_blocks(H)}
+    for order, acc in models.items():
+        out = o.forward(H, I, 1, 1, x, np.zeros((T, 1), np.float32), {0: ex}, want_h=True, acc=acc)
+        h32 = _h32(_f32_sum(P1, order), _f32_sum(P3, order))
+        bad = _in_interval(o, h32, out["hpre"], out["hbound"])
+        assert bad.size == 0, (order, bad[:4])
+
+
+def _adversarial_rows(K, T):
+    """Rows on which fp32 summation errs by almost the worst case.  Token t has
+    x_0 = 1 + t/128 and x_c = a = 2^-24 (1 + 2^-7) for c > 0: each added a
+    exceeds half an ulp of a running sum in [1, 2), so every addition rounds up
+    by almost u.  x2 is x with x_{K-32} = 1.
+      row 0 (x):  W1 all 1, W3 = 1 at input 0 only  -> G adversarial, U = x_0
+      row 1 (x):  W1 = 1 at input 0 only, W3 all 1  -> U adversarial, G = x_0
+      row 2 (x2): W1 = 1 at the first input of every 32-input group, -1 at the
+                  group starting at K - 32; W3 as row 0.  Summed in 32-input
+                  groups, each group after the first rounds up by almost u and
+                  the last one cancels the 1: the accumulated error is of the
+                  order of G itself
+      row 3 (x2): W1 as row 1; W3 all 1 except -1 at K - 32: U summed one by one
+                  errs by almost (K - 33) u and then cancels to t/128 + (K-2) a,
+                  so the error is large against U and against the G term of the
+                  bound.
+    Returns the expert, x and x2."""
+    ex = const_expert(K, 32, 0, 0, 0)
+    ex["w1"][0, :] = 0x22
+    set_nibble(ex["w3"], 0, 0, 2)
+    set_nibble(ex["w1"], 1, 0, 2)
+    ex["w3"][1, :] = 0x22
+    for c in range(0, K, 32):
+        set_nibble(ex["w1"], 2, c, 10 if c == K - 32 else 2)
+    set_nibble(ex["w3"], 2, 0, 2)
+    set_nibble(ex["w1"], 3, 0, 2)
+    ex["w3"][3, :] = 0x22
+    set_nibble(ex["w3"], 3, K - 32, 10)
+    x = np.full((T, K), bf16_bits(2.0 ** -24 * (1 + 2.0 ** -7)), np.uint16)
+    x[:, 0] = [bf16_bits(1.0 + t / 128.0) for t in range(T)]
+    x2 = x.copy()
+    x2[:, K - 32] = bf16_bits(1.0)
+    return ex, x, x2
+
+
+def pin_hbound_adversarial(o):
+    """The bound is tight where fp32 summation is at its worst.  Summed one by
+    one, rows 0 and 1 stray by more than 99% of gamma_K * sum|p|, and row 3 by
+    nearly as much and then cancels; summed in 32-input groups, row 2 strays by
+    about (K/32) u, which only the prefix term of the blocked model covers.  h
+    crosses bf16 rounding boundaries for some tokens in each case, and every h
+    must still be inside the oracle's interval: a bound that dropped the G or
+    the U term, the prefix mass, or used a shorter gamma fails here."""
+    K, T = 5120, 116
+    ex, x, x2 = _adversarial_rows(K, T)
+    W1, W3 = _dequant(ex["w1"], ex["s1"]), _dequant(ex["w3"], ex["s3"])
+    lg = np.zeros((T, 1), np.float32)
+    worst = 0.99 * (K - 1) * _U24 * (1 - 2.0 ** -7)
+    for order, acc, xb, rows in (("forward", None, x, (0, 1)), ("forward", None, x2, (3,)),
+                                 ("blocks", _acc_blocks(K), x2, (2,))):
+        xd = bf16_to_f64(xb)
+        P1, P3 = xd[:, None, :] * W1[None], xd[:, None, :] * W3[None]
+        out = o.forward(K, 32, 1, 1, xb, lg, {0: ex}, want_h=True, acc=acc)
+        G32, U32 = _f32_sum(P1, order), _f32_sum(P3, order)
+        h32 = _h32(G32, U32)
+        hpre, hb = out["hpre"].reshape(T, 32), out["hbound"].reshape(T, 32)
+        for r in rows:
+            if r in (0, 1):   # the evaluation is nearly the worst case
+                S, S32 = (P1[:, r].sum(-1), G32[:, r]) if r == 0 else (P3[:, r].sum(-1), U32[:, r])
+                assert np.all(np.abs(S32 - S) > worst), (r, np.abs(S32 - S).min())
+            crossed = _f32_bf16_bits(hpre[:, r].astype(np.float32)) != h32[:, r]
+            assert crossed.any(), (order, r)    # the rows have teeth
+            bad = _in_interval(o, h32[:, r], hpre[:, r], hb[:, r])
+            assert bad.size == 0, (order, r, bad[:4])
+
+
+def pin_stack_layer(o):
+    """One layer of the residual stack in closed form.  x rows are constant
+    (3/16 and 3/4), so the pre-norm gives u = bf16(x / sqrt(x^2 + 1e-6)) = 1
+    everywhere; with the constant experts of pin_closed_form_swiglu (H = 64,
+    I = 32): expert 0 has G = 64, U = 32, h = 2048, Y0 = 32 * 2048 / 4 = 16384;
+    expert 1 has G = 32, U = -64, h = bf16(-2048 / (1 + e^-32)) = -2048,
+    Y1 = 32 * -2048 * 2 = -131072.  The layer's output is
+    x + (g0 * Y0 + g1 * Y1), each sum stored as fp32."""
+    H, I = 64, 32
+    e0 = const_expert(H, I, 2, 1, 2, s2=125)
+    e1 = const_expert(H, I, 1, 10, 4)
+    x = np.array([[0.1875] * H, [0.75] * H], np.float32)
+    assert np.all(o.prenorm(x) == bf16_bits(1.0))
+    lg = np.array([[0.3, -0.2], [-1.0, 0.5]], np.float32)
+    out = o.stack_layer(I, 2, 2, x, lg, {0: e0, 1: e1})
+    idx, g = o.route(lg, 2)
+    for t in range(2):
+        Y = {0: 16384.0, 1: -131072.0}
+        y = f32(sum(float(g[t, j]) * Y[int(idx[t, j])] for j in range(2)))
+        want = f32(float(x[t, 0]) + y)
+        assert np.all(out[t] == np.float32(want)), (t, out[t][:2], want)
+
+
+ALL_PINS += [pin_hbound_sound, pin_hbound_adversarial, pin_stack_layer]
