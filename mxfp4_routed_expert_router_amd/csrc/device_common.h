@@ -13,10 +13,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// UE8M0 scale byte -> fp32 2^(e-127).  Exact for e in [1, 254]; the library
-// supports e in [2, 252] so that every scaled E2M1 value is a normal number.
+// UE8M0 scale byte -> fp32 2^(e-127): byte 0 is 2^-127 (an fp32 subnormal)
+// and 255 is NaN, as in the OCP MX format.  The library supports e in
+// [2, 252], where every scaled E2M1 value is a normal number.
 __device__ __forceinline__ float ue8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e << 23);
+  const uint32_t b = e == 0u ? 0x00400000u : e == 255u ? 0x7FC00000u : e << 23;
+  return __uint_as_float(b);
 }
 
 // Eight E2M1 codes packed in one dword (code 2i in the low nibble of byte i,

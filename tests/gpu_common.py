@@ -33,7 +33,7 @@ def dev_weights(host: dict):
                                         for n, a in host.items()})
 
 
-def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "", max_abs_rms: float = MAX_ABS_RMS):
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
@@ -45,7 +45,7 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = ""):
     mx = np.max(np.abs(d)) if d.size else 0.0
     say(f"  {what}: rel_l2={rel:.3e} max_abs/rms={mx / rms if rms else mx:.3e}")
     assert rel <= REL_L2, (what, rel)
-    assert mx <= MAX_ABS_RMS * rms, (what, mx, rms)
+    assert mx <= max_abs_rms * rms, (what, mx, rms)
     return rel
 
 
@@ -53,20 +53,44 @@ def bf16_value(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _bf16_order(bits):
+    """bf16 bit patterns -> integers in value order (adjacent values differ by 1)."""
+    b = np.asarray(bits, np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def _bf16_rne_stats(v):
+    """Round doubles to bf16 bit patterns (nearest, ties to even), for the
+    interval-width statistics only; the pass/fail decision uses the oracle's
+    own rounding."""
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def check_h(h_gpu: np.ndarray, h_ref: np.ndarray, hpre: np.ndarray, hbound: np.ndarray,
             what: str = ""):
-    """h is rounded to bf16 at the same point on both sides.  The GPU evaluates
-    silu(G)*U in fp32 from fp32 sums, so its value before rounding lies within
-    the oracle's bound b of the exact value hpre; rounding to nearest is
-    monotone, so the GPU's h must lie between bf16(hpre - b) and bf16(hpre + b).
-    Where that interval holds one bf16 value the GPU must match the oracle
-    exactly.  This is an exact rule, not a tolerance on a count."""
+    """h is rounded to bf16 at the same point on both sides.  The kernel's value
+    before rounding lies within the oracle's bound b of the exact value hpre
+    (b from the accumulation model of the kernel family that ran: tests/accum.py),
+    and rounding to nearest is monotone, so the GPU's h must lie between
+    bf16(hpre - b) and bf16(hpre + b).  Where that interval holds one bf16
+    value the GPU must match the oracle exactly, where it holds two, the GPU may
+    take the adjacent value.  An exact rule, not a tolerance on a count.
+    Prints the mismatch count, the largest distance in bf16 steps and the
+    interval widths."""
     import oracle
     h_gpu = np.asarray(h_gpu, np.uint16)
     h_ref = np.asarray(h_ref, np.uint16)
     bad = np.nonzero(h_gpu != h_ref)
     n = len(bad[0])
-    say(f"  {what}: h mismatches {n} of {h_ref.size}")
+    dist = np.abs(_bf16_order(h_gpu) - _bf16_order(h_ref))
+    width = _bf16_order(_bf16_rne_stats(hpre + hbound)) - _bf16_order(_bf16_rne_stats(hpre - hbound)) + 1
+    say(f"  {what}: h mismatches {n} of {h_ref.size} (largest {int(dist.max()) if dist.size else 0} "
+        f"bf16 steps); interval width median {np.median(width):.0f}, p90 "
+        f"{np.percentile(width, 90):.0f}, p99 {np.percentile(width, 99):.0f} values")
     if n == 0:
         return
     o = oracle.get()

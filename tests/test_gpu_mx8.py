@@ -3,24 +3,27 @@ scaled MFMA) against the oracle's MXFP8 forward.
 
 The quantiser is compared bit for bit.  x is quantised identically on both
 sides, so G and U differ only by accumulation: the scaled FP4 x FP8 matrix
-instruction sums its 128 products with less than fp32 precision (measured on
-MI355X: at most 2^-13.5 of the block's sum of absolute products), so the h
-check takes the oracle's first-order bound with gamma = 2^-12 in place of the
-fp32 summation bound.  y is held to the bf16 path's tolerances against the w2
-stage applied to the GPU's own h (the FP8 codes of h are a discrete decision,
-taken from the same input on both sides), and to its rel-L2 bound end to end."""
+instruction sums its 128 products with much less than fp32 precision (the
+probes of test_gpu_accum.py measure up to 2^-11.85 of its terms' absolute
+sum), and the h check takes the accumulation model of that instruction
+(tests/accum.py, family mx8): its intervals are wide because the hardware's
+sums are.  y is held end to end against the oracle's MXFP8 forward to the
+layer's rel-L2 <= 2e-3 and to max |error| <= 5e-2 * RMS: the same scaled
+instruction sums w2's products with about 12 bits, and the FP8 codes of h are
+decisions taken from a bf16 h that may lie a step from the oracle's, so single
+elements of y move by up to about 2e-2 * RMS (measured 2.07e-2 at T=70,
+H=256, I=128, k=4), beyond the bf16 path's 2e-2."""
+MX_MAX_ABS_RMS = 5e-2
 import numpy as np
 import pytest
 
+import accum
 import pins
 import synth
 from synth.configs import PREFILL
 from gpu_common import check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
 
 pytestmark = pytest.mark.gpu
-
-GAMMA_MX = 2.0 ** -12
-
 
 @pytest.fixture(scope="module")
 def moe():
@@ -63,44 +66,13 @@ def test_quant_mxfp8_bitexact(moe, orc, rows, K):
     assert bad.size == 0, [(tuple(b), int(c[tuple(b)]), int(ref_c[tuple(b)])) for b in bad[:8]]
 
 
-def _y_from_h(orc, experts, idx, gates, h_bits, tokens):
-    """y of the listed tokens from a given bf16 h (pair order): each pair's h is
-    quantised to MXFP8 by the oracle's quantiser, then W2 (float64) and the
-    gate-weighted sum.  Used to compare y on the GPU's own h: where the GPU's h
-    lies one bf16 ulp from the oracle's (allowed by the h check), the block's
-    FP8 codes may differ, and that discrete decision must be taken from the same
-    input on both sides."""
-    k = idx.shape[1]
-    tab = np.array([orc.e4m3(c) for c in range(256)])
-    out = []
-    for t in tokens:
-        acc = np.zeros(experts[int(idx[t, 0])]["w2"].shape[0])
-        for j in range(k):
-            e = int(idx[t, j])
-            hv = pins.bf16_to_f64(h_bits[t * k + j])
-            c, sc = orc.mx8_quant(hv)
-            hq = tab[c] * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32)
-            acc += float(gates[t, j]) * (pins._dequant(experts[e]["w2"], experts[e]["s2"]) @ hq)
-        out.append(acc)
-    return np.array(out)
-
-
-def _check_y_mx(y_gpu, y_ref, y_on_gpu_h, what):
-    """Full tolerance against y from the GPU's own h; rel-L2 end to end."""
-    check_y(y_gpu, y_on_gpu_h, what + " (on the GPU's h)")
-    d = np.asarray(y_gpu, np.float64) - np.asarray(y_ref, np.float64)
-    rel = np.linalg.norm(d) / np.linalg.norm(np.asarray(y_ref, np.float64))
-    say(f"  {what}: end-to-end rel_l2={rel:.3e}")
-    assert rel <= 2e-3, (what, rel)
-
-
 def _forward_mx(moe, orc, T, H, I, E, k, seed):
     import torch
     rng = np.random.default_rng(seed)
     experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
     x = pins.rand_bf16(rng, (T, H))
     lg = rng.standard_normal((T, E)).astype(np.float32)
-    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True, mx8=True, gamma=GAMMA_MX)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True, mx8=True, acc=accum.model("mx8", H))
     dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
     w = dev_weights(dense)
     y, h, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k,
@@ -110,8 +82,7 @@ def _forward_mx(moe, orc, T, H, I, E, k, seed):
     check_route(route, ref["idx"], ref["gates"], orc.permute(ref["idx"], E), what)
     hb = host_bits(h)
     check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what)
-    _check_y_mx(y.cpu().numpy(), ref["y"],
-                _y_from_h(orc, experts, ref["idx"], ref["gates"], hb, range(T)), what)
+    check_y(y.cpu().numpy(), ref["y"], what, MX_MAX_ABS_RMS)
     return x, lg, w, y
 
 
@@ -151,7 +122,7 @@ def test_mxfp8_differs_from_bf16_by_quantisation(moe, orc):
 
 def test_prefill_chunk_mxfp8(moe, orc):
     """T=2048 at the full shape in the MXFP8 mode: routing bit-exact, x quantised
-    bit-exact, y and h on 16 sampled tokens."""
+    bit-exact, h and y of every token against the oracle's MXFP8 forward."""
     import torch
     wl = PREFILL
     say("MXFP8 prefill T=2048: generating the 384-expert layer")
@@ -162,20 +133,17 @@ def test_prefill_chunk_mxfp8(moe, orc):
                                             mode=moe.MODE_PREFILL_MXFP8)
     codes, scales = moe.moe_fp4_quant_mxfp8(dev_bits(x))
     torch.cuda.synchronize()
-    idx, g = orc.route(lg, wl.k)
-    check_route(route, idx, g, orc.permute(idx, wl.E), "MXFP8 prefill route")
-    rng = np.random.default_rng(2049)
-    toks = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 14, replace=False)]))
-    rc, rs = orc.mx8_quant(pins.bf16_to_f64(x[toks]))
-    assert np.array_equal(codes.cpu().numpy()[toks], rc) and np.array_equal(scales.cpu().numpy()[toks], rs)
-    experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in np.unique(idx[toks])}
-    ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, experts, tokens=toks, want_h=True, mx8=True,
-                      gamma=GAMMA_MX)
     y = y.cpu().numpy()
     h = host_bits(h)
-    pairs = (toks[:, None] * wl.k + np.arange(wl.k)[None, :]).ravel()
-    check_h(h[pairs], ref["h"][pairs], ref["hpre"][pairs], ref["hbound"][pairs], "MXFP8 prefill sampled h")
-    _check_y_mx(y[toks], ref["y"], _y_from_h(orc, experts, idx, g, h, toks), "MXFP8 prefill sampled y")
-    assert np.all(np.isfinite(y))
     del w
     torch.cuda.empty_cache()
+    idx, g = orc.route(lg, wl.k)
+    check_route(route, idx, g, orc.permute(idx, wl.E), "MXFP8 prefill route")
+    rc, rs = orc.mx8_quant(pins.bf16_to_f64(x))
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+    say(f"  oracle on all {wl.T} tokens")
+    experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in np.unique(idx)}
+    ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, experts, want_h=True, mx8=True,
+                      acc=accum.model("mx8", wl.H))
+    check_h(h, ref["h"], ref["hpre"], ref["hbound"], "MXFP8 prefill h, all tokens")
+    check_y(y, ref["y"], "MXFP8 prefill y, all tokens", MX_MAX_ABS_RMS)

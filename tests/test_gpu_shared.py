@@ -7,6 +7,7 @@ exact value and fp32 evaluation bound); y to the layer's tolerances (rel-L2
 import numpy as np
 import pytest
 
+import accum
 import pins
 import synth
 from synth.configs import DECODE
@@ -53,7 +54,7 @@ def test_shared_expert(moe, orc, T, H, I):
     y2, _ = moe.moe_fp4_shared_expert(xd, dsw)
     ya, _ = moe.moe_fp4_shared_expert(xd, dsw, y=torch.from_numpy(y0).cuda(), accumulate=True)
     torch.cuda.synchronize()
-    ref = orc.shared(x, sw, want_h=True)
+    ref = orc.shared(x, sw, want_h=True, acc=accum.shared_model(T, H))
     what = f"shared T={T} H={H} I={I}"
     check_h(host_bits(h), ref["h"], ref["hpre"], ref["hbound"], what)
     y = y.cpu().numpy()

@@ -3,8 +3,9 @@ element, through the C-ABI.  Shapes span several tiles and ragged tails."""
 import numpy as np
 import pytest
 
+import accum
 import pins
-from gpu_common import check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
+from gpu_common import bf16_value, check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
 
 pytestmark = pytest.mark.gpu
 
@@ -142,7 +143,8 @@ def _forward_case(moe, orc, T, H, I, E, k, seed, mode, scale_lo=120, scale_hi=12
     experts = {e: pins.random_expert(rng, H, I, scale_lo, scale_hi) for e in range(E)}
     x = pins.rand_bf16(rng, (T, H))
     lg = rng.standard_normal((T, E)).astype(np.float32)
-    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True,
+                      acc=accum.forward_model(T, H, I, E, k, mode))
     dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
     w = dev_weights(dense)
     y0 = None
@@ -237,7 +239,8 @@ def test_probes(moe, orc, mode):
         x[0, c0] = pins.bf16_bits(1.5)
         x[0, c0 ^ 1] = pins.bf16_bits(-0.625)
         lg = np.zeros((1, 1), np.float32)
-        ref = orc.forward(H, I, 1, 1, x, lg, {0: ex}, want_h=True)
+        ref = orc.forward(H, I, 1, 1, x, lg, {0: ex}, want_h=True,
+                          acc=accum.forward_model(1, H, I, 1, 1, mode))
         w = dev_weights({n: a[None] for n, a in ex.items()})
         y, h, _ = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, 1, mode=mode)
         torch.cuda.synchronize()
@@ -348,7 +351,7 @@ def test_prefill_scale_alignment(moe, orc, shift):
     w = moe.ExpertWeights(strides=(buf.shape[1],) * 6, I=I, **views)
     x = pins.rand_bf16(rng, (T, H))
     lg = rng.standard_normal((T, E)).astype(np.float32)
-    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True, acc=accum.model("mfma", H))
     y, h, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k,
                                             mode=moe.MODE_PREFILL)
     torch.cuda.synchronize()
@@ -419,3 +422,41 @@ def test_forward_residual(moe, orc, T, H, I, E, k, mode):
     if mode != 3:
         xr = orc.stack_layer(I, E, k, x0, lg, experts)
         check_y(x1.astype(np.float64) - x0, xr.astype(np.float64) - x0, f"residual mode={mode}")
+
+
+@pytest.mark.parametrize("T,mode", [(1, 1), (2, 1), (2, 2), (40, 2)],
+                         ids=["one_token", "few_tokens", "prefill_T2", "prefill_T40"])
+def test_scale_bytes_0_and_255(moe, orc, T, mode):
+    """UE8M0 byte 0 is 2^-127 and 255 is NaN (OCP MX).  Expert 0 carries bytes 0
+    in some w1, w3 and w2 groups (products that small leave the output as with
+    zero weights there); expert 1 carries a 255 in one w1 group, so every
+    token routed to it has NaN in h and in all of y, on both sides."""
+    import torch
+    H, I, E, k = 256, 128, 2, 1
+    rng = np.random.default_rng(255 + T + mode)
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    experts[0]["s1"][5, 2] = 0
+    experts[0]["s3"][9, 7] = 0
+    experts[0]["s2"][7, 1] = 0
+    experts[1]["s1"][3, 0] = 255
+    x = pins.rand_bf16(rng, (T, H))
+    lg = np.zeros((T, E), np.float32)
+    lg[np.arange(T), np.arange(T) % 2] = 1.0       # odd tokens take expert 1
+    if T == 1:
+        lg[0] = [0.0, 1.0]
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True,
+                      acc=accum.forward_model(T, H, I, E, k, mode))
+    w = dev_weights({n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]})
+    y, h, route = moe.moe_fp4_forward_debug(dev_bits(x), torch.from_numpy(lg).cuda(), w, k, mode=mode)
+    torch.cuda.synchronize()
+    y, h = y.cpu().numpy(), host_bits(h)
+    nan_tok = ref["idx"][:, 0] == 1
+    assert np.array_equal(np.isnan(y), np.isnan(ref["y"])), "NaN positions of y"
+    assert np.all(np.isnan(y[nan_tok])) and not np.isnan(y[~nan_tok]).any()
+    hn = bf16_value(h)
+    assert np.array_equal(np.isnan(hn), np.isnan(bf16_value(ref["h"]))), "NaN positions of h"
+    ok = ~nan_tok
+    if ok.any():
+        pairs = np.nonzero(ok)[0]
+        check_h(h[pairs], ref["h"][pairs], ref["hpre"][pairs], ref["hbound"][pairs], "scale byte 0")
+        check_y(y[ok], ref["y"][ok], "scale byte 0")
