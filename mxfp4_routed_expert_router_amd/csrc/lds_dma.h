@@ -18,11 +18,13 @@ namespace moe_fp4 {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
+// The LDS base goes in as an m0 operand: the compiler sets m0 itself and knows
+// that the instruction reads it.
 __device__ __forceinline__ void lds_load16(uint32_t lds_base, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 __device__ __forceinline__ void lds_load4(uint32_t lds_base, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(g) : "memory");
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 // Wait until at most N of this wave's loads are in flight, then meet the
 // workgroup.  The memory clobber keeps the compiler's LDS accesses on their side.
