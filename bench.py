@@ -7,11 +7,14 @@ top-6 routing, H = 5120, I = 2304.  Each step is one whole layer call -- router,
 permutation, w1/w3 GEMV with SiLU gating, w2 GEMV with the gate-weighted
 combine -- on a fresh token (x ~ N(0,1) in bf16, logits ~ N(0,1) plus a
 per-expert Zipf(1.1) bias).  Inputs are resident in HBM before timing starts.
+The value is the cold figure: L2 and the MALL are flushed before every step.
 
-Also measured, in the same JSON line: the 2048-token prefill chunk (TFLOP/s),
-per-kernel HIP-event durations (roofline of the dominant decode kernel), a
-cold-cache decode figure (L2/MALL flushed between steps), and the CPU oracle
-timed on a bounded sample of the same decode workload.
+Also measured, in the same JSON line: the same steps warm (graph replay),
+per-kernel durations (roofline of the dominant decode kernel), the 2048-token
+prefill chunk (TFLOP/s) in both activation modes, a streaming read of the
+decode kernels' footprints (achievable bandwidth), the router, shared-expert,
+verify and stack figures, and the CPU oracle timed on bounded samples of the
+same units of work.
 
     python bench.py [--gpus 1] [--steps 256] [--warmup 16]
 """
@@ -166,7 +169,8 @@ def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, g
             moe.moe_fp4_forward(xv[j], lv[j], w, vw.k, y=yv, workspace=wsv)
 
         us_v = graph_us(step_v)
-        d_v = [len(np.unique(topk_sets(lv_np[s], vw.k))) for s in range(n_v)]
+        timed = [(args.warmup + i) % n_v for i in range(args.steps)]   # the steps graph_us times
+        d_v = [len(np.unique(topk_sets(lv_np[s], vw.k))) for s in timed]
         b_v = float(np.mean(d_v)) * expert_bytes(vw.H, vw.I)
         verify[vw.name] = {"T": vw.T, "us_per_step": us_v, "us_per_token": us_v / vw.T,
                            "distinct_experts": float(np.mean(d_v)), "bytes_per_step": b_v,
@@ -203,8 +207,9 @@ def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, g
         args.warmup, args.steps = 2, n_s
         us_step = graph_us(step_s)
         args.warmup, args.steps = saved
+        timed = [(2 + i) % n_s for i in range(n_s)]   # the steps graph_us times (2 warm-up)
         d_s = [sum(len(np.unique(topk_sets(lgs_np[s][l], sw_.k))) for l in range(sw_.layers))
-               for s in range(n_s)]
+               for s in timed]
         b_s = float(np.mean(d_s)) * expert_bytes(sw_.H, sw_.I)
         stack[sw_.name] = {"T": sw_.T, "layers": sw_.layers, "E": sw_.E,
                            "us_per_step": us_step, "tokens_per_s": sw_.T / (us_step * 1e-6),
@@ -218,15 +223,153 @@ def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, g
     return routed, shared, verify, stack
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_baseline(args, synth, wl, xs, lgs, idx_all):
+    """The oracle (test infrastructure: plain double loops, OpenMP) on the same
+    units of work as the GPU, on bounded samples, all host threads and one."""
+    import oracle
+    from synth.configs import VERIFY6, VERIFY32, PREFILL as pf, STACK1
+    o = oracle.get()
+    threads = o.threads()
+    cache = {}
+
+    def experts_of(w_, layer, ids):
+        out = {}
+        for e in np.unique(ids):
+            key = (w_.weight_seed, layer, int(e))
+            if key not in cache:
+                cache[key] = synth.expert_host(w_, layer, int(e))
+            out[int(e)] = cache[key]
+        return out
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    res = {}
+    # decode tokens, all threads, until the time budget is spent
+    spent, n = 0.0, 0
+    while spent < args.cpu_seconds and n < len(xs):
+        ex = experts_of(wl, 0, idx_all[n])
+        spent += timed(lambda: o.forward(wl.H, wl.I, wl.E, wl.k, xs[n:n + 1], lgs[n:n + 1], ex))
+        n += 1
+    res["decode_us_per_token"] = spent / n * 1e6
+    res["decode_tokens"] = n
+    # one thread, two decode tokens
+    o.set_threads(1)
+    t1 = [timed(lambda i=i: o.forward(wl.H, wl.I, wl.E, wl.k, xs[i:i + 1], lgs[i:i + 1],
+                                      experts_of(wl, 0, idx_all[i])))
+          for i in range(2)]
+    o.set_threads(threads)
+    res["decode_us_per_token_1_thread"] = float(np.mean(t1)) * 1e6
+    # verify steps (one step each)
+    for vw in (VERIFY6, VERIFY32):
+        x, lg = synth.gen_x(vw, 0), synth.gen_logits(vw, 0)
+        ex = experts_of(vw, 0, topk_sets(lg, vw.k))
+        res[f"verify_T{vw.T}_us_per_step"] = timed(
+            lambda: o.forward(vw.H, vw.I, vw.E, vw.k, x, lg, ex)) * 1e6
+    # the prefill chunk: the first 256 of its 2048 tokens, scaled by 8 (the
+    # oracle's work is proportional to the tokens it computes)
+    x, lg = synth.gen_x(pf, 0), synth.gen_logits(pf, 0)
+    n_s = 256
+    toks = np.arange(n_s)
+    ex = experts_of(pf, 0, topk_sets(lg[:n_s], pf.k))
+    t = timed(lambda: o.forward(pf.H, pf.I, pf.E, pf.k, x, lg, ex, tokens=toks))
+    res["prefill_ms_per_chunk"] = t * (pf.T / n_s) * 1e3
+    # one token of the pruned 40-layer stack (40 layer calls)
+    xf = synth.gen_x_f32(STACK1, 0)
+    lgs_s = [synth.gen_logits(STACK1, 0, l) for l in range(STACK1.layers)]
+
+    def stack_token():
+        xx = xf
+        for l in range(STACK1.layers):
+            xx = o.stack_layer(STACK1.I, STACK1.E, STACK1.k, xx, lgs_s[l],
+                               experts_of(STACK1, l, topk_sets(lgs_s[l], STACK1.k)))
+
+    for l in range(STACK1.layers):     # weight generation stays outside the timing
+        experts_of(STACK1, l, topk_sets(lgs_s[l], STACK1.k))
+    res["stack_ms_per_token"] = timed(stack_token) * 1e3
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cpu = {"value": res["decode_us_per_token"], "unit": "us/token", "cores": threads,
+           "kind": "oracle", "nproc": aff, "cpu_model": cpu_model(),
+           "sample": (f"decode: {n} tokens of the timed workload on {threads} threads, and 2 on one "
+                      f"thread; verify: one T=6 and one T=32 step; prefill: the first 256 tokens of "
+                      f"the 2048-token chunk, scaled by 8; stack: one token through the 40 pruned "
+                      f"layers.  Weight generation excluded."),
+           "configs": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in res.items()}}
+    log(f"cpu oracle: {cpu['value']:.0f} us/token on {threads} threads "
+        f"({res['decode_us_per_token_1_thread']:.0f} on one), verify T=6 "
+        f"{res['verify_T6_us_per_step'] / 1e3:.0f} ms, T=32 {res['verify_T32_us_per_step'] / 1e3:.0f} ms, "
+        f"prefill chunk {res['prefill_ms_per_chunk'] / 1e3:.1f} s, stack token "
+        f"{res['stack_ms_per_token']:.0f} ms")
+    return cpu
+
+
+def run_stream(torch, dev, reps=6):
+    """Achievable read bandwidth of one kernel reading the decode kernels'
+    footprints and a long stream, caches cold (the windows rotate over 6 GiB)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_routed_expert_router_amd", "libmoe_fp4_measure.so"))
+    lib.moe_fp4_measure_stream_read.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    total = 6 << 30
+    buf = torch.full((total,), 3, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty(1 << 21, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, nb in (("w13_75MB", 75202560 + 10240), ("w2_38MB", 37601280 + 10240),
+                     ("step_113MB", 112803840), ("long_4GB", 4 << 30)):
+        best = None
+        for threads, per_cu, unroll in ((512, 2, 8), (256, 4, 8), (1024, 1, 8), (512, 2, 16)):
+            ts = []
+            for r in range(reps):
+                flush.sum()
+                span = (total - nb) // (1 << 24)
+                off = ((r * 7 + 3) % max(span, 1)) * (1 << 24)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                b.record()
+                rc = lib.moe_fp4_measure_stream_read(
+                    ctypes.c_void_p(buf.data_ptr() + off), ctypes.c_size_t(nb), cus * per_cu, threads,
+                    unroll, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(a.cuda_event),
+                    ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(stream.cuda_stream))
+                assert rc == 0, rc
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            us = float(np.median(ts[1:]))
+            if best is None or us < best["us"]:
+                best = {"bytes": nb, "us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                        "threads": threads, "workgroups": cus * per_cu, "loads_in_flight": unroll}
+        out[name] = best
+        log(f"stream read {name}: {best['us']:.2f} us, {best['GBps']:.0f} GB/s cold")
+    del buf, flush, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--prefill-reps", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode figure")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm (graph replay) decode figures: every decode launch is then cold")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router, shared-expert, verify and stack figures (profiling runs)")
     args = ap.parse_args()
@@ -251,8 +394,7 @@ def main():
     torch.cuda.synchronize()
     log(f"weights: {wl.E} experts x {expert_bytes(wl.H, wl.I)} B generated in HBM "
         f"in {time.time() - t0:.1f} s")
-    n_tok = max(args.steps, 1)
-    n_gen = min(wl.steps, n_tok + args.warmup)
+    n_gen = args.warmup + max(args.steps, 1)   # one distinct token per step
     xs = np.stack([synth.gen_x(wl, s)[0] for s in range(n_gen)])
     lgs = np.stack([synth.gen_logits(wl, s)[0] for s in range(n_gen)])
     x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -261,6 +403,7 @@ def main():
     ws = torch.empty(moe.moe_fp4_workspace_size(1, wl.H, wl.I, wl.E, wl.k), dtype=torch.uint8,
                      device=dev)
     idx_all = topk_sets(lgs, wl.k)
+    timed_ids = [args.warmup + i for i in range(args.steps)]
 
     def step(i, events=None):
         j = i % n_gen
@@ -270,57 +413,46 @@ def main():
         else:
             moe.moe_fp4_forward_profiled(xi, li, w, wl.k, events, y=yi, workspace=ws)
 
-    # ---------------------------------------------------------------- decode, timed
-    # The steps are captured once into HIP graphs and replayed: a serving loop
-    # issues a layer call this way, and it keeps the host's per-call launch
-    # overhead (Python + ctypes, tens of microseconds) out of the GPU timeline.
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    g_plain = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_plain):
-        for i in range(args.steps):
-            step(args.warmup + i)
-    g_plain.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    g_plain.replay()
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
-
-    # Kernel durations: each kernel's dispatch records a start and an end event
-    # on the layer's stream (moe_fp4_forward_profiled).  The steps are enqueued
-    # behind a spin kernel so that they are all queued before the first one runs
-    # and execute back to back, as in the graph.
-    evs = [moe.StageEvents() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SPIN_CYCLES)
-    tp0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    ms_per_step_prof = evs[0].events[0].elapsed_time(evs[-1].events[-1]) / args.steps
-    stage = np.array([e.stage_ms() for e in evs])  # [steps, 4]: route, w13, w2, combine
-    k_ms = {"route": float(stage[:, 0].mean()), "w13": float(stage[:, 1].mean()),
-            "w2": float(stage[:, 2].mean())}
-    by = [decode_bytes(wl, idx_all[(args.warmup + i) % n_gen][None]) for i in range(args.steps)]
+    by = [decode_bytes(wl, idx_all[i][None]) for i in timed_ids]
     k_bytes = {n: float(np.mean([b[n] for b in by])) for n in ("route", "w13", "w2")}
     step_bytes = k_bytes["route"] + k_bytes["w13"] + k_bytes["w2"]
-    us_tok = ms_per_step * 1e3 / wl.T
-    dom = max(("w13", "w2"), key=lambda n: k_ms[n])
-    achieved = k_bytes[dom] / (k_ms[dom] * 1e-3) / 1e9
-    log(f"decode: {us_tok:.2f} us/token graph replay ({step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s "
-        f"algorithmic; {ms_per_step_prof * 1e3:.2f} us per step with timed dispatches); kernels route "
-        f"{k_ms['route'] * 1e3:.2f} us, w1/w3 {k_ms['w13'] * 1e3:.2f} us, "
-        f"w2+combine {k_ms['w2'] * 1e3:.2f} us")
-    eager_t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
-    log(f"decode eager (one Python call per step): {us_eager:.2f} us/token")
 
+    # ---------------------------------------------------------------- decode, cold (the value)
+    # Every step runs with L2 and the MALL cold: a read-only sweep of 1 GiB
+    # between steps (no dirty lines left to write back during the step).  Each
+    # kernel's dispatch records its own start and end events
+    # (moe_fp4_forward_profiled), so a step is timed from the start of its first
+    # kernel to the end of its last, launch gap between them included; the
+    # sweeps fall outside.  Warm-up steps are cold too, so every launch of the
+    # decode kernels in a --no-warm run is a cold one.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    evc = [moe.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    sinks = []
+    for i in range(args.warmup):
+        sinks.append(flush.sum())
+        step(i)
+    for n, i in enumerate(timed_ids):
+        sinks.append(flush.sum())
+        step(i, evc[n])
+    torch.cuda.synchronize()
+    del flush, sinks
+    ev = [e.events for e in evc]
+    span_us = np.array([e[2].elapsed_time(e[5]) for e in ev]) * 1e3    # w1/w3 start -> w2 end
+    st = np.array([e.stage_ms() for e in evc]) * 1e3                   # [steps, 4] us
+    k_us = {"route": float(st[:, 0].mean()), "w13": float(st[:, 1].mean()),
+            "w2": float(st[:, 2].mean())}
+    us_tok = float(span_us.mean()) / wl.T
+    dom = max(("w13", "w2"), key=lambda n: k_us[n])
+    achieved = k_bytes[dom] / (k_us[dom] * 1e-6) / 1e9
+    log(f"decode cold: {us_tok:.2f} us/token (first kernel start to last kernel end; median "
+        f"{np.median(span_us):.2f}), {step_bytes / (us_tok * 1e-6) / 1e9:.0f} GB/s; kernels w1/w3 "
+        f"{k_us['w13']:.2f} us, w2 {k_us['w2']:.2f} us")
+
+    # ---------------------------------------------------------------- decode, warm
+    # The same steps captured into one HIP graph and replayed (caches warm:
+    # consecutive tokens share experts, and the MALL holds part of the layer).
     def graph_us(fn):
         for i in range(args.warmup):
             fn(i)
@@ -336,115 +468,98 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e6 / args.steps
 
+    warm = None
     routed = shared = None
     verify, stack = {}, {}
-    if not args.no_extras:
-        routed, shared, verify, stack = run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d,
-                                                   y_d, ws, n_gen, graph_us)
-
-    # ---------------------------------------------------------------- decode, cold caches
-    # A read-only flush (summing a 1 GiB buffer) between steps evicts the
-    # experts from L2 and the MALL without leaving dirty lines whose write-back
-    # would compete with the timed step.
-    cold = None
-    if not args.no_cold:
-        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-        n_cold = min(64, args.steps)
-        evc = [moe.StageEvents() for _ in range(n_cold)]
+    if not args.no_warm:
+        us_warm = graph_us(step)
+        evs = [moe.StageEvents() for _ in range(args.steps)]
         torch.cuda.synchronize()
         torch.cuda._sleep(SPIN_CYCLES)
-        sinks = []
-        for i in range(n_cold):
-            sinks.append(flush.sum())
-            step(args.warmup + i, evc[i])
+        for n, i in enumerate(timed_ids):
+            step(i, evs[n])
         torch.cuda.synchronize()
-        st = np.array([e.stage_ms() for e in evc])
-        tot = st[:, 1:3].sum(1)  # w1/w3 (routing inside) + w2 (combine inside)
-        cold = {"us_per_token": float(tot.mean() * 1e3),
-                "w13_us": float(st[:, 1].mean() * 1e3), "w2_us": float(st[:, 2].mean() * 1e3),
-                "w13_GBps": float(k_bytes["w13"] / (st[:, 1].mean() * 1e-3) / 1e9),
-                "w2_GBps": float(k_bytes["w2"] / (st[:, 2].mean() * 1e-3) / 1e9),
-                "steps": n_cold, "note": "1 GiB read between steps, outside the events"}
-        del flush, sinks
-        log(f"decode cold: {cold['us_per_token']:.2f} us/token (kernel sum), w1/w3 "
-            f"{cold['w13_GBps']:.0f} GB/s, w2 {cold['w2_GBps']:.0f} GB/s")
+        stw = np.array([e.stage_ms() for e in evs]) * 1e3
+        eager_t0 = time.perf_counter()
+        for i in timed_ids:
+            step(i)
+        torch.cuda.synchronize()
+        us_eager = (time.perf_counter() - eager_t0) * 1e6 / args.steps
+        warm = {"us_per_token": us_warm, "GBps": step_bytes / (us_warm * 1e-6) / 1e9,
+                "w13_us": float(stw[:, 1].mean()), "w2_us": float(stw[:, 2].mean()),
+                "us_per_token_eager": us_eager,
+                "note": "the timed steps captured in one HIP graph, replayed once (wall clock); "
+                        "kernel times from dispatch events, steps back to back; eager: one "
+                        "Python call per step"}
+        log(f"decode warm: {us_warm:.2f} us/token graph replay; kernels w1/w3 "
+            f"{warm['w13_us']:.2f} us, w2 {warm['w2_us']:.2f} us; eager {us_eager:.2f} us/token")
+        if not args.no_extras:
+            routed, shared, verify, stack = run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d,
+                                                       y_d, ws, n_gen, graph_us)
 
     # ---------------------------------------------------------------- prefill chunk
-    xp = torch.from_numpy(synth.gen_x(pf, 0).view(np.int16)).to(dev).view(torch.bfloat16)
-    lp_np = synth.gen_logits(pf, 0)
-    lp = torch.from_numpy(lp_np).to(dev)
-    yp = torch.empty((pf.T, pf.H), dtype=torch.float32, device=dev)
-    pairs = pf.T * pf.k
-    flops = pairs * (2 * 2 * pf.H * pf.I + 2 * pf.I * pf.H)
-    Dp = len(np.unique(topk_sets(lp_np, pf.k)))
-    p_bytes = Dp * expert_bytes(pf.H, pf.I) + pf.T * pf.H * 2 + pf.T * pf.H * 4
+    prefill = prefill_mx = None
+    if args.prefill_reps > 0:
+        xp = torch.from_numpy(synth.gen_x(pf, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+        lp_np = synth.gen_logits(pf, 0)
+        lp = torch.from_numpy(lp_np).to(dev)
+        yp = torch.empty((pf.T, pf.H), dtype=torch.float32, device=dev)
+        pairs = pf.T * pf.k
+        flops = pairs * (2 * 2 * pf.H * pf.I + 2 * pf.I * pf.H)
+        Dp = len(np.unique(topk_sets(lp_np, pf.k)))
+        p_bytes = Dp * expert_bytes(pf.H, pf.I) + pf.T * pf.H * 2 + pf.T * pf.H * 4
 
-    def run_prefill(mode, label, mfma_peak):
-        wsp = torch.empty(moe.moe_fp4_workspace_size(pf.T, pf.H, pf.I, pf.E, pf.k, mode),
-                          dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp)
-        torch.cuda.synchronize()
-        evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
-        tp0 = time.perf_counter()
-        for i in range(args.prefill_reps):
-            moe.moe_fp4_forward_profiled(xp, lp, w, pf.k, evp[i], y=yp, mode=mode, workspace=wsp)
-        torch.cuda.synchronize()
-        tp1 = time.perf_counter()
-        pst = np.array([e.stage_ms() for e in evp])
-        p_ms = (tp1 - tp0) * 1e3 / args.prefill_reps
-        out = {
-            "workload": "prefill chunk T=2048, E=384, top-6, H=5120, I=2304, Zipf(0.3) logit bias",
-            "activations": label,
-            "ms_per_chunk": p_ms, "tflops": flops / (p_ms * 1e-3) / 1e12, "gflop": flops / 1e9,
-            "distinct_experts": Dp, "weight_GB": Dp * expert_bytes(pf.H, pf.I) / 1e9,
-            "hbm_frac": p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "mfma_frac": flops / (p_ms * 1e-3) / 1e12 / mfma_peak, "mfma_peak_tflops": mfma_peak,
-            "kernel_ms": {"route": float(pst[:, 0].mean()), "w13": float(pst[:, 1].mean()),
-                          "w2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
-        }
-        out["roofline_frac"] = max(out["hbm_frac"], out["mfma_frac"])
-        # the same chunk with the saliency side output (moe_fp4_forward_saliency)
-        sal = torch.zeros(pf.E, dtype=torch.float32, device=dev)
-        moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode, workspace=wsp)
-        torch.cuda.synchronize()
-        ts0 = time.perf_counter()
-        for i in range(args.prefill_reps):
-            moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode,
-                                         workspace=wsp)
-        torch.cuda.synchronize()
-        out["ms_per_chunk_with_saliency"] = (time.perf_counter() - ts0) * 1e3 / args.prefill_reps
-        log(f"prefill ({label}): {p_ms:.3f} ms/chunk, {out['tflops']:.1f} TFLOP/s, HBM frac "
-            f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}; with saliency "
-            f"{out['ms_per_chunk_with_saliency']:.3f} ms")
-        del wsp, sal
-        return out
+        def run_prefill(mode, label, mfma_peak):
+            wsp = torch.empty(moe.moe_fp4_workspace_size(pf.T, pf.H, pf.I, pf.E, pf.k, mode),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp)
+            torch.cuda.synchronize()
+            evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
+            tp0 = time.perf_counter()
+            for i in range(args.prefill_reps):
+                moe.moe_fp4_forward_profiled(xp, lp, w, pf.k, evp[i], y=yp, mode=mode, workspace=wsp)
+            torch.cuda.synchronize()
+            tp1 = time.perf_counter()
+            pst = np.array([e.stage_ms() for e in evp])
+            p_ms = (tp1 - tp0) * 1e3 / args.prefill_reps
+            out = {
+                "workload": "prefill chunk T=2048, E=384, top-6, H=5120, I=2304, Zipf(0.3) logit bias",
+                "activations": label,
+                "ms_per_chunk": p_ms, "tflops": flops / (p_ms * 1e-3) / 1e12, "gflop": flops / 1e9,
+                "distinct_experts": Dp, "weight_GB": Dp * expert_bytes(pf.H, pf.I) / 1e9,
+                "hbm_frac": p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "mfma_frac": flops / (p_ms * 1e-3) / 1e12 / mfma_peak, "mfma_peak_tflops": mfma_peak,
+                "kernel_ms": {"route": float(pst[:, 0].mean()), "w13": float(pst[:, 1].mean()),
+                              "w2": float(pst[:, 2].mean()), "combine": float(pst[:, 3].mean())},
+            }
+            out["roofline_frac"] = max(out["hbm_frac"], out["mfma_frac"])
+            # the same chunk with the saliency side output (moe_fp4_forward_saliency)
+            sal = torch.zeros(pf.E, dtype=torch.float32, device=dev)
+            moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode, workspace=wsp)
+            torch.cuda.synchronize()
+            ts0 = time.perf_counter()
+            for i in range(args.prefill_reps):
+                moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode,
+                                             workspace=wsp)
+            torch.cuda.synchronize()
+            out["ms_per_chunk_with_saliency"] = (time.perf_counter() - ts0) * 1e3 / args.prefill_reps
+            log(f"prefill ({label}): {p_ms:.3f} ms/chunk, {out['tflops']:.1f} TFLOP/s, HBM frac "
+                f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}; with saliency "
+                f"{out['ms_per_chunk_with_saliency']:.3f} ms")
+            del wsp, sal
+            return out
 
-    prefill = run_prefill(moe.MODE_PREFILL, "bf16 (MFMA 16x16x32 bf16, FP4 staged in LDS and "
-                                            "decoded to bf16 in registers)",
-                          BF16_PEAK_TFLOPS)
-    prefill_mx = run_prefill(moe.MODE_PREFILL_MXFP8,
-                             "MXFP8 (x and h quantised; FP4 x FP8 scaled MFMA 16x16x128)",
-                             FP8_PEAK_TFLOPS)
+        prefill = run_prefill(moe.MODE_PREFILL, "bf16 (MFMA 16x16x32 bf16, FP4 staged in LDS and "
+                                                "decoded to bf16 in registers)", BF16_PEAK_TFLOPS)
+        prefill_mx = run_prefill(moe.MODE_PREFILL_MXFP8,
+                                 "MXFP8 (x and h quantised; FP4 x FP8 scaled MFMA 16x16x128)",
+                                 FP8_PEAK_TFLOPS)
 
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        o = oracle.get()
-        spent, n, i = 0.0, 0, 0
-        while spent < args.cpu_seconds and n < n_gen:
-            ids = np.unique(idx_all[i])
-            experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in ids}
-            tc = time.perf_counter()
-            o.forward(wl.H, wl.I, wl.E, wl.k, xs[i:i + 1], lgs[i:i + 1], experts)
-            spent += time.perf_counter() - tc
-            n += 1
-            i += 1
-        cpu = {"value": spent / n * 1e6, "unit": "us/token", "cores": o.threads(), "kind": "oracle",
-               "sample": f"{n} decode tokens of the same workload (T=1, 6 of 384 experts, full "
-                         f"H=5120, I=2304), one oracle call each; weight generation excluded"}
-        log(f"cpu oracle: {cpu['value']:.0f} us/token on {cpu['cores']} threads ({n} tokens)")
+    del w
+    torch.cuda.empty_cache()
+    stream = None if args.no_stream else run_stream(torch, dev)
+    cpu = None if args.no_cpu else run_cpu_baseline(args, synth, wl, xs, lgs, idx_all)
 
     res = {
         "metric": METRIC,
@@ -453,30 +568,33 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(us_tok * wl.T / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode T=1, E=384 resident (7.22 GB FP4 E2M1 + UE8M0), top-6, "
-                               "H=5120, I=2304, Zipf(1.1) logit bias, 256 distinct tokens",
+        "config": {"workload": f"decode T=1, E=384 resident (7.22 GB FP4 E2M1 + UE8M0), top-6, "
+                               f"H=5120, I=2304, Zipf(1.1) logit bias, {n_gen} distinct tokens "
+                               f"({args.warmup} warm-up, {args.steps} timed), L2 and MALL cold",
                    "T": wl.T, "E": wl.E, "k": wl.k, "H": wl.H, "I": wl.I},
-        "tokens_per_s": 1e3 / ms_per_step * wl.T,
-        "hbm_GBps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "tokens_per_s": 1e6 / us_tok,
+        "hbm_GBps": step_bytes / (us_tok * 1e-6) / 1e9,
+        "step_bytes": step_bytes,
+        "step_frac": step_bytes / (us_tok * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": DECODE_KERNELS[dom],
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(DECODE_KERNELS[dom]), "traffic_unit": "bytes/launch",
-                     "bytes_per_launch": k_bytes[dom], "avg_us": k_ms[dom] * 1e3},
-        "kernels_us": {n: round(v * 1e3, 3) for n, v in k_ms.items()},
-        "timing": "value: HIP graph of all steps, replayed once (wall clock); kernel durations: "
-                  "start/end events recorded by each kernel's own dispatch on the layer's "
-                  "stream, steps queued back to back; one-token routing runs inside the w1/w3 "
-                  "kernel and its bytes (logits) are counted there",
-        "us_per_token_with_events": ms_per_step_prof * 1e3 / wl.T,
-        "us_per_token_eager": us_eager,
-        "cold": cold,
+                     "bytes_per_launch": k_bytes[dom], "avg_us": k_us[dom],
+                     "note": "cold launches (L2 and MALL flushed before each step)"},
+        "kernels_us": {n: round(v, 3) for n, v in k_us.items()},
+        "timing": "value: mean over the timed steps of the span from the start of a step's first "
+                  "kernel to the end of its last (events recorded by the dispatches themselves), "
+                  "each step on a fresh token with L2 and the MALL flushed before it; the one-token "
+                  "routing runs inside the w1/w3 kernel and its bytes (the logits) are counted there",
+        "warm": warm,
+        "stream_read": stream,
         "decode_routed": routed,
         "decode_shared": shared,
         "verify": verify,

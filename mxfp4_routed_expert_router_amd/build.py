@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_fp4.so")
+MEASURE_LIB = os.path.join(HERE, "libmoe_fp4_measure.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "route.hip", "router.hip", "decode.hip", "prefill.hip", "prefill_lds.hip", "mx8.hip", "shared.hip", "stack.hip"]
 
@@ -38,8 +39,12 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # the measurement companion (a plain streaming read), loaded by the benchmark only
+    tmp = MEASURE_LIB + ".tmp"
+    _run([HIPCC, *FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "measure.hip")])
+    os.replace(tmp, MEASURE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", MEASURE_LIB)
     return LIB
 
 
