@@ -172,6 +172,24 @@ int moe_fp4_forward(const moe_fp4_dims *dims, const uint16_t *x, const float *lo
                     const moe_fp4_weights *w, float *y, int mode, int flags, void *ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/* As moe_fp4_forward, with no workspace argument and no allocation: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc).  The workspace is a static
+ * device array of MOE_FP4_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends; its address is looked up on the first
+ * call on each device (hipGetSymbolAddress), and no call allocates or frees
+ * anything.  Every call on a GPU uses that GPU's array: calls that overlap on
+ * one GPU (other streams, other host threads) race and must not be made.
+ * Nothing in it needs clearing between calls.
+ * Errors: as moe_fp4_forward; EWORKSPACE when the call needs more workspace
+ * than the array holds (moe_fp4_workspace_size(dims, mode) >
+ * MOE_FP4_NOALLOC_SCRATCH_BYTES: one decode token needs about 30 KB, a
+ * 2048-token prefill chunk about 311 MB), found before any HIP call. */
+#define MOE_FP4_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_fp4_forward_noalloc(const moe_fp4_dims *dims, const uint16_t *x, const float *logits,
+                            const moe_fp4_weights *w, float *y, int mode, int flags,
+                            hipStream_t stream);
+
 /* As moe_fp4_forward, and also writes the intermediates:
  *   h_out      [T*k][I] bf16 bits in pair order (row p = t*k + j), or NULL
  *   route_out  routing result as moe_fp4_route writes it, or NULL */

@@ -59,6 +59,8 @@ def _load():
     lib.moe_fp4_route.argtypes = [ctypes.POINTER(Dims), P, ctypes.POINTER(RouteOut), P, SZ, P]
     lib.moe_fp4_route_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(SZ)]
     lib.moe_fp4_plan.argtypes = [ctypes.POINTER(Dims), I32, ctypes.POINTER(I32)]
+    lib.moe_fp4_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights), P,
+                                            I32, I32, P]
     lib.moe_fp4_forward.argtypes = [ctypes.POINTER(Dims), P, P, ctypes.POINTER(Weights), P, I32,
                                     I32, P, SZ, P]
     lib.moe_fp4_forward_debug.argtypes = lib.moe_fp4_forward.argtypes + [P, ctypes.POINTER(RouteOut)]
@@ -79,7 +81,7 @@ def _load():
                                              P, P, I32, I32, P, SZ, P]
     lib.moe_fp4_status_string.restype = ctypes.c_char_p
     for f in ("moe_fp4_workspace_size", "moe_fp4_route", "moe_fp4_forward", "moe_fp4_plan",
-              "moe_fp4_route_workspace_size",
+              "moe_fp4_route_workspace_size", "moe_fp4_forward_noalloc",
               "moe_fp4_forward_debug", "moe_fp4_prenorm_bf16", "moe_fp4_quant_mxfp8",
               "moe_fp4_router_logits", "moe_fp4_forward_routed", "moe_fp4_forward_saliency",
               "moe_fp4_shared_expert", "moe_fp4_forward_shared", "moe_fp4_forward_residual"):
@@ -286,6 +288,24 @@ class StageEvents:
     def span_ms(self):
         """ms from the start of routing to the end of the combine."""
         return self.events[0].elapsed_time(self.events[-1])
+
+
+def moe_fp4_forward_noalloc(x, logits, weights: ExpertWeights, k: int, y=None, mode=MODE_AUTO,
+                            accumulate=False):
+    """As moe_fp4_forward with the library's static per-GPU workspace (no
+    allocation inside the library; y is allocated here only when not given)."""
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    _need(logits, "logits", (torch.float32,), 2)
+    T, H = x.shape
+    E = logits.shape[1]
+    I = weights.intermediate()
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    ws = weights.as_struct()
+    _check(_lib.moe_fp4_forward_noalloc(
+        ctypes.byref(Dims(T, H, I, E, k)), x.data_ptr(), logits.data_ptr(), ctypes.byref(ws),
+        y.data_ptr(), mode, ACCUMULATE if accumulate else 0, _stream(x)), "moe_fp4_forward_noalloc")
+    return y
 
 
 def moe_fp4_forward_profiled(x, logits, weights: ExpertWeights, k: int, events: StageEvents,

@@ -3,6 +3,7 @@
 // host before the first HIP call, so a rejected call enqueues nothing.
 #include "../../include/moe_fp4.h"
 
+#include <mutex>
 #include <new>
 
 #include "kernels.h"
@@ -117,7 +118,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
                  void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                  moe_fp4_route_out* route_out, const hipEvent_t* events,
                  float* saliency = nullptr, float* x_resid = nullptr,
-                 const SharedArgs* shared13 = nullptr) {
+                 const SharedArgs* shared13 = nullptr, bool validate_only = false) {
   if (x_resid) {
     if (x) return MOE_FP4_EINVAL;
     y = x_resid;
@@ -156,7 +157,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
        stride[3] % 4 || stride[5] % 4))
     return MOE_FP4_EALIGN;
   const WsLayout L = layout(d, rmode);
-  if (ws_bytes < L.total) return MOE_FP4_EWORKSPACE;
+  if (ws_bytes < L.total || validate_only) return MOE_FP4_EWORKSPACE;
 
   // the pre-norm: inside the w1/w3 kernel on the one-token path, else a
   // kernel of its own into the workspace
@@ -268,9 +269,58 @@ const uint8_t* const* shared_tensors(const moe_fp4_shared_weights* sw, const uin
   return t;
 }
 
+// The workspace of moe_fp4_forward_noalloc: one array per GPU, held until the
+// process ends.  Host code never uses its name as an address (on the host it
+// is a stand-in symbol): the device address comes from hipGetSymbolAddress,
+// taken once per device and kept in scratch_ptr.
+constexpr size_t kScratchBytes = MOE_FP4_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, or null (and *err set) on failure.
+void* device_scratch(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_fp4_forward_noalloc(const moe_fp4_dims* dims, const uint16_t* x, const float* logits,
+                            const moe_fp4_weights* w, float* y, int mode, int flags,
+                            hipStream_t stream) {
+  // Every check of moe_fp4_forward, with a stand-in workspace address that
+  // passes its alignment rule and is never used: forward_impl returns
+  // EWORKSPACE at its workspace check when everything before it passed.
+  // Then the size rule.  All of it before the first HIP call.
+  const int rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags,
+                              reinterpret_cast<void*>(kAlign), 0, stream, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, nullptr, /*validate_only=*/true);
+  if (rc != MOE_FP4_EWORKSPACE) return rc;
+  if (layout(*dims, resolve_mode(*dims, mode)).total > kScratchBytes) return MOE_FP4_EWORKSPACE;
+  hipError_t err = hipSuccess;
+  void* ws = device_scratch(&err);
+  if (!ws) return MOE_FP4_EHIP;
+  return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, kScratchBytes, stream,
+                      nullptr, nullptr, nullptr);
+}
 
 int moe_fp4_workspace_size(const moe_fp4_dims* dims, int mode, size_t* bytes) {
   if (!dims || !bytes) return MOE_FP4_EINVAL;

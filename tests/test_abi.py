@@ -364,3 +364,18 @@ def test_forward_residual_validation(lib):
     assert call(None, n.value) == lib.EINVAL
     assert call(FAKE + 8, n.value) == lib.EALIGN
     assert call(FAKE, 0) == lib.EWORKSPACE
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The no-allocation forward refuses a call whose workspace would exceed its
+    static array (the 2048-token chunk), and bad arguments, before any HIP call."""
+    f = lib._lib.moe_fp4_forward_noalloc
+    w = _weights(lib)
+    big = lib.Dims(2048, 5120, 2304, 384, 6)
+    assert lib.moe_fp4_workspace_size(2048, 5120, 2304, 384, 6) > (8 << 20)
+    assert f(ctypes.byref(big), FAKE, FAKE, ctypes.byref(w), FAKE, 0, 0, None) == lib.EWORKSPACE
+    small = lib.Dims(4, 256, 128, 16, 2)
+    assert f(ctypes.byref(small), None, FAKE, ctypes.byref(w), FAKE, 0, 0, None) == lib.EINVAL
+    assert f(ctypes.byref(small), FAKE + 2, FAKE, ctypes.byref(w), FAKE, 0, 0, None) == lib.EALIGN
+    assert f(ctypes.byref(small), FAKE, FAKE, ctypes.byref(w), FAKE, 7, 0, None) == lib.EUNSUPPORTED
+    assert f(ctypes.byref(big), None, FAKE, ctypes.byref(w), FAKE, 0, 0, None) == lib.EINVAL
