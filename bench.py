@@ -419,36 +419,79 @@ def main():
 
     # ---------------------------------------------------------------- decode, cold (the value)
     # Every step runs with L2 and the MALL cold: a read-only sweep of 1 GiB
-    # between steps (no dirty lines left to write back during the step).  Each
-    # kernel's dispatch records its own start and end events
-    # (moe_fp4_forward_profiled), so a step is timed from the start of its first
-    # kernel to the end of its last, launch gap between them included; the
-    # sweeps fall outside.  Warm-up steps are cold too, so every launch of the
-    # decode kernels in a --no-warm run is a cold one.
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    # (libmoe_fp4_measure's streaming read) before each step, which leaves no
+    # dirty lines to write back during the step.  The K timed steps, each after
+    # its sweep, are one HIP graph; a second graph holds the K sweeps alone.
+    # Both are replayed (wall clock between synchronisations, median of reps)
+    # and the cold step is the difference over K: every launch gap between the
+    # layer's kernels is inside it, the sweeps are not.
+    import ctypes
+    mlib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_routed_expert_router_amd", "libmoe_fp4_measure.so"))
+    mlib.moe_fp4_measure_stream_read.restype = ctypes.c_int
+    fbuf = torch.full((1 << 30,), 1, dtype=torch.uint8, device=dev)
+    fsink = torch.empty(1 << 21, dtype=torch.int32, device=dev)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def sweep():
+        rc = mlib.moe_fp4_measure_stream_read(
+            ctypes.c_void_p(fbuf.data_ptr()), ctypes.c_size_t(1 << 30), 2 * n_cu, 512, 8,
+            ctypes.c_void_p(fsink.data_ptr()), None, None,
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        assert rc == 0, rc
+
+    def graph_of(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_us(g, reps=5):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e6
+
+    for i in range(args.warmup):
+        sweep()
+        step(i)
+    torch.cuda.synchronize()
+
+    def cold_step(n):
+        sweep()
+        step(args.warmup + n)
+
+    g_cold = graph_of(cold_step, args.steps)
+    g_sweep = graph_of(lambda n: sweep(), args.steps)
+    t_cold, t_sweep = replay_us(g_cold), replay_us(g_sweep)
+    us_tok = (t_cold - t_sweep) / args.steps / wl.T
+    del g_cold, g_sweep
+    # kernel durations for the roofline: the same cold steps run eagerly, each
+    # kernel's dispatch recording its own start and end events
+    # (moe_fp4_forward_profiled); warm-up steps are cold too, so every launch of
+    # the decode kernels in a --no-warm run is a cold one
     evc = [moe.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(SPIN_CYCLES)
-    sinks = []
-    for i in range(args.warmup):
-        sinks.append(flush.sum())
-        step(i)
     for n, i in enumerate(timed_ids):
-        sinks.append(flush.sum())
+        sweep()
         step(i, evc[n])
     torch.cuda.synchronize()
-    del flush, sinks
-    ev = [e.events for e in evc]
-    span_us = np.array([e[2].elapsed_time(e[5]) for e in ev]) * 1e3    # w1/w3 start -> w2 end
+    del fbuf, fsink
     st = np.array([e.stage_ms() for e in evc]) * 1e3                   # [steps, 4] us
     k_us = {"route": float(st[:, 0].mean()), "w13": float(st[:, 1].mean()),
             "w2": float(st[:, 2].mean())}
-    us_tok = float(span_us.mean()) / wl.T
     dom = max(("w13", "w2"), key=lambda n: k_us[n])
     achieved = k_bytes[dom] / (k_us[dom] * 1e-6) / 1e9
-    log(f"decode cold: {us_tok:.2f} us/token (first kernel start to last kernel end; median "
-        f"{np.median(span_us):.2f}), {step_bytes / (us_tok * 1e-6) / 1e9:.0f} GB/s; kernels w1/w3 "
-        f"{k_us['w13']:.2f} us, w2 {k_us['w2']:.2f} us")
+    log(f"decode cold: {us_tok:.2f} us/token (graph of {args.steps} swept steps {t_cold / args.steps:.1f} "
+        f"us each, sweeps alone {t_sweep / args.steps:.1f}), {step_bytes / (us_tok * 1e-6) / 1e9:.0f} "
+        f"GB/s; kernels w1/w3 {k_us['w13']:.2f} us, w2 {k_us['w2']:.2f} us")
 
     # ---------------------------------------------------------------- decode, warm
     # The same steps captured into one HIP graph and replayed (caches warm:
@@ -589,10 +632,12 @@ def main():
                      "bytes_per_launch": k_bytes[dom], "avg_us": k_us[dom],
                      "note": "cold launches (L2 and MALL flushed before each step)"},
         "kernels_us": {n: round(v, 3) for n, v in k_us.items()},
-        "timing": "value: mean over the timed steps of the span from the start of a step's first "
-                  "kernel to the end of its last (events recorded by the dispatches themselves), "
-                  "each step on a fresh token with L2 and the MALL flushed before it; the one-token "
-                  "routing runs inside the w1/w3 kernel and its bytes (the logits) are counted there",
+        "timing": "value: the timed steps, each on a fresh token after a 1 GiB read-only sweep that "
+                  "leaves L2 and the MALL cold, captured in one HIP graph and replayed; minus the "
+                  "same graph of sweeps alone; divided by the steps.  Kernel durations (roofline): "
+                  "the same cold steps run eagerly with start/end events recorded by each kernel's "
+                  "own dispatch.  The one-token routing runs inside the w1/w3 kernel and its bytes "
+                  "(the logits) are counted there",
         "warm": warm,
         "stream_read": stream,
         "decode_routed": routed,
