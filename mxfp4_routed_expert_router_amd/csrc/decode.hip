@@ -285,36 +285,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// The k chosen experts of the token by ascending id (slot d), ranked by the one
-// wave that calls this (wave 0 of each workgroup) into the workgroup's table;
-// the other waves wait for it at the barrier that also publishes x.  Each
-// chosen expert holds exactly one pair, so the expert of rank j sits in sorted
-// slot (number of chosen ids below it).  Wave 0 of workgroup 0 publishes the
-// routing result.
-__device__ __forceinline__ void route_one_wave(const LayerArgs& a, const float (&lv)[kFusedVPL],
-                                               int (&de)[kMaxK]) {
-  const int lane = threadIdx.x & (kWave - 1), k = a.k;
-  int my_e;
-  float my_g;
-  wave_topk_vals<kFusedVPL>(lv, a.E, k, lane, my_e, my_g);
-  const int key = lane < k ? my_e : 0x7FFFFFFF;
-  int rank = 0;
-  for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(key, i) < key ? 1 : 0;
-  if (lane < k) de[rank] = my_e;
-  if (blockIdx.x == 0 && threadIdx.x < kWave && lane < k) {
-    const RouteArgs& r = a.route;
-    r.idx[lane] = my_e;
-    r.gates[lane] = my_g;
-    r.sorted_pairs[rank] = lane;
-    r.pair_slot[lane] = rank;
-    r.slot_gate[rank] = my_g;
-    r.slot_tok[rank] = 0;
-    r.dinfo[4 * rank + 0] = my_e;
-    r.dinfo[4 * rank + 1] = rank;
-    r.dinfo[4 * rank + 2] = 1;
-    r.dinfo[4 * rank + 3] = 0;
+// The one-token w1/w3 kernel's tables, in LDS.  Its units are taken in the
+// ranking's order: the expert of rank j (largest logit first) is de_rank[j],
+// and its rows of h go to sorted slot slot_of[j], the number of chosen ids
+// below it (each chosen expert holds exactly one pair).  de_w lists the
+// chosen experts by ascending id (slot order).
+struct OneTables {
+  int de_rank[kMaxK], slot_of[kMaxK], de_w[kMaxK];
+};
+
+// Wave 0 of each workgroup ranks the logits; after round j it stores rank j's
+// expert, so the other waves can start on the first ranks while it ranks the
+// rest.
+struct OneRanking {
+  WaveRanking<kFusedVPL> rk;
+  int my_e = 0;
+  float my_v = 0.f, v0 = 0.f;
+
+  __device__ __forceinline__ void round(int j, int lane, OneTables& tb) {
+    uint32_t m;
+    const int e = (int)rk.next(m);
+    const float v = key_value(m);
+    if (j == 0) v0 = v;
+    if (j == lane) {
+      my_e = e;
+      my_v = v;
+      tb.de_rank[j] = e;
+    }
   }
-}
+
+  // After the last round: the slots, the ascending table, and (workgroup 0)
+  // the routing result with the gates.
+  __device__ __forceinline__ void finish(const LayerArgs& a, int lane, OneTables& tb) {
+    const int k = a.k;
+    const int key = lane < k ? my_e : 0x7FFFFFFF;
+    int rank = 0;
+    for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(key, i) < key ? 1 : 0;
+    if (lane < k) {
+      tb.slot_of[lane] = rank;
+      tb.de_w[rank] = my_e;
+    }
+    if (blockIdx.x == 0) {
+      const float my_g = rank_gate(my_v, v0, k);
+      if (lane < k) {
+        const RouteArgs& r = a.route;
+        r.idx[lane] = my_e;
+        r.gates[lane] = my_g;
+        r.sorted_pairs[rank] = lane;
+        r.pair_slot[lane] = rank;
+        r.slot_gate[rank] = my_g;
+        r.slot_tok[rank] = 0;
+        r.dinfo[4 * rank + 0] = my_e;
+        r.dinfo[4 * rank + 1] = rank;
+        r.dinfo[4 * rank + 2] = 1;
+        r.dinfo[4 * rank + 3] = 0;
+      }
+    }
+  }
+};
 
 // Workgroup 0's counts and offsets of the fused routing (after a barrier that
 // makes wave 0's table visible).
@@ -340,7 +368,7 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 // (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
 template <int NXG>
 __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
-  __shared__ int de_w[kMaxK];  // the chosen experts in ascending order
+  __shared__ OneTables tb;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = H / 32;
@@ -369,15 +397,27 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     xv0 = ld16(a.x + 8 * cc0);
     xv1 = ld16(a.x + 8 * cc1);
   }
-  // Wave 0 ranks the logits while the other waves stage x; the barrier
-  // below publishes both.  (Every wave ranking for itself, which needs no
-  // barrier before its first loads, kept the SIMDs busy for 3-4 us: 16 waves
-  // a CU running the same six wave-wide reductions.)
+  // Wave 0 ranks the logits while the other waves stage x.  The first unit of
+  // every wave needs only the first `early` ranks: wave 0 stores those, the
+  // barrier that publishes x publishes them, every wave issues its first unit,
+  // and wave 0 ranks the rest while those loads are in flight; a second
+  // barrier publishes the remaining ranks and the slots.  (Every wave ranking
+  // for itself kept the SIMDs busy for 3-4 us: 16 waves a CU running the same
+  // wave-wide reductions.)
+  const int nunits = a.k * I;
+  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
+  const int early = ((nw < nunits ? nw : nunits) - 1) / I + 1;
+  OneRanking rank;
   if (w == 0) {
-    if (a.fused_route)
-      route_one_wave(a, lv, de_w);
-    else if (lane < a.k)
-      de_w[lane] = a.dinfo[4 * lane];
+    if (a.fused_route) {
+      rank.rk.init(lv, a.E, lane);
+      for (int j = 0; j < early; ++j) rank.round(j, lane, tb);
+    } else if (lane < a.k) {
+      const int e = a.dinfo[4 * lane];
+      tb.de_rank[lane] = e;
+      tb.slot_of[lane] = lane;
+      tb.de_w[lane] = e;
+    }
   }
 
   int gc[NXG], xo[NXG];
@@ -387,8 +427,6 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     gc[i] = g < CPR ? g : CPR - 1;
     xo[i] = g < CPR ? 4 * g : 4 * CPR;
   }
-  const int nunits = a.k * I;
-  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
   const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;  // units of this wave
   const int wbytes = I * (H / 2), sbytes = I * CPR;
 
@@ -397,8 +435,8 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     uint32_t s1[NXG], s3[NXG];
   };
   auto issue = [&](int f, Unit& B) {
-    const int u = wid + f * nw, d = u / I, r = u - d * I;
-    const int e = uniform(de_w[d]);
+    const int u = wid + f * nw, j = u / I, r = u - j * I;
+    const int e = uniform(tb.de_rank[j]);
     const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
     const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
     const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
@@ -413,7 +451,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     }
   };
   auto compute = [&](int f, const Unit& B) {
-    const int u = wid + f * nw, d = u / I, r = u - d * I;
+    const int u = wid + f * nw, j = u / I, r = u - j * I;
     float G = 0.f, U = 0.f;
 #pragma unroll
     for (int i = 0; i < NXG; ++i) {
@@ -427,7 +465,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     }
     G = wave_sum_f32(G);
     U = wave_sum_f32(U);
-    if (lane == 0) a.h[(size_t)d * I + r] = swiglu_bf16(G, U);
+    if (lane == 0) a.h[(size_t)uniform(tb.slot_of[j]) * I + r] = swiglu_bf16(G, U);
   };
 
   Unit A, B;
@@ -446,10 +484,17 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   if (c1 < nc) xl[c1] = xv1;
   if (tid < 4) xl[nc + tid] = zero4();
   lds_barrier();
-  if (a.fused_route && blockIdx.x == 0) publish_counts(a, de_w);
-  if (F == 0) return;
-  issue(0, A);
+  if (F > 0) issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
+  if (a.fused_route) {
+    if (w == 0) {
+      for (int j = early; j < a.k; ++j) rank.round(j, lane, tb);
+      rank.finish(a, lane, tb);
+    }
+    lds_barrier();
+    if (blockIdx.x == 0) publish_counts(a, tb.de_w);
+  }
+  if (F == 0) return;
 
   // Two register buffers; the loop body has no conditional loads, so each wait
   // is for the older buffer only and the next unit stays in flight.  The

@@ -38,26 +38,31 @@ __device__ __forceinline__ void wave_load_logits(const float* __restrict__ lrow,
   }
 }
 
-// One wave ranks the E logits of one token (vals as wave_load_logits leaves
-// them); lane j < k receives the expert of rank j and its gate.  Each round
-// takes the wave-wide maximum key (DPP), and among lanes holding it the lowest
-// expert id, then clears that entry.  Requires k <= E and all 64 lanes active.
+// A ranking in progress: one wave holds the E logits of one token (lane l the
+// keys of logits l, l+64, ... as wave_load_logits leaves them), and each call
+// of next() takes the largest remaining one: the wave-wide maximum key (DPP),
+// among lanes holding it the lowest expert id, which is then cleared.  Rounds
+// can be spread over a kernel's prologue.  Requires all 64 lanes active.
 template <int VPL>
-__device__ __forceinline__ void wave_topk_vals(const float (&vals)[VPL], int E, int k, int lane,
-                                               int& e_out, float& g_out) {
+struct WaveRanking {
   uint32_t keys[VPL];
+  int lane;
+
+  __device__ __forceinline__ void init(const float (&vals)[VPL], int E, int lane_) {
+    lane = lane_;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i)  // a mask, not a select: see wave_load_logits
-    keys[i] = order_key(vals[i]) & (0u - (uint32_t)(lane + kWave * i < E));
-  int my_e = 0;
-  float my_v = 0.f, v0 = 0.f, s = 0.f;
-  for (int j = 0; j < k; ++j) {
+    for (int i = 0; i < VPL; ++i)  // a mask, not a select: see wave_load_logits
+      keys[i] = order_key(vals[i]) & (0u - (uint32_t)(lane + kWave * i < E));
+  }
+
+  // The expert of the next rank (uniform over the wave); its key in m.
+  __device__ __forceinline__ uint32_t next(uint32_t& m) {
     uint32_t bk = 0;
     int bi = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (keys[i] > bk) { bk = keys[i]; bi = i; }  // strict: lower slot (lower id) wins ties
-    const uint32_t m = wave_max_u32(bk);
+    m = wave_max_u32(bk);
     const uint64_t tied = __ballot(bk == m);
     uint32_t e_win;
     if (__popcll(tied) == 1) {
@@ -71,16 +76,39 @@ __device__ __forceinline__ void wave_topk_vals(const float (&vals)[VPL], int E, 
       for (int i = 0; i < VPL; ++i)
         if (i == (int)(e_win >> 6)) keys[i] = 0u;
     }
+    return e_win;
+  }
+};
+
+// The softmax over the k chosen logits: lane j < k holds the logit of rank j
+// (my_v), v0 is the largest.  One exp per lane, and the denominator summed in
+// rank order from the lanes' terms.
+__device__ __forceinline__ float rank_gate(float my_v, float v0, int k) {
+  const float ev = expf(my_v - v0);
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ev), j));
+  return ev / s;
+}
+
+// One wave ranks the E logits of one token (vals as wave_load_logits leaves
+// them); lane j < k receives the expert of rank j and its gate.  Requires
+// k <= E and all 64 lanes active.
+template <int VPL>
+__device__ __forceinline__ void wave_topk_vals(const float (&vals)[VPL], int E, int k, int lane,
+                                               int& e_out, float& g_out) {
+  WaveRanking<VPL> rk;
+  rk.init(vals, E, lane);
+  int my_e = 0;
+  float my_v = 0.f, v0 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t m;
+    const uint32_t e_win = rk.next(m);
     const float v = key_value(m);
     if (j == 0) v0 = v;
     if (j == lane) { my_e = (int)e_win; my_v = v; }
   }
-  // lane j < k holds the j-th chosen logit; one exp per lane, and the softmax
-  // denominator summed in rank order from the lanes' terms
-  const float ev = expf(my_v - v0);
-  for (int j = 0; j < k; ++j) s += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ev), j));
   e_out = my_e;
-  g_out = ev / s;
+  g_out = rank_gate(my_v, v0, k);
 }
 
 // As wave_topk_vals, loading the logits itself.
