@@ -118,7 +118,8 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
                  void* ws, size_t ws_bytes, hipStream_t stream, uint16_t* h_out,
                  moe_fp4_route_out* route_out, const hipEvent_t* events,
                  float* saliency = nullptr, float* x_resid = nullptr,
-                 const SharedArgs* shared13 = nullptr, bool validate_only = false) {
+                 const SharedArgs* shared13 = nullptr, const SharedArgs* shared2 = nullptr,
+                 bool validate_only = false) {
   if (x_resid) {
     if (x) return MOE_FP4_EINVAL;
     y = x_resid;
@@ -224,6 +225,7 @@ int forward_impl(const moe_fp4_dims* dims, const uint16_t* x, const float* logit
     a.eps = kStackEps;
   }
   a.shared13 = shared13;
+  a.shared2 = shared2;
   if (saliency) {
     a.sal_part = at<float>(ws, L.sal);
     a.sal_tiles = sal_tiles(d.H);
@@ -312,7 +314,7 @@ int moe_fp4_forward_noalloc(const moe_fp4_dims* dims, const uint16_t* x, const f
   // Then the size rule.  All of it before the first HIP call.
   const int rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags,
                               reinterpret_cast<void*>(kAlign), 0, stream, nullptr, nullptr, nullptr,
-                              nullptr, nullptr, nullptr, /*validate_only=*/true);
+                              nullptr, nullptr, nullptr, nullptr, /*validate_only=*/true);
   if (rc != MOE_FP4_EWORKSPACE) return rc;
   if (layout(*dims, resolve_mode(*dims, mode)).total > kScratchBytes) return MOE_FP4_EWORKSPACE;
   hipError_t err = hipSuccess;
@@ -451,20 +453,22 @@ int moe_fp4_forward_shared(const moe_fp4_dims* dims, const uint16_t* x, const fl
   const moe_fp4_dims& d = *dims;
   if (rmode == MOE_FP4_MODE_DECODE && d.T == 1 && decode_one_token(d.T, d.H, d.I, d.k) &&
       sw->I <= d.H && ws && ws_bytes >= layout(d, rmode).total) {
-    // One token: the shared w1/w3 rows run in the routed w2 launch, their h in
-    // the pre-norm input's section (unused without a residual); then the
-    // shared w2 adds to y.  Same kernels' arithmetic, same bits.
+    // One token: the shared w1/w3 rows run in the routed w1/w3 launch, their
+    // h in the pre-norm input's section (unused without a residual), and the
+    // shared w2 rows in the routed w2 launch, added to the routed y.  The
+    // shared expert's own row arithmetic and the order of the two calls: the
+    // same bits.
     SharedArgs s13{};
     s13.act = x;
     s13.w[0] = sw->w1; s13.s[0] = sw->s1; s13.w[1] = sw->w3; s13.s[1] = sw->s3;
     s13.N = sw->I; s13.K = d.H; s13.T = 1;
     s13.h = at<uint16_t>(ws, layout(d, rmode).u);
-    rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
-                      nullptr, nullptr, nullptr, nullptr, &s13);
-    if (rc != MOE_FP4_OK) return rc;
-    return launch_shared_w2(s13.h, sw->w2, sw->s2, 1, d.H, sw->I, y, 1, stream) == hipSuccess
-               ? MOE_FP4_OK
-               : MOE_FP4_EHIP;
+    SharedArgs s2{};
+    s2.act = s13.h;
+    s2.w[0] = sw->w2; s2.s[0] = sw->s2;
+    s2.N = d.H; s2.K = sw->I; s2.T = 1; s2.accumulate = 1;
+    return forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
+                        nullptr, nullptr, nullptr, nullptr, &s13, &s2);
   }
   rc = forward_impl(dims, x, logits, nullptr, w, y, mode, flags, ws, ws_bytes, stream, nullptr,
                     nullptr, nullptr);

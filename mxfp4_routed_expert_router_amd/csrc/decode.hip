@@ -366,8 +366,20 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 // and keeps the next unit's loads in flight while it computes the current one.
 // A unit is one row of w1 and the same row of w3: NXG load instructions each
 // (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
-template <int NXG>
-__global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
+//
+// SH: the shared expert's w1/w3 rows too (sh: M = 2, T = 1).  They need no
+// routing, so they take the first two ring slots of waves 0 .. N_s - 1: the
+// first slot's loads go out at entry, while wave 0 ranks, and fill the time in
+// which routed rows cannot be addressed yet.  A shared row is two units of
+// the same shape as a routed one: part p holds, for each matrix, the 16-byte
+// chunks l + 64 (NXG p + i) of FP8 codes (lane l, i < NXG) and their scale
+// bytes.  The routed units take the remaining slots in order.  Both kinds
+// issue the same load instructions (only the bases and offsets differ), so the
+// waits of the ring stay exact.  The row's two sums run through its chunks in
+// the order shared_gemv_row takes them (fp8_chunk_dot each, x from LDS), then
+// the wave sums and swiglu_bf16: the shared expert's own bits.
+template <int NXG, bool SH>
+__global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, SharedArgs sh) {
   __shared__ OneTables tb;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
@@ -397,6 +409,21 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     xv0 = ld16(a.x + 8 * cc0);
     xv1 = ld16(a.x + 8 * cc1);
   }
+
+  // Work of the grid: S shared rows (two units each, in ring slots 0 and 1 of
+  // waves 0 .. S - 1) and k I routed units.  Routed unit ru is row ru % I of
+  // the expert of rank ru / I.
+  constexpr int SP = SH ? 2 : 0;
+  const int S = SH ? sh.N : 0;
+  const int nunits = a.k * I;
+  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
+  const int V = SP * S + nunits;
+  const int F = wid < V ? (V - 1 - wid) / nw + 1 : 0;  // units of this wave
+  const bool mine_sh = wid < S;                         // slots 0 and 1 are a shared row
+  auto routed_index = [&](int f) {
+    return wid + f * nw - (f < SP ? f : SP) * S - (f < SP ? (wid < S ? wid : S) : 0);
+  };
+
   // Wave 0 ranks the logits while the other waves stage x.  The first unit of
   // every wave needs only the first `early` ranks: wave 0 stores those, the
   // barrier that publishes x publishes them, every wave issues its first unit,
@@ -404,9 +431,8 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   // barrier publishes the remaining ranks and the slots.  (Every wave ranking
   // for itself kept the SIMDs busy for 3-4 us: 16 waves a CU running the same
   // wave-wide reductions.)
-  const int nunits = a.k * I;
-  const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
-  const int early = ((nw < nunits ? nw : nunits) - 1) / I + 1;
+  const int first_routed = (nw < V ? nw : V) - 1 - S;  // largest routed index in slot 0
+  const int early = first_routed >= 0 ? first_routed / I + 1 : 0;
   OneRanking rank;
   if (w == 0) {
     if (a.fused_route) {
@@ -427,31 +453,76 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
     gc[i] = g < CPR ? g : CPR - 1;
     xo[i] = g < CPR ? 4 * g : 4 * CPR;
   }
-  const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;  // units of this wave
   const int wbytes = I * (H / 2), sbytes = I * CPR;
+  // shared rows: chunk of part p, slot i at lane + 64 (NXG p + i), clamped
+  const int snc = SH ? sh.K / 16 : 1;
+  int shc[SP > 0 ? SP : 1][NXG];
+#pragma unroll
+  for (int p = 0; p < (SP > 0 ? SP : 1); ++p)
+#pragma unroll
+    for (int i = 0; i < NXG; ++i) {
+      const int c = lane + kWave * (NXG * p + i);
+      shc[p][i] = c < snc ? c : snc - 1;
+    }
+  float shG = 0.f, shU = 0.f;  // the shared row's sums, carried from part 0 to part 1
 
   struct Unit {
     u32x4 q1[NXG], q3[NXG];
     uint32_t s1[NXG], s3[NXG];
   };
   auto issue = [&](int f, Unit& B) {
-    const int u = wid + f * nw, j = u / I, r = u - j * I;
-    const int e = uniform(tb.de_rank[j]);
-    const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
-    const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
-    const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
-    const __amdgpu_buffer_rsrc_t q3 = rsrc(a.s3 + (size_t)e * a.stride[3], sbytes);
-    const int ow = r * (H / 2), os = r * CPR;
+    const bool is_sh = SH && f < SP && mine_sh;
+    const int ru = routed_index(f), j = ru / I, r = ru - j * I;
+    const int e = uniform(tb.de_rank[is_sh ? 0 : j]);
+    const uint8_t* b1 = a.w1 + (size_t)e * a.stride[0];
+    const uint8_t* b3 = a.w3 + (size_t)e * a.stride[2];
+    const uint8_t* p1 = a.s1 + (size_t)e * a.stride[1];
+    const uint8_t* p3 = a.s3 + (size_t)e * a.stride[3];
+    int ow = r * (H / 2), os = r * CPR, nb = wbytes, ns = sbytes;
+    if (SH && is_sh) {
+      b1 = sh.w[0];
+      b3 = sh.w[1];
+      p1 = sh.s[0];
+      p3 = sh.s[1];
+      ow = wid * sh.K;
+      os = (wid / 32) * (sh.K / 32);
+      nb = sh.N * sh.K;
+      ns = (sh.N / 32) * (sh.K / 32);
+    }
+    const __amdgpu_buffer_rsrc_t r1 = rsrc(b1, nb), r3 = rsrc(b3, nb);
+    const __amdgpu_buffer_rsrc_t q1 = rsrc(p1, ns), q3 = rsrc(p3, ns);
 #pragma unroll
     for (int i = 0; i < NXG; ++i) {
-      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, gc[i] * 16, ow, 0));
-      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, gc[i] * 16, ow, 0));
-      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, gc[i], os, 0);
-      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, gc[i], os, 0);
+      int vo = gc[i] * 16, vs = gc[i];
+      if (SH && is_sh) {
+        const int c = f == 0 ? shc[0][i] : shc[SP > 1 ? 1 : 0][i];
+        vo = c * 16;
+        vs = c / 2;
+      }
+      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, vo, ow, 0));
+      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, vo, ow, 0));
+      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, vs, os, 0);
+      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, vs, os, 0);
     }
   };
   auto compute = [&](int f, const Unit& B) {
-    const int u = wid + f * nw, j = u / I, r = u - j * I;
+    if (SH && f < SP && mine_sh) {
+#pragma unroll
+      for (int i = 0; i < NXG; ++i) {
+        const int c = lane + kWave * (NXG * f + i);
+        if (c < snc) {
+          const u32x4 xc[2] = {xl[2 * c], xl[2 * c + 1]};
+          shG = fp8_chunk_dot(B.q1[i], B.s1[i], xc, shG);
+          shU = fp8_chunk_dot(B.q3[i], B.s3[i], xc, shU);
+        }
+      }
+      if (f == SP - 1) {
+        const float r0 = wave_sum_f32(shG), r1 = wave_sum_f32(shU);
+        if (lane == 0) sh.h[wid] = swiglu_bf16(r0, r1);
+      }
+      return;
+    }
+    const int ru = routed_index(f), j = ru / I, r = ru - j * I;
     float G = 0.f, U = 0.f;
 #pragma unroll
     for (int i = 0; i < NXG; ++i) {
@@ -469,6 +540,10 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   };
 
   Unit A, B;
+  // a shared row's first part needs neither the ranking nor x: out at once
+  const bool first_now = SH && F > 0 && mine_sh;
+  if (first_now) issue(0, A);
+  __builtin_amdgcn_sched_barrier(0);
   if (a.xf) {
     // the layer's input is the pre-norm of the fp32 row xf, computed as
     // moe_fp4_prenorm_bf16 computes it (same ownership and order: same bits)
@@ -484,7 +559,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a) {
   if (c1 < nc) xl[c1] = xv1;
   if (tid < 4) xl[nc + tid] = zero4();
   lds_barrier();
-  if (F > 0) issue(0, A);
+  if (F > 0 && !first_now) issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
   if (a.fused_route) {
     if (w == 0) {
@@ -659,9 +734,22 @@ __global__ void __launch_bounds__(NW * kWave) gemv13_few_kernel(LayerArgs a) {
 // pairs t k .. t k + k - 1 through pair_slot; a row block's workgroups for all
 // tokens sit on one XCD (grid x a multiple of 8), so the w2 rows of an expert
 // that several tokens chose are read from HBM about once.
-template <int NPL, bool FEW>
-__device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int nblk, int tok) {
+//
+// SC > 0 (one token): the shared expert's w2 rows [m0, m1) too (sh: M = 1,
+// SC chunks a lane covering its whole row).  Wave w takes rows m0 + w + 8 i,
+// kShRows at a time; their loads (and those of the shared h) go out at entry
+// beside the routed ones, and they are evaluated after the routed rows as
+// shared_gemv_row evaluates them (fp8_chunk_dot per chunk, then the wave sum),
+// then added to the routed result: y = routed + shared, the order of the
+// routed layer followed by the shared expert accumulating into y.
+constexpr int kShRows = 3;
+constexpr int kShMaxChunks = 4;  // chunks a lane of a shared w2 row in this kernel (K <= 4096)
+
+template <int NPL, bool FEW, int SC = 0>
+__device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int nblk, int tok,
+                                               const SharedArgs& sh = SharedArgs{}) {
   __shared__ float part[kWaves][kOneRowsMax];
+  __shared__ float shr[SC > 0 ? kOneRowsMax : 1];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = I / 32;
@@ -707,6 +795,40 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
     }
   }
 
+  // the shared rows' loads: weights of up to kShRows rows, and the shared h
+  // chunks (the same for every row)
+  constexpr int SCN = SC > 0 ? SC : 1;
+  const int NCs = SC > 0 ? sh.K / 16 : 0;
+  u32x4 sw[kShRows][SCN], sx[SCN][2];
+  uint32_t ss[kShRows][SCN];
+  int scc[SCN];
+  auto sh_load = [&](int m_first) {
+#pragma unroll
+    for (int j = 0; j < SCN; ++j) {
+      const int c = lane + kWave * j;
+      scc[j] = c < NCs ? c : NCs - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < kShRows; ++i) {
+      const int n = min(m_first + kWaves * i, m1 - 1);  // past the end: a row already loaded
+#pragma unroll
+      for (int j = 0; j < SCN; ++j) {
+        sw[i][j] = ld16(sh.w[0] + (size_t)n * sh.K + (size_t)scc[j] * 16);
+        ss[i][j] = sh.s[0][(n / 32) * (sh.K / 32) + scc[j] / 2];
+      }
+    }
+  };
+  if constexpr (SC > 0) {
+#pragma unroll
+    for (int j = 0; j < SCN; ++j) {
+      const int c = lane + kWave * j;
+      const int cc = c < NCs ? c : NCs - 1;
+      sx[j][0] = ld16(sh.act + (size_t)cc * 16);
+      sx[j][1] = ld16(sh.act + (size_t)cc * 16 + 8);
+    }
+    sh_load(m0 + w);
+  }
+
   const size_t wrow = I / 2;
   u32x4 qb[kOneDP][NPL];
   uint32_t sb[kOneDP][NPL];
@@ -744,35 +866,41 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (SC > 0) {
+    // the shared rows of this wave, kShRows at a time (one batch at the real
+    // shape: 20 rows a workgroup)
+    for (int mb = m0 + w; mb < m1; mb += kWaves * kShRows) {
+      if (mb != m0 + w) sh_load(mb);
+#pragma unroll
+      for (int i = 0; i < kShRows; ++i) {
+        const int n = mb + kWaves * i;
+        if (n < m1) {
+          float acc = 0.f;
+#pragma unroll
+          for (int j = 0; j < SCN; ++j)
+            if (lane + kWave * j < NCs) acc = fp8_chunk_dot(sw[i][j], ss[i][j], sx[j], acc);
+          acc = wave_sum_f32(acc);
+          if (lane == 0) shr[n - m0] = acc;
+        }
+      }
+    }
+  }
   lds_barrier();
   if (tid < m1 - m0) {
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) s += part[q][tid];
     float* yp = a.y + (size_t)tok * H + m0 + tid;
-    *yp = a.accumulate ? *yp + s : s;
+    float v = a.accumulate ? *yp + s : s;
+    if constexpr (SC > 0) v = v + shr[tid];
+    *yp = v;
   }
 }
 
 // Workgroup b of nb takes rows b R .. (b + 1) R - 1 of y (R = H / nb rounded up).
-template <int NPL, bool FEW>
-__global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a) {
-  gemv2_one_body<NPL, FEW>(a, blockIdx.x, gridDim.x, FEW ? (int)blockIdx.y : 0);
-}
-
-// The one-token w2 (workgroups below n2, as gemv2_one_kernel) and, in the same
-// launch, the shared expert's w1/w3 rows, one wave a row (the rest): those need
-// only x, and the w2 workgroups, one a compute unit, leave most of each CU's
-// waves free while their row loads are in flight.
-template <int NPL, int SC>
-__global__ void __launch_bounds__(kThreads) gemv2_one_shared_kernel(LayerArgs a, SharedArgs s,
-                                                                     int n2) {
-  if ((int)blockIdx.x < n2) {
-    gemv2_one_body<NPL, false>(a, blockIdx.x, n2, 0);
-    return;
-  }
-  const int n = ((int)blockIdx.x - n2) * kWaves + (int)(threadIdx.x / kWave);
-  if (n < s.N) shared_gemv_row<2, SC>(s, n, threadIdx.x & (kWave - 1));
+template <int NPL, bool FEW, int SC>
+__global__ void __launch_bounds__(kThreads) gemv2_one_kernel(LayerArgs a, SharedArgs sh) {
+  gemv2_one_body<NPL, FEW, SC>(a, blockIdx.x, gridDim.x, FEW ? (int)blockIdx.y : 0, sh);
 }
 
 // Workgroups of `kernel` (`threads` threads, `lds` bytes of dynamic LDS) that the
@@ -809,60 +937,100 @@ Residency residency(const void* kernel, size_t lds, int threads = kThreads) {
   return r;
 }
 
-template <int NXG>
-const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NXG>); }
+template <int NXG, bool SH>
+const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NXG, SH>); }
+
+// The one-token w1/w3 kernel for (NXG, SH): its address, or its launch.
+template <bool SH>
+const void* k13_one_sh(int nxg) {
+  return nxg == 1 ? k13_one<1, SH>() : nxg == 2 ? k13_one<2, SH>() : nxg == 3 ? k13_one<3, SH>()
+                                                                              : k13_one<4, SH>();
+}
+template <bool SH>
+void launch13_one(int nxg, dim3 g, const LayerArgs& a, const SharedArgs& sh, hipStream_t stream) {
+  const dim3 blk(kThreads);
+  const hipEvent_t e0 = ev_start(a.ev, 1), e1 = ev_stop(a.ev, 1);
+  switch (nxg) {
+    case 1: launch_k(gemv13_one_kernel<1, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 2: launch_k(gemv13_one_kernel<2, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 3: launch_k(gemv13_one_kernel<3, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    default: launch_k(gemv13_one_kernel<4, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+  }
+}
+template <int NPL, bool FEW, int SC>
+void launch2_one(dim3 g, const LayerArgs& a, const SharedArgs& sh, hipStream_t stream) {
+  launch_k(gemv2_one_kernel<NPL, FEW, SC>, g, dim3(kThreads), 0, stream, ev_start(a.ev, 2),
+           ev_stop(a.ev, 2), a, sh);
+}
+
+// Chunks a lane of a shared-expert row of K inputs takes when the one-token
+// launches carry it (the whole row in one round, at most maxc), or 0 when they
+// cannot.
+int shared_one_chunks(int K, int maxc) {
+  const int ncl = (K / 16 + kWave - 1) / kWave;
+  return ncl <= maxc ? ncl : 0;
+}
+// A shared w1/w3 row of K = H inputs fits two units of the w1/w3 kernel.
+bool shared13_fits(int H) { return shared_one_chunks(H, 2 * one_xg(H)) > 0; }
 
 hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
-  const hipEvent_t* ev = a.ev;
   const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
-  const void* k13 = nxg == 1 ? k13_one<1>() : nxg == 2 ? k13_one<2>() : nxg == 3 ? k13_one<3>()
-                                                                             : k13_one<4>();
-  const Residency res = residency(k13, 0);
-  if (res.wgs <= 0) return hipErrorInvalidValue;
-  const int units = a.k * a.I;
-  const dim3 blk(kThreads), g13(std::min(res.wgs, (units + kWaves - 1) / kWaves));
-  const hipEvent_t e0 = ev_start(ev, 1), e1 = ev_stop(ev, 1);
-  switch (nxg) {
-    case 1: launch_k(gemv13_one_kernel<1>, g13, blk, 0, stream, e0, e1, a); break;
-    case 2: launch_k(gemv13_one_kernel<2>, g13, blk, 0, stream, e0, e1, a); break;
-    case 3: launch_k(gemv13_one_kernel<3>, g13, blk, 0, stream, e0, e1, a); break;
-    default: launch_k(gemv13_one_kernel<4>, g13, blk, 0, stream, e0, e1, a); break;
+  const SharedArgs none{};
+  // With a shared expert (a.shared13, a.shared2) its rows ride in the two
+  // launches when they fit: a w1/w3 row in two units, a w2 row in one round
+  // of kShMaxChunks chunks a lane, one wave for every shared w1/w3 row and
+  // every wave below the row count owning ring slots 0 and 1 (W <= S + routed
+  // units).  Otherwise the shared expert's own kernels run after the layer.
+  bool shared = a.shared13 != nullptr;
+  const int routed = a.k * a.I, S = shared ? a.shared13->N : 0;
+  int sc2 = shared ? shared_one_chunks(a.shared2->K, kShMaxChunks) : 0;
+  bool carry = shared && shared13_fits(a.shared13->K) && sc2 > 0;
+  Residency res{};
+  int want = 0;
+  if (carry) {
+    res = residency(k13_one_sh<true>(nxg), 0);
+    want = std::min(res.wgs, (S + routed) / kWaves);
+    carry = res.wgs > 0 && want * kWaves >= S;
   }
+  if (shared && !carry) {
+    LayerArgs b = a;
+    b.shared13 = b.shared2 = nullptr;
+    const hipError_t e = launch_one(b, stream);
+    if (e != hipSuccess) return e;
+    const SharedArgs &s13 = *a.shared13, &s2 = *a.shared2;
+    const uint8_t* const t[6] = {s13.w[0], s13.s[0], s13.w[1], s13.s[1], s2.w[0], s2.s[0]};
+    return launch_shared(s13.act, t, 1, s13.K, s13.N, a.y, 1, s13.h, stream);
+  }
+  // w1/w3: as many workgroups as are resident
+  if (!carry) {
+    res = residency(k13_one_sh<false>(nxg), 0);
+    want = std::min(res.wgs, (routed + kWaves - 1) / kWaves);
+  }
+  if (res.wgs <= 0) return hipErrorInvalidValue;
+  const dim3 g13(std::max(1, want));
+  if (shared)
+    launch13_one<true>(nxg, g13, a, *a.shared13, stream);
+  else
+    launch13_one<false>(nxg, g13, a, none, stream);
   // w2: one workgroup per compute unit, at most kOneRowsMax rows each
   const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
   const dim3 g2(n2);
-  if (a.shared13) {
-    // the shared expert's w1/w3 rows ride along: one wave a row after the n2
-    // w2 workgroups, with the chunk count its own kernel would take
-    const SharedArgs& s = *a.shared13;
-    const int ncl = std::min((s.K / 16 + kWave - 1) / kWave, kGvMaxChunks);
-    const dim3 gs(n2 + (s.N + kWaves - 1) / kWaves);
-#define MOE_W2S(NPL, SC) \
-  launch_k(gemv2_one_shared_kernel<NPL, SC>, gs, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a, s, n2)
-#define MOE_W2S_NPL(NPL)                                                              \
-  switch (ncl) {                                                                     \
-    case 1: MOE_W2S(NPL, 1); break;                                                  \
-    case 2: MOE_W2S(NPL, 2); break;                                                  \
-    case 3: MOE_W2S(NPL, 3); break;                                                  \
-    case 4: MOE_W2S(NPL, 4); break;                                                  \
-    case 5: MOE_W2S(NPL, 5); break;                                                  \
-    case 6: MOE_W2S(NPL, 6); break;                                                  \
-    case 7: MOE_W2S(NPL, 7); break;                                                  \
-    default: MOE_W2S(NPL, 8); break;                                                 \
+  if (!shared) {
+    if (npl == 1)
+      launch2_one<1, false, 0>(g2, a, none, stream);
+    else
+      launch2_one<2, false, 0>(g2, a, none, stream);
+  } else if (sc2 <= 3) {
+    if (npl == 1)
+      launch2_one<1, false, 3>(g2, a, *a.shared2, stream);
+    else
+      launch2_one<2, false, 3>(g2, a, *a.shared2, stream);
+  } else {
+    if (npl == 1)
+      launch2_one<1, false, kShMaxChunks>(g2, a, *a.shared2, stream);
+    else
+      launch2_one<2, false, kShMaxChunks>(g2, a, *a.shared2, stream);
   }
-    if (npl == 1) {
-      MOE_W2S_NPL(1)
-    } else {
-      MOE_W2S_NPL(2)
-    }
-#undef MOE_W2S_NPL
-#undef MOE_W2S
-    return hipSuccess;
-  }
-  if (npl == 1)
-    launch_k(gemv2_one_kernel<1, false>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
-  else
-    launch_k(gemv2_one_kernel<2, false>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
   return hipSuccess;
 }
 
@@ -919,10 +1087,11 @@ hipError_t launch_few(const LayerArgs& a, hipStream_t stream) {
   int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, cus));
   n2 = (n2 + 7) / 8 * 8;
   const dim3 g2(n2, a.T);
+  const SharedArgs none{};
   if (npl == 1)
-    launch_k(gemv2_one_kernel<1, true>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+    launch2_one<1, true, 0>(g2, a, none, stream);
   else
-    launch_k(gemv2_one_kernel<2, true>, g2, blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+    launch2_one<2, true, 0>(g2, a, none, stream);
   return hipSuccess;
 }
 
@@ -937,6 +1106,7 @@ bool decode_fits(int T, int H, int I, int k) {
 }
 
 bool decode_one_token(int T, int H, int I, int k) { return T == 1 && one_token_fits(H, I, k); }
+
 
 int decode_family(int T, int H, int I, int k) {
   if (T == 1 && one_token_fits(H, I, k)) return 1;

@@ -97,9 +97,12 @@ struct LayerArgs {
   // unused and the layer's input is bf16(xf / sqrt(mean(xf^2) + eps))
   const float* xf;
   float eps;
-  // one-token decode: the shared expert's w1/w3 (M = 2, T = 1), run in the
-  // routed w2 launch; host memory, read when launching (null: none)
+  // one-token decode with the shared expert: its w1/w3 rows (M = 2, T = 1) run
+  // in the routed w1/w3 launch and its w2 rows (M = 1, T = 1, accumulating
+  // into y) in the routed w2 launch; host memory, read when launching (null:
+  // none; both or neither)
   const SharedArgs* shared13;
+  const SharedArgs* shared2;
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);

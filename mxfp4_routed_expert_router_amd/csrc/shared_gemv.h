@@ -23,6 +23,18 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4& v, float scale, bf16
 }
 
 
+// acc + (16 E4M3 codes times their block scale byte) . (16 bf16 inputs, two
+// 16-byte chunks): the first eight products, then the last eight, each through
+// dot8_bf16.  Every kernel that evaluates a shared-expert row does its chunks
+// through this, so they give the same bits.
+__device__ __forceinline__ float fp8_chunk_dot(const u32x4& w, uint32_t scale_byte,
+                                               const u32x4 (&x)[2], float acc) {
+  bf16x8 lo, hi;
+  fp8x16_to_bf16(w, ue8m0_to_f32(scale_byte), lo, hi);
+  acc = dot8_bf16(lo, as_bf16x8(x[0]), acc);
+  return dot8_bf16(hi, as_bf16x8(x[1]), acc);
+}
+
 constexpr int kGvMaxT = 4;
 constexpr int kGvMaxChunks = 8;  // 16-byte chunks per lane and round (K <= 8192 in one round)
 
@@ -69,12 +81,7 @@ __device__ __forceinline__ void shared_gemv_row(const SharedArgs& a, int n, int 
       for (int j = 0; j < kGvChunks; ++j)
         if (g0 + j < NCL && lane + kWave * (g0 + j) < NC)
 #pragma unroll
-          for (int m = 0; m < M; ++m) {
-            bf16x8 lo, hi;
-            fp8x16_to_bf16(wv[m][j], ue8m0_to_f32(sv[m][j]), lo, hi);
-            acc[m][t] = dot8_bf16(lo, as_bf16x8(xv[j][0]), acc[m][t]);
-            acc[m][t] = dot8_bf16(hi, as_bf16x8(xv[j][1]), acc[m][t]);
-          }
+          for (int m = 0; m < M; ++m) acc[m][t] = fp8_chunk_dot(wv[m][j], sv[m][j], xv[j], acc[m][t]);
     }
   }
 #pragma unroll

@@ -68,7 +68,7 @@ def test_shared_expert(moe, orc, T, H, I):
 def test_forward_shared(moe, orc, mode, T):
     """forward_shared is forward followed by the shared expert added to y (bit
     for bit), and matches the oracle's routed layer plus its shared expert.
-    One token runs the shared w1/w3 rows inside the routed w2 launch."""
+    One token carries the shared rows in the routed launches."""
     import torch
     H, I, E, k = (256, 128, 16, 2) if mode == 1 else (256, 128, 24, 6)
     say(f"forward_shared T={T} mode={mode}")
@@ -93,8 +93,8 @@ def test_forward_shared(moe, orc, mode, T):
 
 
 def test_forward_shared_one_token_accumulate(moe, orc):
-    """One token with MOE_FP4_ACCUMULATE (the shared w1/w3 rows inside the
-    routed w2 launch): y0 + layer + shared expert, bit for bit the separate
+    """One token with MOE_FP4_ACCUMULATE (the shared rows carried in the
+    routed launches): y0 + layer + shared expert, bit for bit the separate
     calls', and the oracle's sum to the layer tolerance."""
     import torch
     T, H, I, E, k = 1, 512, 256, 12, 3
@@ -122,6 +122,33 @@ def test_forward_shared_one_token_accumulate(moe, orc):
     check_y(ya, ref, "forward_shared T=1 accumulate")
 
 
+@pytest.mark.parametrize("H", [1024, 2048, 3072, 4096, 5120])
+def test_forward_shared_one_token_row_parts(moe, orc, H):
+    """One token: a shared w1/w3 row is carried as two units of the routed
+    w1/w3 kernel (its 16-byte chunks split 1+0, 1+1, 2+1, 2+2 and 3+2 per lane
+    over these H).  Bit for bit the separate calls, and the oracle's sum."""
+    import torch
+    T, I, E, k = 1, 256, 8, 2
+    say(f"forward_shared T=1 H={H}")
+    rng = np.random.default_rng(H)
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    dense = {n: np.stack([experts[e][n] for e in range(E)]) for n in experts[0]}
+    w = dev_weights(dense)
+    sw = pins.random_shared(rng, H, 384)
+    dsw = _dev_shared(moe, sw)
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    xd, lgd = dev_bits(x), torch.from_numpy(lg).cuda()
+    y = moe.moe_fp4_forward_shared(xd, lgd, w, dsw, k, mode=1)
+    y1 = moe.moe_fp4_forward(xd, lgd, w, k, mode=1)
+    y1, _ = moe.moe_fp4_shared_expert(xd, dsw, y=y1, accumulate=True)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y1.cpu().numpy().view(np.uint32))
+    ref = orc.forward(H, I, E, k, x, lg, experts)["y"].astype(np.float64) + orc.shared(x, sw)["y"]
+    check_y(y, ref, f"forward_shared T=1 H={H}")
+
+
 def test_forward_shared_decode_real_shape(moe, orc):
     """One token at the real shape: 6 of 384 routed experts plus the shared expert."""
     import torch
@@ -131,9 +158,12 @@ def test_forward_shared_decode_real_shape(moe, orc):
     sw = synth.gen_shared(wl)
     x = synth.gen_x(wl, 5)
     lg = synth.gen_logits(wl, 5)
-    y = moe.moe_fp4_forward_shared(dev_bits(x), torch.from_numpy(lg).cuda(), w, _dev_shared(moe, sw),
-                                   wl.k)
+    dsw, xd, lgd = _dev_shared(moe, sw), dev_bits(x), torch.from_numpy(lg).cuda()
+    y = moe.moe_fp4_forward_shared(xd, lgd, w, dsw, wl.k)
+    y1 = moe.moe_fp4_forward(xd, lgd, w, wl.k)
+    y1, _ = moe.moe_fp4_shared_expert(xd, dsw, y=y1, accumulate=True)
     torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y1.cpu().numpy().view(np.uint32))
     idx, _ = orc.route(lg, wl.k)
     experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in idx[0]}
     ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, experts)["y"].astype(np.float64)
