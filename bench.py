@@ -372,6 +372,9 @@ def main():
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router, shared-expert, verify and stack figures (profiling runs)")
+    ap.add_argument("--eager", action="store_true",
+                    help="no graph capture: the cold value is the mean span of eager steps, from "
+                         "the first kernel's start to the last one's end (counter-collection runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -467,11 +470,12 @@ def main():
         sweep()
         step(args.warmup + n)
 
-    g_cold = graph_of(cold_step, args.steps)
-    g_sweep = graph_of(lambda n: sweep(), args.steps)
-    t_cold, t_sweep = replay_us(g_cold), replay_us(g_sweep)
-    us_tok = (t_cold - t_sweep) / args.steps / wl.T
-    del g_cold, g_sweep
+    if not args.eager:
+        g_cold = graph_of(cold_step, args.steps)
+        g_sweep = graph_of(lambda n: sweep(), args.steps)
+        t_cold, t_sweep = replay_us(g_cold), replay_us(g_sweep)
+        us_tok = (t_cold - t_sweep) / args.steps / wl.T
+        del g_cold, g_sweep
     # kernel durations for the roofline: the same cold steps run eagerly, each
     # kernel's dispatch recording its own start and end events
     # (moe_fp4_forward_profiled); warm-up steps are cold too, so every launch of
@@ -484,6 +488,11 @@ def main():
         step(i, evc[n])
     torch.cuda.synchronize()
     del fbuf, fsink
+    if args.eager:
+        ev = [e.events for e in evc]
+        span = np.array([e[2].elapsed_time(e[5]) for e in ev]) * 1e3   # w1/w3 start -> w2 end
+        us_tok = float(span.mean()) / wl.T
+        t_cold, t_sweep = us_tok * wl.T * args.steps, 0.0
     st = np.array([e.stage_ms() for e in evc]) * 1e3                   # [steps, 4] us
     k_us = {"route": float(st[:, 0].mean()), "w13": float(st[:, 1].mean()),
             "w2": float(st[:, 2].mean())}
@@ -514,7 +523,7 @@ def main():
     warm = None
     routed = shared = None
     verify, stack = {}, {}
-    if not args.no_warm:
+    if not args.no_warm and not args.eager:
         us_warm = graph_us(step)
         evs = [moe.StageEvents() for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -632,12 +641,15 @@ def main():
                      "bytes_per_launch": k_bytes[dom], "avg_us": k_us[dom],
                      "note": "cold launches (L2 and MALL flushed before each step)"},
         "kernels_us": {n: round(v, 3) for n, v in k_us.items()},
-        "timing": "value: the timed steps, each on a fresh token after a 1 GiB read-only sweep that "
+        "timing": ("value (--eager): mean span from the start of each cold step's first kernel to "
+                   "the end of its last (per-dispatch events), each step after a 1 GiB read-only "
+                   "sweep" if args.eager else
+                   "value: the timed steps, each on a fresh token after a 1 GiB read-only sweep that "
                   "leaves L2 and the MALL cold, captured in one HIP graph and replayed; minus the "
                   "same graph of sweeps alone; divided by the steps.  Kernel durations (roofline): "
                   "the same cold steps run eagerly with start/end events recorded by each kernel's "
                   "own dispatch.  The one-token routing runs inside the w1/w3 kernel and its bytes "
-                  "(the logits) are counted there",
+                  "(the logits) are counted there"),
         "warm": warm,
         "stream_read": stream,
         "decode_routed": routed,
