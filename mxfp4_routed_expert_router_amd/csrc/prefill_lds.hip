@@ -85,11 +85,53 @@ __device__ __forceinline__ void wait_step(int hb, int NHB, int NB, bool xw) {
     wait_n<0>();
 }
 
+// Weight block b (256 inputs) of the wave's tiles into stage b % 3, and for b
+// even the scale bytes of blocks b and b + 1 into pair slot (b / 2) % 2.
+// Scale lanes: tile row lane % 16, dword lane / 16 of a block pair's 16 bytes
+// (dwords 2, 3 belong to the odd block; past the last block a lane re-reads
+// the even block's).
+template <class C, int M, int kRT>
+__device__ __forceinline__ void issue_wblock(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
+                                             const uint8_t* const (&srow0)[M][kRT], size_t wrow,
+                                             size_t srow, int b, int NB) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c16 = lane & 15, kb = lane >> 4;
+  const int wr_r = lane >> 3, wr_c0 = wtile_chunk(lane, 0), wr_c1 = wtile_chunk(lane, 1);
+  const int s = b % 3;
+  const bool even = (b & 1) == 0;
+  const int so = b * 8 + 4 * (b + 1 < NB ? kb : kb & 1);
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      uint8_t* const dst = &sm.w[s][w][m * kRT + rt][0];
+      const uint8_t* const g = wrow0[m][rt] + (size_t)b * 128;
+      lds_load16(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
+      lds_load16(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
+      if (even)
+        lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
+    }
+}
+
+// Weight blocks 0 and 1 of a pass: they need only the expert and the rows, so
+// the kernels issue them before the token rows of the pass are known.
+template <class C, int M, int kRT>
+__device__ __forceinline__ void issue_first_wblocks(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
+                                                    const uint8_t* const (&srow0)[M][kRT],
+                                                    size_t wrow, size_t srow, int K) {
+  const int NB = K / kKB;
+  issue_wblock<C, M, kRT>(sm, wrow0, srow0, wrow, srow, 0, NB);
+  if (NB > 1) issue_wblock<C, M, kRT>(sm, wrow0, srow0, wrow, srow, 1, NB);
+}
+
 // One pass over all K (a multiple of 256) for up to NT*16 staged token rows of
 // src (row length ld = K): acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].
 // wrow0[m][rt] points at row 0 of the wave's 16-row tile (inside the weights
 // even for a tile past the end, whose results are not stored), srow0 at that
-// row's scales.  Tokens past nc read token 0's row.
+// row's scales.  Tokens past nc read token 0's row.  The caller has issued
+// weight blocks 0 and 1 (issue_first_wblocks) before the pass's token rows
+// were staged.
 template <class C, int M, int kRT, int NT>
 __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
                                               const uint8_t* const (&srow0)[M][kRT], size_t wrow,
@@ -107,7 +149,6 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[m][rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int wr_r = lane >> 3, wr_c0 = wtile_chunk(lane, 0), wr_c1 = wtile_chunk(lane, 1);
   // activation lanes: quarter q covers tokens 8 w + 4 q + lane / 16, slot lane % 16
   const bool xw = 8 * w < 16 * NT;  // this wave stages tokens that are read
   const uint8_t* xsrc[2];
@@ -118,25 +159,7 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
               ((c16 ^ xsw(t)) << 4);
   }
 
-  // scale lanes: tile row lane % 16, dword lane / 16 of a block pair's 16
-  // bytes (dwords 2, 3 belong to the odd block; past the last block a lane
-  // re-reads the even block's)
-  auto issue_w = [&](int b) {
-    const int s = b % 3;
-    const bool even = (b & 1) == 0;
-    const int so = b * 8 + 4 * (b + 1 < NB ? kb : kb & 1);
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        uint8_t* const dst = &sm.w[s][w][m * kRT + rt][0];
-        const uint8_t* const g = wrow0[m][rt] + (size_t)b * 128;
-        lds_load16(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
-        lds_load16(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
-        if (even)
-          lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
-      }
-  };
+  auto issue_w = [&](int b) { issue_wblock<C, M, kRT>(sm, wrow0, srow0, wrow, srow, b, NB); };
   auto issue_x = [&](int hb) {
     if (!xw) return;
     uint8_t* const dst = &sm.x[hb % 3][0];
@@ -175,16 +198,24 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
     }
   };
 
-  // Issue order: W0 X0 W1 X1, then per step hb: X(hb + 2), and for hb even
-  // W(hb/2 + 2).  At step hb, X(hb) (and W(hb/2), which precedes it) were
-  // issued before W((hb + 1)/2 + 1) and X(hb + 1), the loads wait_step leaves
-  // in flight: two weight blocks are in flight during each step.
-  issue_w(0);
+  // Issue order: W0 W1 (by the caller) X0 X1, then per step hb: X(hb + 2), and
+  // for hb even W(hb/2 + 2).  At step hb > 0, X(hb) (and W(hb/2), which
+  // precedes it) were issued before W((hb + 1)/2 + 1) and X(hb + 1), the loads
+  // wait_step leaves in flight: two weight blocks are in flight during each
+  // step.  At step 0 only X1 follows X0 (W1 came first).
   issue_x(0);
-  if (NB > 1) issue_w(1);
   issue_x(1);
   for (int hb = 0; hb < NHB; ++hb) {
-    wait_step(hb, NHB, NB, xw);
+    if (hb == 0) {
+      if (xw && NHB > 1)
+        wait_n<kXLoads>();
+      else if (!xw && NB > 1)
+        wait_n<kWLoadsOdd>();
+      else
+        wait_n<0>();
+    } else {
+      wait_step(hb, NHB, NB, xw);
+    }
     // every wave is past step hb - 1: its slots (x (hb - 1) % 3, and for hb
     // even the weight slot of block hb/2 - 1, and the scale pair slot of
     // blocks hb/2 - 2 and hb/2 - 1) may be loaded again
@@ -217,10 +248,20 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
                                    {a.w3 + (size_t)e * a.stride[2] + ro * wrow}};
   const uint8_t* const sr[2][1] = {{a.s1 + (size_t)e * a.stride[1] + ro * srow},
                                    {a.s3 + (size_t)e * a.stride[3] + ro * srow}};
+  const int NB = a.H / kKB;
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
-    if (tid < nc) sm.row[tid] = a.slot_tok[off + c0 + tid];
-    lds_barrier();
+    // The pass's token rows go to LDS by a DMA load of wave 0 issued before
+    // weight blocks 0 and 1 (which need only the expert and the rows), so the
+    // wait for the rows leaves the weights in flight and the activation loads
+    // can follow while block 0 travels.
+    static_assert(kTok <= kWave, "one row-table load per pass");
+    if (w == 0) lds_load4(lds_addr(&sm.row[0]), a.slot_tok + off + c0 + min(lane, nc - 1));
+    issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
+    if (NB > 1)
+      wait_n<kWLoads + kWLoadsOdd>();
+    else
+      wait_n<kWLoads>();
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[2][1][NT];
@@ -280,6 +321,7 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
   }
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
+    issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
     if (tid < nc) sm.row[tid] = off + c0 + tid;
     lds_barrier();
     auto pass = [&](auto nt_const) {
