@@ -6,11 +6,12 @@
 // one wave in a fixed order, so the logits -- and the routing taken from
 // them -- are the same bits on every run.
 //
-//   router_gemv_kernel  T <= 4: one wave per expert row.  Lane l takes the
-//                       16-byte chunks l + 64 j of the row (whole 128-byte
-//                       lines per load), all issued before the first use;
-//                       the token rows are read the same way (L2-served after
-//                       the first wave) and the wave reduces with DPP.
+//   router_gemv_kernel  T <= 4: one wave per expert row, four rows a
+//                       workgroup.  Lane l takes the 16-byte chunks l + 64 j
+//                       of the row (whole 128-byte lines per load), all issued
+//                       before the first use; the token rows are read the same
+//                       way (L2-served after the first wave) and the wave
+//                       reduces with DPP.
 //   router_gemm_kernel  T > 4: 64 experts x 64 tokens per workgroup, four
 //                       waves of 16 experts; K in blocks of 64 staged through
 //                       a double-buffered LDS tile; 16x16x32 bf16 MFMA.
@@ -23,11 +24,14 @@ namespace {
 constexpr int kGemvMaxT = 4;
 constexpr int kGemvChunks = 16;  // 16-byte chunks per lane in flight (H <= 8192 in one round)
 
-__global__ void __launch_bounds__(kWave) router_gemv_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w,
-                                                            float* __restrict__ logits, int T,
-                                                            int H, int E) {
-  const int e = blockIdx.x, lane = threadIdx.x;
+constexpr int kGemvRows = 4;  // expert rows (waves) per workgroup
+
+__global__ void __launch_bounds__(kGemvRows * kWave) router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                                         const uint16_t* __restrict__ w,
+                                                                         float* __restrict__ logits,
+                                                                         int T, int H, int E) {
+  const int e = blockIdx.x * kGemvRows + (int)(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
+  if (e >= E) return;  // whole wave
   const int NC = H / 8;                                   // chunks per row
   const int NCL = (NC + kWave - 1) / kWave;               // chunks per lane
   const uint16_t* const wr = w + (size_t)e * H;
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(kRThreads) router_gemm_kernel(const uint16_t* 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,
                                 int E, hipStream_t stream) {
   if (T <= kGemvMaxT)
-    hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(kWave), 0, stream, x, w, logits, T, H, E);
+    hipLaunchKernelGGL(router_gemv_kernel, dim3((E + kGemvRows - 1) / kGemvRows), dim3(kGemvRows * kWave),
+                       0, stream, x, w, logits, T, H, E);
   else
     hipLaunchKernelGGL(router_gemm_kernel, dim3((E + kRT - 1) / kRT, (T + kRT - 1) / kRT),
                        dim3(kRThreads), 0, stream, x, w, logits, T, H, E);
