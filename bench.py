@@ -69,23 +69,31 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
                                "moe_layer_decode_T1_prefill_T2048_hbm_traffic.md")
 
 
-def profiled_traffic(kernel):
-    """HBM bytes (read + written) per launch of `kernel` from the committed
-    rocprofv3 PMC summary (FETCH_SIZE / WRITE_SIZE scaled by a device-copy
-    calibration), or None when the library sources differ from the ones the
-    counters were taken with."""
+# The sources the decode kernels are compiled from (decode.hip and the headers
+# it includes): the traffic record of a decode kernel holds while they do.
+DECODE_SOURCES = ("decode.hip", "device_common.h", "kernels.h", "shared_gemv.h", "topk.h")
+
+
+def decode_sources_hash():
     import hashlib
+    csrc = os.path.join(ROOT, "mxfp4_routed_expert_router_amd", "csrc")
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel):
+    """HBM bytes (read + written) per launch of the decode kernel `kernel` from
+    the committed rocprofv3 PMC summary (FETCH_SIZE / WRITE_SIZE scaled by a
+    device-copy calibration), or None when the decode kernels' sources differ
+    from the ones the counters were taken with."""
     try:
         line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic_json: "))
     except (OSError, StopIteration):
         return None
     rec = json.loads(line[len("traffic_json: "):])
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mxfp4_routed_expert_router_amd",
-                        "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    if h.hexdigest()[:16] != rec["src_sha256_16"] or kernel not in rec["kernels"]:
+    if decode_sources_hash() != rec.get("decode_sources_sha256_16") or kernel not in rec["kernels"]:
         return None
     k = rec["kernels"][kernel]
     return float(k["read_bytes"] + k["write_bytes"])
@@ -567,12 +575,21 @@ def main():
             for _ in range(2):
                 moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp)
             torch.cuda.synchronize()
-            # the chunk time: plain calls back to back (wall clock over the reps)
-            tp0 = time.perf_counter()
-            for i in range(args.prefill_reps):
-                moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp)
-            torch.cuda.synchronize()
-            p_ms = (time.perf_counter() - tp0) * 1e3 / args.prefill_reps
+
+            def chunk_ms(call):
+                # median over the reps of plain calls back to back, each between
+                # two events on the stream (markers between the calls, not per
+                # dispatch)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.prefill_reps)]
+                for e0, e1 in evs:
+                    e0.record()
+                    call()
+                    e1.record()
+                torch.cuda.synchronize()
+                return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+            p_ms = chunk_ms(lambda: moe.moe_fp4_forward(xp, lp, w, pf.k, y=yp, mode=mode, workspace=wsp))
             # the stage split: the same calls with per-dispatch events, which
             # themselves cost a few percent of the chunk
             evp = [moe.StageEvents() for _ in range(args.prefill_reps)]
@@ -595,12 +612,8 @@ def main():
             sal = torch.zeros(pf.E, dtype=torch.float32, device=dev)
             moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode, workspace=wsp)
             torch.cuda.synchronize()
-            ts0 = time.perf_counter()
-            for i in range(args.prefill_reps):
-                moe.moe_fp4_forward_saliency(xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode,
-                                             workspace=wsp)
-            torch.cuda.synchronize()
-            out["ms_per_chunk_with_saliency"] = (time.perf_counter() - ts0) * 1e3 / args.prefill_reps
+            out["ms_per_chunk_with_saliency"] = chunk_ms(lambda: moe.moe_fp4_forward_saliency(
+                xp, lp, w, pf.k, saliency=sal, y=yp, mode=mode, workspace=wsp))
             log(f"prefill ({label}): {p_ms:.3f} ms/chunk, {out['tflops']:.1f} TFLOP/s, HBM frac "
                 f"{out['hbm_frac']:.2f}, kernels {out['kernel_ms']}; with saliency "
                 f"{out['ms_per_chunk_with_saliency']:.3f} ms")
