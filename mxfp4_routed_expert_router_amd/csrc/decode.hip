@@ -473,7 +473,7 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, Share
   auto issue = [&](int f, Unit& B) {
     const bool is_sh = SH && f < SP && mine_sh;
     const int ru = routed_index(f), j = ru / I, r = ru - j * I;
-    const int e = uniform(tb.de_rank[is_sh ? 0 : j]);
+    const int e = is_sh ? 0 : uniform(tb.de_rank[j]);  // a shared unit reads no routing
     const uint8_t* b1 = a.w1 + (size_t)e * a.stride[0];
     const uint8_t* b3 = a.w3 + (size_t)e * a.stride[2];
     const uint8_t* p1 = a.s1 + (size_t)e * a.stride[1];
