@@ -25,6 +25,11 @@ def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"command failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # the sources build without warnings; the host pass's note that it does not
+    # know the packed-fp32 feature is expected
+    warn = [l for l in r.stderr.splitlines() if "warning" in l and "packed-fp32-ops" not in l]
+    if warn:
+        raise RuntimeError(f"compiler warnings: {' '.join(cmd)}\n" + "\n".join(warn))
     return r
 
 

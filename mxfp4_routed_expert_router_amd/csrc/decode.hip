@@ -1074,14 +1074,12 @@ hipError_t launch_few13(const LayerArgs& a, int nxg, size_t lds, hipStream_t str
 }
 
 hipError_t launch_few(const LayerArgs& a, hipStream_t stream) {
-  const hipEvent_t* ev = a.ev;
   const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
   const size_t lds = few13_lds(a.T, a.H, a.k);
   int cus = 0;
   const hipError_t e13 = lds <= kDecodeLds ? launch_few13<kWaves>(a, nxg, lds, stream, cus)
                                            : launch_few13<2 * kWaves>(a, nxg, lds, stream, cus);
   if (e13 != hipSuccess) return e13;
-  const dim3 blk(kThreads);
   // w2: (row block, token) workgroups; the row-block count a multiple of 8 so
   // that a row block's workgroups share an XCD
   int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, cus));

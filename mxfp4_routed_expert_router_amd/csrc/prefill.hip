@@ -35,7 +35,6 @@ constexpr int kRT2 = 2;                   // 16-row MFMA tiles per wave, w2 pass
 constexpr int kRows13 = 16 * kRT13 * kWaves;  // weight rows per workgroup
 constexpr int kRows2 = 16 * kRT2 * kWaves;
 constexpr int kTok = 64;                  // tokens per pass
-constexpr int kNT = kTok / 16;            // MFMA column tiles per pass
 constexpr int kKB = 128;                  // inputs per K block (4 scale groups)
 constexpr int kXS = kKB + 8;              // LDS row stride in bf16: rows 4 banks apart
 constexpr int kPF13 = 3;                  // K blocks in flight per wave, w1/w3 pass
@@ -339,14 +338,23 @@ hipError_t launch_prefill(const LayerArgs& a, hipStream_t stream) {
   const int t13 = a.E * ((a.I + kRows13 - 1) / kRows13), t2 = a.E * ((a.H + kRows2 - 1) / kRows2);
   const uint8_t* const s13[2] = {a.s1, a.s3};
   const int64_t st13[2] = {a.stride[1], a.stride[3]};
-  if (prefill_lds_takes(a.H, s13, st13, 2))
-    launch_gemm13_lds(a, stream, ev_start(ev, 1), ev_stop(ev, 1));
-  else
+  // (each launcher returns hipGetLastError(), which also clears the error:
+  // its result is the only report of a failed launch)
+  hipError_t e;
+  if (prefill_lds_takes(a.H, s13, st13, 2)) {
+    e = launch_gemm13_lds(a, stream, ev_start(ev, 1), ev_stop(ev, 1));
+  } else {
     launch_k(gemm13_kernel, dim3(xcd_grid(t13)), blk, 0, stream, ev_start(ev, 1), ev_stop(ev, 1), a);
-  if (prefill_lds_takes(a.I, &a.s2, &a.stride[5], 1))
-    launch_gemm2_lds(a, stream, ev_start(ev, 2), ev_stop(ev, 2));
-  else
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  if (prefill_lds_takes(a.I, &a.s2, &a.stride[5], 1)) {
+    e = launch_gemm2_lds(a, stream, ev_start(ev, 2), ev_stop(ev, 2));
+  } else {
     launch_k(gemm2_kernel, dim3(xcd_grid(t2)), blk, 0, stream, ev_start(ev, 2), ev_stop(ev, 2), a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
   return launch_combine(a, stream);
 }
 

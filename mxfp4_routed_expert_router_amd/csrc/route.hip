@@ -92,7 +92,7 @@ __device__ void block_permute(const int32_t* idx, int P, int E, int k, int32_t* 
                               int32_t* dinfo, int32_t* meta, const float* gsrc, float* slot_gate,
                               int32_t* slot_tok, PermSmem<NTH>& sm) {
   constexpr int NW = NTH / kWave, PER = kMaxExperts / NTH;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int tid = threadIdx.x;
   for (int e = tid; e < kMaxExperts; e += NTH) {
     sm.cnt[e] = 0;
 #pragma unroll
