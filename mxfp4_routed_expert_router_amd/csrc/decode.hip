@@ -258,20 +258,23 @@ __global__ void __launch_bounds__(kThreads) gemv2_combine_kernel(LayerArgs a) {
 }
 
 // =========================================================================== one-token path
-// Lane l of a wave owns the 32-input groups g = l + 64 i (i < NXG) of the rows
-// it reads.  In the w1/w3 kernel the token's activations sit in LDS (read per
-// unit, 16 bytes per group and dword; in registers they would cost 48 VGPRs
-// and the kernel measured 0.7 us slower at H = 5120); in the w2 kernel each
-// lane keeps its 32 h values in registers.  The weights are the only HBM
+// In the one-token w1/w3 kernel half a wave reads a row (half-lane j the
+// 32-input groups j + 32 i); in the few-token one lane l owns the groups
+// l + 64 i (i < NXG) of the rows it reads.  In both the token's activations
+// sit in LDS (read per unit, 16 bytes per group and dword; in registers they
+// would cost 48 VGPRs and the kernel measured 0.7 us slower at H = 5120); in
+// the w2 kernel each lane keeps its 32 h values in registers.  The weights are the only HBM
 // stream, and the inner loop is the FP4 decode (v_cvt_scalef32_pk_bf16_fp4)
 // and the dot products (v_dot2c_f32_bf16, bf16 products exact in fp32).
 
-constexpr int kOneMaxXG = 4;      // x groups per lane: H <= 64 * 32 * 4
+constexpr int kOneMaxXG = 4;      // x groups per lane: H <= 64 * 32 * 4 (w1/w3 slots <= 8)
 constexpr int kOneMaxPL = 2;      // (slot, group) pairs per lane in the w2 kernel
 constexpr int kOneRowsMax = 64;   // w2 rows per workgroup
 constexpr int kOneDP = 4;         // w2 rows in flight per wave (measured best of 2..12)
 
 int one_xg(int H) { return (H / 32 + kWave - 1) / kWave; }
+// 16-byte slots a lane takes of one w1 row and one w3 row together
+int one_ns(int H) { return (2 * (H / 32) + kWave - 1) / kWave; }
 int one_pl(int I, int k) {
   const int pw = (k * (I / 32) + kWaves - 1) / kWaves;
   return (pw + kWave - 1) / kWave;
@@ -364,21 +367,27 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 // G and U for every (chosen expert, row) unit.  The grid is persistent (what
 // is resident at once); wave w of the grid takes units w, w + W, w + 2W, ...
 // and keeps the next unit's loads in flight while it computes the current one.
-// A unit is one row of w1 and the same row of w3: NXG load instructions each
-// (lane l reads the 16-byte chunk of group l + 64 i), plus the scale bytes.
+// A unit is one row of w1 and the same row of w3, read as NS = H / 1024 slots
+// (rounded up) of 16-byte loads: slot i of lane l reads group l + 64 i of the
+// 2 H / 32 groups of the two rows (w1's first, then w3's), so at H = 5120 the
+// middle slot holds the end of the w1 row in lanes 0-31 and the start of the
+// w3 row in lanes 32-63, and no lane loads a duplicate.  Each slot brings its
+// group's scale byte; lanes past the last group re-read it and take the zero
+// group of x.  Lane l's sum over its w1 groups is G's part, over its w3
+// groups U's.
 //
-// SH: the shared expert's w1/w3 rows too (sh: M = 2, T = 1).  They need no
-// routing, so they take the first two ring slots of waves 0 .. N_s - 1: the
+// SH: the shared expert's w1/w3 rows too (sh: M = 2, T = 1, K = H).  They need
+// no routing, so they take the first two ring slots of waves 0 .. N_s - 1: the
 // first slot's loads go out at entry, while wave 0 ranks, and fill the time in
-// which routed rows cannot be addressed yet.  A shared row is two units of
-// the same shape as a routed one: part p holds, for each matrix, the 16-byte
-// chunks l + 64 (NXG p + i) of FP8 codes (lane l, i < NXG) and their scale
-// bytes.  The routed units take the remaining slots in order.  Both kinds
-// issue the same load instructions (only the bases and offsets differ), so the
-// waits of the ring stay exact.  The row's two sums run through its chunks in
-// the order shared_gemv_row takes them (fp8_chunk_dot each, x from LDS), then
-// the wave sums and swiglu_bf16: the shared expert's own bits.
-template <int NXG, bool SH>
+// which routed rows cannot be addressed yet.  A shared row is two units of the
+// same shape: part 0 the w1 row, part 1 the w3 row, slot i of lane l the
+// 16-byte chunk l + 64 i of FP8 codes (K / 16 = NS 64 chunks at most) and its
+// scale byte.  The routed units take the remaining slots in order.  All loads
+// are global loads with per-lane addresses, the same instructions for both
+// kinds, so the waits of the ring stay exact.  A part's sum runs through its
+// chunks in the order shared_gemv_row takes them (fp8_chunk_dot each, x from
+// LDS); then the wave sums and swiglu_bf16: the shared expert's own bits.
+template <int NS, bool SH>
 __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, SharedArgs sh) {
   __shared__ OneTables tb;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -446,96 +455,84 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, Share
     }
   }
 
-  int gc[NXG], xo[NXG];
-#pragma unroll
-  for (int i = 0; i < NXG; ++i) {
-    const int g = lane + kWave * i;
-    gc[i] = g < CPR ? g : CPR - 1;
-    xo[i] = g < CPR ? 4 * g : 4 * CPR;
-  }
-  const int wbytes = I * (H / 2), sbytes = I * CPR;
-  // shared rows: chunk of part p, slot i at lane + 64 (NXG p + i), clamped
-  const int snc = SH ? sh.K / 16 : 1;
-  int shc[SP > 0 ? SP : 1][NXG];
-#pragma unroll
-  for (int p = 0; p < (SP > 0 ? SP : 1); ++p)
-#pragma unroll
-    for (int i = 0; i < NXG; ++i) {
-      const int c = lane + kWave * (NXG * p + i);
-      shc[p][i] = c < snc ? c : snc - 1;
-    }
-  float shG = 0.f, shU = 0.f;  // the shared row's sums, carried from part 0 to part 1
+  const int snc = SH ? sh.K / 16 : 1;  // a shared row's 16-byte chunks
+  float shG = 0.f;  // a shared row's G part, carried from part 0 to part 1
 
   struct Unit {
-    u32x4 q1[NXG], q3[NXG];
-    uint32_t s1[NXG], s3[NXG];
+    u32x4 q[NS];
+    uint32_t s[NS];
   };
+  // a routed unit: lanes 0-31 read the w1 row, lanes 32-63 the w3 row; slot i
+  // of half-lane hl is group hl + 32 i.  Only the last slot can pass the row's
+  // end (32 (NS - 1) < CPR): it alone is clamped, the others are a fixed step
+  // from the lane's first chunk.  A shared part's lane l reads chunks l + 64 i,
+  // likewise clamped in the last slot only (64 (NS - 1) < 2 CPR).
+  const bool hi = lane >= kWave / 2;
+  const int hl = lane & (kWave / 2 - 1);
+  const int g_last = hl + kWave / 2 * (NS - 1);
+  const int gc_last = g_last < CPR ? g_last : CPR - 1;
+  const int c_last = lane + kWave * (NS - 1);
+  const int cc_last = c_last < snc ? c_last : snc - 1;
   auto issue = [&](int f, Unit& B) {
     const bool is_sh = SH && f < SP && mine_sh;
     const int ru = routed_index(f), j = ru / I, r = ru - j * I;
     const int e = is_sh ? 0 : uniform(tb.de_rank[j]);  // a shared unit reads no routing
-    const uint8_t* b1 = a.w1 + (size_t)e * a.stride[0];
-    const uint8_t* b3 = a.w3 + (size_t)e * a.stride[2];
-    const uint8_t* p1 = a.s1 + (size_t)e * a.stride[1];
-    const uint8_t* p3 = a.s3 + (size_t)e * a.stride[3];
-    int ow = r * (H / 2), os = r * CPR, nb = wbytes, ns = sbytes;
-    if (SH && is_sh) {
-      b1 = sh.w[0];
-      b3 = sh.w[1];
-      p1 = sh.s[0];
-      p3 = sh.s[1];
-      ow = wid * sh.K;
-      os = (wid / 32) * (sh.K / 32);
-      nb = sh.N * sh.K;
-      ns = (sh.N / 32) * (sh.K / 32);
+    const uint8_t* wrow = (hi ? a.w3 + (size_t)e * a.stride[2] : a.w1 + (size_t)e * a.stride[0]) +
+                          (size_t)r * (H / 2);
+    const uint8_t* srow = (hi ? a.s3 + (size_t)e * a.stride[3] : a.s1 + (size_t)e * a.stride[1]) +
+                          (size_t)r * CPR;
+    int w0 = hl * 16, s0 = hl, wstep = kWave / 2 * 16, wl = gc_last * 16, sl = gc_last;
+    if (SH && is_sh) {  // one row of a shared part
+      wrow = sh.w[f] + (size_t)wid * sh.K;
+      srow = sh.s[f] + (size_t)(wid / 32) * (sh.K / 32);
+      w0 = lane * 16;
+      s0 = lane / 2;
+      wstep = kWave * 16;
+      wl = cc_last * 16;
+      sl = cc_last / 2;
     }
-    const __amdgpu_buffer_rsrc_t r1 = rsrc(b1, nb), r3 = rsrc(b3, nb);
-    const __amdgpu_buffer_rsrc_t q1 = rsrc(p1, ns), q3 = rsrc(p3, ns);
+    const uint8_t* wp = wrow + w0;
+    const uint8_t* sp = srow + s0;
 #pragma unroll
-    for (int i = 0; i < NXG; ++i) {
-      int vo = gc[i] * 16, vs = gc[i];
-      if (SH && is_sh) {
-        const int c = f == 0 ? shc[0][i] : shc[SP > 1 ? 1 : 0][i];
-        vo = c * 16;
-        vs = c / 2;
-      }
-      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, vo, ow, 0));
-      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, vo, ow, 0));
-      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, vs, os, 0);
-      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, vs, os, 0);
+    for (int i = 0; i < NS - 1; ++i) {
+      B.q[i] = ld16(wp + wstep * i);
+      B.s[i] = sp[kWave / 2 * i];  // 32 groups (routed) or 64 chunks (shared) on
     }
+    B.q[NS - 1] = ld16(wrow + wl);
+    B.s[NS - 1] = srow[sl];
   };
   auto compute = [&](int f, const Unit& B) {
     if (SH && f < SP && mine_sh) {
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < NXG; ++i) {
-        const int c = lane + kWave * (NXG * f + i);
+      for (int i = 0; i < NS; ++i) {
+        const int c = lane + kWave * i;
         if (c < snc) {
           const u32x4 xc[2] = {xl[2 * c], xl[2 * c + 1]};
-          shG = fp8_chunk_dot(B.q1[i], B.s1[i], xc, shG);
-          shU = fp8_chunk_dot(B.q3[i], B.s3[i], xc, shU);
+          acc = fp8_chunk_dot(B.q[i], B.s[i], xc, acc);
         }
       }
-      if (f == SP - 1) {
-        const float r0 = wave_sum_f32(shG), r1 = wave_sum_f32(shU);
+      if (f == 0) {
+        shG = acc;
+      } else {
+        const float r0 = wave_sum_f32(shG), r1 = wave_sum_f32(acc);
         if (lane == 0) sh.h[wid] = swiglu_bf16(r0, r1);
       }
       return;
     }
     const int ru = routed_index(f), j = ru / I, r = ru - j * I;
-    float G = 0.f, U = 0.f;
+    float acc = 0.f;  // G's part in lanes 0-31, U's in lanes 32-63
 #pragma unroll
-    for (int i = 0; i < NXG; ++i) {
-      const float c1 = ue8m0_to_f32(B.s1[i]), c3 = ue8m0_to_f32(B.s3[i]);
+    for (int i = 0; i < NS; ++i) {
+      const int g = hl + kWave / 2 * i;
+      const int xg = i < NS - 1 || g < CPR ? g : CPR;  // past the row: zero group
+      const float c = ue8m0_to_f32(B.s[i]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x8 xq = as_bf16x8(xl[xo[i] + q]);
-        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), xq, G);
-        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), xq, U);
-      }
+      for (int q = 0; q < 4; ++q)
+        acc = dot8_bf16(fp4x8_to_bf16x8(B.q[i][q], c), as_bf16x8(xl[4 * xg + q]), acc);
     }
-    G = wave_sum_f32(G);
-    U = wave_sum_f32(U);
+    float G, U;
+    wave_half_sums_f32(acc, G, U);
     if (lane == 0) a.h[(size_t)uniform(tb.slot_of[j]) * I + r] = swiglu_bf16(G, U);
   };
 
@@ -937,24 +934,37 @@ Residency residency(const void* kernel, size_t lds, int threads = kThreads) {
   return r;
 }
 
-template <int NXG, bool SH>
-const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NXG, SH>); }
+// The one-token w1/w3 kernel for NS = H / 1024 (rounded up) slots and SH: its
+// address, or its launch.
+template <int NS, bool SH>
+const void* k13_one() { return reinterpret_cast<const void*>(gemv13_one_kernel<NS, SH>); }
 
-// The one-token w1/w3 kernel for (NXG, SH): its address, or its launch.
 template <bool SH>
-const void* k13_one_sh(int nxg) {
-  return nxg == 1 ? k13_one<1, SH>() : nxg == 2 ? k13_one<2, SH>() : nxg == 3 ? k13_one<3, SH>()
-                                                                              : k13_one<4, SH>();
+const void* k13_one_sh(int ns) {
+  switch (ns) {
+    case 1: return k13_one<1, SH>();
+    case 2: return k13_one<2, SH>();
+    case 3: return k13_one<3, SH>();
+    case 4: return k13_one<4, SH>();
+    case 5: return k13_one<5, SH>();
+    case 6: return k13_one<6, SH>();
+    case 7: return k13_one<7, SH>();
+    default: return k13_one<8, SH>();
+  }
 }
 template <bool SH>
-void launch13_one(int nxg, dim3 g, const LayerArgs& a, const SharedArgs& sh, hipStream_t stream) {
+void launch13_one(int ns, dim3 g, const LayerArgs& a, const SharedArgs& sh, hipStream_t stream) {
   const dim3 blk(kThreads);
   const hipEvent_t e0 = ev_start(a.ev, 1), e1 = ev_stop(a.ev, 1);
-  switch (nxg) {
+  switch (ns) {
     case 1: launch_k(gemv13_one_kernel<1, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
     case 2: launch_k(gemv13_one_kernel<2, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
     case 3: launch_k(gemv13_one_kernel<3, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
-    default: launch_k(gemv13_one_kernel<4, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 4: launch_k(gemv13_one_kernel<4, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 5: launch_k(gemv13_one_kernel<5, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 6: launch_k(gemv13_one_kernel<6, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    case 7: launch_k(gemv13_one_kernel<7, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
+    default: launch_k(gemv13_one_kernel<8, SH>, g, blk, 0, stream, e0, e1, a, sh); break;
   }
 }
 template <int NPL, bool FEW, int SC>
@@ -970,11 +980,12 @@ int shared_one_chunks(int K, int maxc) {
   const int ncl = (K / 16 + kWave - 1) / kWave;
   return ncl <= maxc ? ncl : 0;
 }
-// A shared w1/w3 row of K = H inputs fits two units of the w1/w3 kernel.
-bool shared13_fits(int H) { return shared_one_chunks(H, 2 * one_xg(H)) > 0; }
+// A shared w1/w3 row of K = H inputs fits two units of the w1/w3 kernel (one
+// a matrix, a chunk a slot).
+bool shared13_fits(int K, int H) { return K == H && shared_one_chunks(K, one_ns(H)) > 0; }
 
 hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
-  const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
+  const int ns = one_ns(a.H), npl = one_pl(a.I, a.k);
   const SharedArgs none{};
   // With a shared expert (a.shared13, a.shared2) its rows ride in the two
   // launches when they fit: a w1/w3 row in two units, a w2 row in one round
@@ -984,11 +995,11 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
   bool shared = a.shared13 != nullptr;
   const int routed = a.k * a.I, S = shared ? a.shared13->N : 0;
   int sc2 = shared ? shared_one_chunks(a.shared2->K, kShMaxChunks) : 0;
-  bool carry = shared && shared13_fits(a.shared13->K) && sc2 > 0;
+  bool carry = shared && shared13_fits(a.shared13->K, a.H) && sc2 > 0;
   Residency res{};
   int want = 0;
   if (carry) {
-    res = residency(k13_one_sh<true>(nxg), 0);
+    res = residency(k13_one_sh<true>(ns), 0);
     want = std::min(res.wgs, (S + routed) / kWaves);
     carry = res.wgs > 0 && want * kWaves >= S;
   }
@@ -1003,15 +1014,15 @@ hipError_t launch_one(const LayerArgs& a, hipStream_t stream) {
   }
   // w1/w3: as many workgroups as are resident
   if (!carry) {
-    res = residency(k13_one_sh<false>(nxg), 0);
+    res = residency(k13_one_sh<false>(ns), 0);
     want = std::min(res.wgs, (routed + kWaves - 1) / kWaves);
   }
   if (res.wgs <= 0) return hipErrorInvalidValue;
   const dim3 g13(std::max(1, want));
   if (shared)
-    launch13_one<true>(nxg, g13, a, *a.shared13, stream);
+    launch13_one<true>(ns, g13, a, *a.shared13, stream);
   else
-    launch13_one<false>(nxg, g13, a, none, stream);
+    launch13_one<false>(ns, g13, a, none, stream);
   // w2: one workgroup per compute unit, at most kOneRowsMax rows each
   const int n2 = std::max((a.H + kOneRowsMax - 1) / kOneRowsMax, std::min(a.H, res.cus));
   const dim3 g2(n2);

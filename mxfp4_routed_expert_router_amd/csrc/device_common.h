@@ -125,6 +125,21 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// The sums over lanes 0-31 (lo) and 32-63 (hi) of a wave, with the same DPP
+// steps as wave_sum_f32: lo = row 0 + row 1, hi = row 2 + row 3.  Uniform.
+__device__ __forceinline__ void wave_half_sums_f32(float v, float& lo, float& hi) {
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  lo = r0 + r1;
+  hi = r2 + r3;
+}
+
 // sum_{i<8} a[i] * b[i] + c with bf16 products exact in fp32 (v_dot2c_f32_bf16).
 __device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b, float c) {
   c = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[0], a[1]}, bf16x2{b[0], b[1]}, c, false);
