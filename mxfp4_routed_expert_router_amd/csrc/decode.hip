@@ -368,13 +368,12 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 // is resident at once); wave w of the grid takes units w, w + W, w + 2W, ...
 // and keeps the next unit's loads in flight while it computes the current one.
 // A unit is one row of w1 and the same row of w3, read as NS = H / 1024 slots
-// (rounded up) of 16-byte loads: slot i of lane l reads group l + 64 i of the
-// 2 H / 32 groups of the two rows (w1's first, then w3's), so at H = 5120 the
-// middle slot holds the end of the w1 row in lanes 0-31 and the start of the
-// w3 row in lanes 32-63, and no lane loads a duplicate.  Each slot brings its
-// group's scale byte; lanes past the last group re-read it and take the zero
-// group of x.  Lane l's sum over its w1 groups is G's part, over its w3
-// groups U's.
+// (rounded up) of 16-byte loads: lanes 0-31 read the w1 row and lanes 32-63
+// the w3 row, slot i of half-lane j the 32-input group j + 32 i, so a load
+// covers 512 contiguous bytes of each row and at H = 5120 no lane idles.  Each
+// slot brings its group's scale byte; in the last slot, lanes past the row's
+// end re-read its last group and take the zero group of x.  A lane's sum is
+// G's part (lanes 0-31) or U's (lanes 32-63).
 //
 // SH: the shared expert's w1/w3 rows too (sh: M = 2, T = 1, K = H).  They need
 // no routing, so they take the first two ring slots of waves 0 .. N_s - 1: the
