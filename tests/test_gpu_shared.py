@@ -122,11 +122,12 @@ def test_forward_shared_one_token_accumulate(moe, orc):
     check_y(ya, ref, "forward_shared T=1 accumulate")
 
 
-@pytest.mark.parametrize("H", [1024, 2048, 3072, 4096, 5120])
+@pytest.mark.parametrize("H", [1024, 1568, 2048, 3072, 4096, 5120, 8192])
 def test_forward_shared_one_token_row_parts(moe, orc, H):
-    """One token: a shared w1/w3 row is carried as two units of the routed
-    w1/w3 kernel (its 16-byte chunks split 1+0, 1+1, 2+1, 2+2 and 3+2 per lane
-    over these H).  Bit for bit the separate calls, and the oracle's sum."""
+    """One token: a shared expert's w1 row and w3 row are carried as two units
+    of the routed w1/w3 kernel, each 1 to 8 16-byte chunks a lane over these H
+    (at H = 1568 the second chunk of a lane covers only 34 of 64 lanes).  Bit
+    for bit the separate calls, and the oracle's sum."""
     import torch
     T, I, E, k = 1, 256, 8, 2
     say(f"forward_shared T=1 H={H}")

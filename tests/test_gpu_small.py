@@ -175,6 +175,9 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (1, 352, 96, 7, 3),       # one token, ragged groups
     (1, 256, 2080, 10, 5),    # one token, 65 groups per w2 row
     (1, 256, 1024, 16, 16),   # one token, k = 16: k * I / 32 at the one-token path's limit
+    (1, 1568, 96, 7, 3),      # one token, two slots a lane, the second one ragged (49 groups a row)
+    (1, 3104, 160, 9, 4),     # one token, four slots, one group in the last
+    (1, 8192, 128, 8, 4),     # one token, eight slots a lane (H = 8192)
     (100, 64, 32, 1024, 16),  # E = 1024, k = 16: the largest router tables, 1600 pairs
     (2, 8192, 256, 8, 4),     # few-token GEMV path, 4 groups a lane (H = 8192)
     (6, 1024, 2304, 12, 8),   # few-token path at T = 6, two (pair, group)s a lane in w2
