@@ -758,7 +758,8 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
   const uint8_t* sp[NPL];
   float gt[NPL];
   bf16x8 Hv[NPL][4];
-  {
+  const bool routed = NP > 0;  // none: the shared expert's rows alone
+  if (routed) {
     int ev[NPL], sl[NPL], gg[NPL];
     u32x4 hr[NPL][4];
 #pragma unroll
@@ -837,6 +838,7 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
     }
   };
   // loads complete in issue order: issue the ring in the order it is consumed
+  if (routed) {
 #pragma unroll
   for (int b = 0; b < kOneDP; ++b) {
     load(b, m0 + b);
@@ -862,6 +864,7 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  }
   if constexpr (SC > 0) {
     // the shared rows of this wave, kShRows at a time (one batch at the real
     // shape: 20 rows a workgroup)
@@ -883,12 +886,19 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
   }
   lds_barrier();
   if (tid < m1 - m0) {
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) s += part[q][tid];
     float* yp = a.y + (size_t)tok * H + m0 + tid;
-    float v = a.accumulate ? *yp + s : s;
-    if constexpr (SC > 0) v = v + shr[tid];
+    float v;
+    if (routed) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) s += part[q][tid];
+      v = a.accumulate ? *yp + s : s;
+      if constexpr (SC > 0) v = v + shr[tid];
+    } else if constexpr (SC > 0) {
+      v = a.accumulate ? *yp + shr[tid] : shr[tid];  // the shared expert's own y
+    } else {
+      v = a.accumulate ? *yp : 0.f;
+    }
     *yp = v;
   }
 }
@@ -1123,6 +1133,44 @@ int decode_family(int T, int H, int I, int k) {
 
 bool decode_fuses_route(int T, int H, int I, int E, int k) {
   return T == 1 && one_token_fits(H, I, k) && E <= kFusedVPL * kWave;
+}
+
+hipError_t launch_shared_one(const uint16_t* x, const uint8_t* const w[6], int H, int I, float* y,
+                             int accumulate, uint16_t* h, hipStream_t stream, bool& done) {
+  done = false;
+  // the one-token kernels with no routed expert: a wave for every shared
+  // w1/w3 row (two units: the w1 row, then the w3 row), the w2 rows in one
+  // round of at most kShMaxChunks chunks a lane
+  if (!one_token_fits(H, 32, 1) || !shared13_fits(H, H)) return hipSuccess;
+  const int sc2 = shared_one_chunks(I, kShMaxChunks);
+  if (sc2 == 0) return hipSuccess;
+  const int ns = one_ns(H);
+  const Residency res = residency(k13_one_sh<true>(ns), 0);
+  if (res.wgs <= 0 || I % kWaves != 0 || I / kWaves > res.wgs) return hipSuccess;
+  LayerArgs a{};
+  a.H = H;
+  a.I = 32;  // no routed unit reads it
+  a.k = 0;
+  a.E = 1;
+  a.x = x;
+  a.y = y;
+  a.accumulate = accumulate;
+  SharedArgs s13{};
+  s13.act = x;
+  s13.w[0] = w[0]; s13.s[0] = w[1]; s13.w[1] = w[2]; s13.s[1] = w[3];
+  s13.N = I; s13.K = H; s13.T = 1; s13.h = h;
+  SharedArgs s2{};
+  s2.act = h;
+  s2.w[0] = w[4]; s2.s[0] = w[5];
+  s2.N = H; s2.K = I; s2.T = 1; s2.y = y; s2.accumulate = accumulate;
+  launch13_one<true>(ns, dim3(I / kWaves), a, s13, stream);
+  const dim3 g2(std::max((H + kOneRowsMax - 1) / kOneRowsMax, std::min(H, res.cus)));
+  if (sc2 <= 3)
+    launch2_one<1, false, 3>(g2, a, s2, stream);
+  else
+    launch2_one<1, false, kShMaxChunks>(g2, a, s2, stream);
+  done = true;
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const LayerArgs& a, hipStream_t stream) {

@@ -136,6 +136,10 @@ hipError_t launch_shared_w2(const uint16_t* h, const uint8_t* w2, const uint8_t*
                             int I, float* y, int accumulate, hipStream_t stream);
 hipError_t launch_shared(const uint16_t* x, const uint8_t* const w[6], int T, int H, int I,
                          float* y, int accumulate, uint16_t* h, hipStream_t stream);
+// One token through the one-token decode kernels with no routed expert (sets
+// done; leaves it false, launching nothing, where the shapes do not fit them).
+hipError_t launch_shared_one(const uint16_t* x, const uint8_t* const w[6], int H, int I, float* y,
+                             int accumulate, uint16_t* h, hipStream_t stream, bool& done);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, float* logits, int T, int H,
                                 int E, hipStream_t stream);
 hipError_t launch_prenorm(const float* x, uint16_t* u, int T, int H, float eps, hipStream_t stream);

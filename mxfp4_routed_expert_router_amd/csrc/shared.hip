@@ -170,6 +170,11 @@ void launch_one_gemm(const SharedArgs& s, hipStream_t stream) {
 
 hipError_t launch_shared(const uint16_t* x, const uint8_t* const w[6], int T, int H, int I,
                          float* y, int accumulate, uint16_t* h, hipStream_t stream) {
+  if (T == 1) {
+    bool done = false;
+    const hipError_t e = launch_shared_one(x, w, H, I, y, accumulate, h, stream, done);
+    if (done || e != hipSuccess) return e;
+  }
   SharedArgs s13{};
   s13.act = x;
   s13.w[0] = w[0]; s13.s[0] = w[1]; s13.w[1] = w[2]; s13.s[1] = w[3];
