@@ -145,17 +145,28 @@ def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, g
         j = i % n_gen
         moe.moe_fp4_shared_expert(x_d[j:j + 1], sw_d, y=y_s, h=h_s)
 
+    def step_router_shared(i):  # the whole decode step: router, routed layer, shared expert
+        j = i % n_gen
+        moe.moe_fp4_router_logits(x_d[j:j + 1], wr_d, out=lg_out)
+        moe.moe_fp4_forward_shared(x_d[j:j + 1], lg_out, w, sw_d, wl.k, y=y_d[j:j + 1],
+                                   workspace=ws)
+
     us_shared = graph_us(step_shared)
     us_shared_only = graph_us(step_shared_only)
+    us_router_shared = graph_us(step_router_shared)
     shared_bytes = sum(a.nbytes for a in sw_np.values()) + wl.H * 2 + wl.H * 4
     shared = {"us_per_token": us_shared, "shared_expert_us": us_shared_only,
+              "us_per_token_with_router": us_router_shared,
               "shared_bytes": shared_bytes,
               "shared_GBps": shared_bytes / (us_shared_only * 1e-6) / 1e9,
               "note": "routed layer + shared expert (FP8 E4M3, 32x32 UE8M0 block scales, "
                       "I = 2304; 35.4 MB); graph replay; shared_expert_us: the shared expert "
-                      "alone (two kernels), one call per step in a graph"}
+                      "alone (two kernels), one call per step in a graph; "
+                      "us_per_token_with_router: router logits, then the routed layer with "
+                      "the shared expert (four kernels a step)"}
     log(f"decode with the shared expert: {us_shared:.2f} us/token; shared expert alone "
-        f"{us_shared_only:.2f} us ({shared['shared_GBps']:.0f} GB/s)")
+        f"{us_shared_only:.2f} us ({shared['shared_GBps']:.0f} GB/s); router + layer + shared "
+        f"expert {us_router_shared:.2f} us/token")
     del sw_d
 
     # ---------------------------------------------------------------- speculative-verify batches
