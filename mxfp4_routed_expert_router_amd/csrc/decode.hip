@@ -432,14 +432,16 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, Share
     return wid + f * nw - (f < SP ? f : SP) * S - (f < SP ? (wid < S ? wid : S) : 0);
   };
 
-  // Wave 0 ranks the logits while the other waves stage x.  The first unit of
-  // every wave needs only the first `early` ranks: wave 0 stores those, the
-  // barrier that publishes x publishes them, every wave issues its first unit,
-  // and wave 0 ranks the rest while those loads are in flight; a second
-  // barrier publishes the remaining ranks and the slots.  (Every wave ranking
-  // for itself kept the SIMDs busy for 3-4 us: 16 waves a CU running the same
+  // Wave 0 ranks the logits while the other waves stage x.  The first units
+  // of this workgroup's waves need only the first `early` ranks (one where
+  // they are all rows of the top expert): wave 0 stores those, the barrier
+  // that publishes x publishes them, every wave issues its first unit, and
+  // wave 0 ranks the rest while those loads are in flight; a second barrier
+  // publishes the remaining ranks and the slots.  (Every wave ranking for
+  // itself kept the SIMDs busy for 3-4 us: 16 waves a CU running the same
   // wave-wide reductions.)
-  const int first_routed = (nw < V ? nw : V) - 1 - S;  // largest routed index in slot 0
+  const int wg_last = min((int)(blockIdx.x + 1) * kWaves, nw < V ? nw : V) - 1;
+  const int first_routed = wg_last - S;  // largest routed index in this workgroup's slot 0
   const int early = first_routed >= 0 ? first_routed / I + 1 : 0;
   OneRanking rank;
   if (w == 0) {

@@ -31,8 +31,12 @@ def _dev_shared(moe, sw):
                                         for n, a in sw.items()})
 
 
-SHARED_CASES = [  # (T, H, I): T <= 4 one wave per row, T > 4 MFMA tiles
+SHARED_CASES = [  # (T, H, I): T = 1 on the one-token decode kernels where they fit,
+    # T <= 4 one wave per row, T > 4 MFMA tiles
     (1, 256, 128),
+    (1, 5120, 2304),     # one token at the real shape
+    (1, 256, 4128),      # one token, a w2 row of 258 chunks: the one-wave-per-row kernels
+    (1, 8224, 64),       # one token, H past the one-token kernels: the one-wave-per-row kernels
     (3, 224, 96),        # 7 and 3 chunks of 32 columns: ragged lanes
     (4, 5120, 2304),     # the real shape
     (5, 256, 128),
