@@ -23,6 +23,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void lds_load16(uint32_t lds_base, const void* g) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
+// The same with the non-temporal hint, for data read once (weights): the L2
+// keeps it at low priority, so reused activation rows stay resident.
+__device__ __forceinline__ void lds_load16_nt(uint32_t lds_base, const void* g) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
 __device__ __forceinline__ void lds_load4(uint32_t lds_base, const void* g) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }

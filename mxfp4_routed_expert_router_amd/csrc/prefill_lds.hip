@@ -86,7 +86,11 @@ __device__ __forceinline__ void wait_step(int hb, int NHB, int NB, bool xw) {
 }
 
 // Weight block b (256 inputs) of the wave's tiles into stage b % 3, and for b
-// even the scale bytes of blocks b and b + 1 into pair slot (b / 2) % 2.
+// even the scale bytes of blocks b and b + 1 into pair slot (b / 2) % 2.  The
+// weight halves carry the non-temporal hint: each is read once a pass, and
+// the L2 then keeps the gathered activation rows that every row tile of the
+// expert reads again (w1/w3 reads 5.50 -> 5.07 GB, 1.375 -> 1.368 ms; the
+// same hint made the MXFP8 kernels 3% slower, so they go without it).
 // Scale lanes: tile row lane % 16, dword lane / 16 of a block pair's 16 bytes
 // (dwords 2, 3 belong to the odd block; past the last block a lane re-reads
 // the even block's).
@@ -107,8 +111,8 @@ __device__ __forceinline__ void issue_wblock(SmemL<C>& sm, const uint8_t* const 
     for (int rt = 0; rt < kRT; ++rt) {
       uint8_t* const dst = &sm.w[s][w][m * kRT + rt][0];
       const uint8_t* const g = wrow0[m][rt] + (size_t)b * 128;
-      lds_load16(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
-      lds_load16(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
+      lds_load16_nt(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
+      lds_load16_nt(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
       if (even)
         lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
     }
