@@ -377,8 +377,9 @@ __device__ __forceinline__ void publish_counts(const LayerArgs& a, const int (&d
 //
 // SH: the shared expert's w1/w3 rows too (sh: M = 2, T = 1, K = H).  They need
 // no routing, so they take the first two ring slots of waves 0 .. N_s - 1: the
-// first slot's loads go out at entry, while wave 0 ranks, and fill the time in
-// which routed rows cannot be addressed yet.  A shared row is two units of the
+// first slot's loads go out before the first barrier, once the loads of x and
+// the logits issued ahead of them are back, and fill the time in which routed
+// rows cannot be addressed yet.  A shared row is two units of the
 // same shape: part 0 the w1 row, part 1 the w3 row, slot i of lane l the
 // 16-byte chunk l + 64 i of FP8 codes (K / 16 = NS 64 chunks at most) and its
 // scale byte.  The routed units take the remaining slots in order.  All loads
@@ -538,7 +539,8 @@ __global__ void __launch_bounds__(kThreads) gemv13_one_kernel(LayerArgs a, Share
   };
 
   Unit A, B;
-  // a shared row's first part needs neither the ranking nor x: out at once
+  // a shared row's first part needs neither the ranking nor x: out before the
+  // first barrier
   const bool first_now = SH && F > 0 && mine_sh;
   if (first_now) issue(0, A);
   __builtin_amdgcn_sched_barrier(0);
