@@ -258,10 +258,8 @@ __global__ void __launch_bounds__(kThreads) gemv2_combine_kernel(LayerArgs a) {
 }
 
 // =========================================================================== one-token path
-// In the one-token w1/w3 kernel half a wave reads a row (half-lane j the
-// 32-input groups j + 32 i); in the few-token one lane l owns the groups
-// l + 64 i (i < NXG) of the rows it reads.  In both the token's activations
-// sit in LDS (read per unit, 16 bytes per group and dword; in registers they
+// In the w1/w3 kernels half a wave reads a row (half-lane j the 32-input
+// groups j + 32 i).  The token's activations sit in LDS (read per unit, 16 bytes per group and dword; in registers they
 // would cost 48 VGPRs and the kernel measured 0.7 us slower at H = 5120); in
 // the w2 kernel each lane keeps its 32 h values in registers.  The weights are the only HBM
 // stream, and the inner loop is the FP4 decode (v_cvt_scalef32_pk_bf16_fp4)
@@ -283,9 +281,6 @@ bool one_token_fits(int H, int I, int k) {
   return one_xg(H) <= kOneMaxXG && one_pl(I, k) <= kOneMaxPL;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // The one-token w1/w3 kernel's tables, in LDS.  Its units are taken in the
@@ -611,7 +606,7 @@ size_t few13_lds(int T, int H, int k) {
   return (size_t)T * (H / 32 * 4 + 4) * 16 + (size_t)2 * T * k * 4;
 }
 
-template <int NXG, int NW>
+template <int NS, int NW>
 __global__ void __launch_bounds__(NW * kWave) gemv13_few_kernel(LayerArgs a) {
   constexpr int kThreads = NW * kWave, kWaves = NW;
   extern __shared__ __align__(16) uint8_t fsm[];
@@ -650,55 +645,53 @@ __global__ void __launch_bounds__(NW * kWave) gemv13_few_kernel(LayerArgs a) {
   if (tid < 4 * T) xl[(tid >> 2) * RS + CPR * 4 + (tid & 3)] = zero4();
   lds_barrier();
 
-  int gc[NXG], xo[NXG];
-#pragma unroll
-  for (int i = 0; i < NXG; ++i) {
-    const int g = lane + kWave * i;
-    gc[i] = g < CPR ? g : CPR - 1;
-    xo[i] = g < CPR ? 4 * g : 4 * CPR;
-  }
   const int nunits = P * I;
   const int nw = gridDim.x * kWaves, wid = blockIdx.x * kWaves + w;
   const int F = wid < nunits ? (nunits - 1 - wid) / nw + 1 : 0;
   if (F == 0) return;
-  const int wbytes = I * (H / 2), sbytes = I * CPR;
 
+  // the one-token kernel's units: lanes 0-31 the w1 row, lanes 32-63 the w3
+  // row, slot i of half-lane hl group hl + 32 i, only the last slot clamped
   struct Unit {
-    u32x4 q1[NXG], q3[NXG];
-    uint32_t s1[NXG], s3[NXG];
+    u32x4 q[NS];
+    uint32_t s[NS];
   };
+  const bool hi = lane >= kWave / 2;
+  const int hl = lane & (kWave / 2 - 1);
+  const int g_last = hl + kWave / 2 * (NS - 1);
+  const int gc_last = g_last < CPR ? g_last : CPR - 1;
   auto issue = [&](int f, Unit& B) {
     const int u = wid + f * nw, r = u / P, sl = u - r * P;
     const int e = uniform(tab_e[sl]);
-    const __amdgpu_buffer_rsrc_t r1 = rsrc(a.w1 + (size_t)e * a.stride[0], wbytes);
-    const __amdgpu_buffer_rsrc_t r3 = rsrc(a.w3 + (size_t)e * a.stride[2], wbytes);
-    const __amdgpu_buffer_rsrc_t q1 = rsrc(a.s1 + (size_t)e * a.stride[1], sbytes);
-    const __amdgpu_buffer_rsrc_t q3 = rsrc(a.s3 + (size_t)e * a.stride[3], sbytes);
-    const int ow = r * (H / 2), os = r * CPR;
+    const uint8_t* wrow = (hi ? a.w3 + (size_t)e * a.stride[2] : a.w1 + (size_t)e * a.stride[0]) +
+                          (size_t)r * (H / 2);
+    const uint8_t* srow = (hi ? a.s3 + (size_t)e * a.stride[3] : a.s1 + (size_t)e * a.stride[1]) +
+                          (size_t)r * CPR;
+    const uint8_t* wp = wrow + hl * 16;
+    const uint8_t* sp = srow + hl;
 #pragma unroll
-    for (int i = 0; i < NXG; ++i) {
-      B.q1[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, gc[i] * 16, ow, 0));
-      B.q3[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r3, gc[i] * 16, ow, 0));
-      B.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(q1, gc[i], os, 0);
-      B.s3[i] = __builtin_amdgcn_raw_buffer_load_b8(q3, gc[i], os, 0);
+    for (int i = 0; i < NS - 1; ++i) {
+      B.q[i] = ld16(wp + kWave / 2 * 16 * i);
+      B.s[i] = sp[kWave / 2 * i];
     }
+    B.q[NS - 1] = ld16(wrow + gc_last * 16);
+    B.s[NS - 1] = srow[gc_last];
   };
   auto compute = [&](int f, const Unit& B) {
     const int u = wid + f * nw, r = u / P, sl = u - r * P;
     const u32x4* xr = xl + uniform(tab_x[sl]);
-    float G = 0.f, U = 0.f;
+    float acc = 0.f;  // G's part in lanes 0-31, U's in lanes 32-63
 #pragma unroll
-    for (int i = 0; i < NXG; ++i) {
-      const float c1 = ue8m0_to_f32(B.s1[i]), c3 = ue8m0_to_f32(B.s3[i]);
+    for (int i = 0; i < NS; ++i) {
+      const int g = hl + kWave / 2 * i;
+      const int xg = i < NS - 1 || g < CPR ? g : CPR;  // past the row: zero group
+      const float c = ue8m0_to_f32(B.s[i]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x8 xq = as_bf16x8(xr[xo[i] + q]);
-        G = dot8_bf16(fp4x8_to_bf16x8(B.q1[i][q], c1), xq, G);
-        U = dot8_bf16(fp4x8_to_bf16x8(B.q3[i][q], c3), xq, U);
-      }
+      for (int q = 0; q < 4; ++q)
+        acc = dot8_bf16(fp4x8_to_bf16x8(B.q[i][q], c), as_bf16x8(xr[4 * xg + q]), acc);
     }
-    G = wave_sum_f32(G);
-    U = wave_sum_f32(U);
+    float G, U;
+    wave_half_sums_f32(acc, G, U);
     if (lane == 0) a.h[(size_t)sl * I + r] = swiglu_bf16(G, U);
   };
 
@@ -1062,14 +1055,20 @@ bool few_fits(int T, int H, int I, int k) {
   return T >= 2 && T <= kFewMaxT && one_token_fits(H, I, k) && few13_lds(T, H, k) <= kFewLdsBig;
 }
 
-// The few-token w1/w3 kernel for NXG and the workgroup size the LDS allows;
-// the dynamic LDS limit is raised once per (device, kernel).
+// The few-token w1/w3 kernel for NS slots and the workgroup size the LDS
+// allows; the dynamic LDS limit is raised once per (device, kernel).
+template <int NS, int NW>
+const void* k13_few() { return reinterpret_cast<const void*>(gemv13_few_kernel<NS, NW>); }
 template <int NW>
-hipError_t launch_few13(const LayerArgs& a, int nxg, size_t lds, hipStream_t stream, int& cus) {
-  const void* k = nxg == 1   ? reinterpret_cast<const void*>(gemv13_few_kernel<1, NW>)
-                  : nxg == 2 ? reinterpret_cast<const void*>(gemv13_few_kernel<2, NW>)
-                  : nxg == 3 ? reinterpret_cast<const void*>(gemv13_few_kernel<3, NW>)
-                             : reinterpret_cast<const void*>(gemv13_few_kernel<4, NW>);
+hipError_t launch_few13(const LayerArgs& a, int ns, size_t lds, hipStream_t stream, int& cus) {
+  const void* k = ns == 1   ? k13_few<1, NW>()
+                  : ns == 2 ? k13_few<2, NW>()
+                  : ns == 3 ? k13_few<3, NW>()
+                  : ns == 4 ? k13_few<4, NW>()
+                  : ns == 5 ? k13_few<5, NW>()
+                  : ns == 6 ? k13_few<6, NW>()
+                  : ns == 7 ? k13_few<7, NW>()
+                            : k13_few<8, NW>();
   if (lds > kDecodeLds) {
     static std::mutex mu;
     static std::vector<std::pair<int, const void*>> done;
@@ -1088,21 +1087,25 @@ hipError_t launch_few13(const LayerArgs& a, int nxg, size_t lds, hipStream_t str
   const int units = a.T * a.k * a.I;
   const dim3 blk(NW * kWave), g(std::min(res.wgs, (units + NW - 1) / NW));
   const hipEvent_t e0 = ev_start(a.ev, 1), e1 = ev_stop(a.ev, 1);
-  switch (nxg) {
+  switch (ns) {
     case 1: launch_k(gemv13_few_kernel<1, NW>, g, blk, lds, stream, e0, e1, a); break;
     case 2: launch_k(gemv13_few_kernel<2, NW>, g, blk, lds, stream, e0, e1, a); break;
     case 3: launch_k(gemv13_few_kernel<3, NW>, g, blk, lds, stream, e0, e1, a); break;
-    default: launch_k(gemv13_few_kernel<4, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 4: launch_k(gemv13_few_kernel<4, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 5: launch_k(gemv13_few_kernel<5, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 6: launch_k(gemv13_few_kernel<6, NW>, g, blk, lds, stream, e0, e1, a); break;
+    case 7: launch_k(gemv13_few_kernel<7, NW>, g, blk, lds, stream, e0, e1, a); break;
+    default: launch_k(gemv13_few_kernel<8, NW>, g, blk, lds, stream, e0, e1, a); break;
   }
   return hipSuccess;
 }
 
 hipError_t launch_few(const LayerArgs& a, hipStream_t stream) {
-  const int nxg = one_xg(a.H), npl = one_pl(a.I, a.k);
+  const int ns = one_ns(a.H), npl = one_pl(a.I, a.k);
   const size_t lds = few13_lds(a.T, a.H, a.k);
   int cus = 0;
-  const hipError_t e13 = lds <= kDecodeLds ? launch_few13<kWaves>(a, nxg, lds, stream, cus)
-                                           : launch_few13<2 * kWaves>(a, nxg, lds, stream, cus);
+  const hipError_t e13 = lds <= kDecodeLds ? launch_few13<kWaves>(a, ns, lds, stream, cus)
+                                           : launch_few13<2 * kWaves>(a, ns, lds, stream, cus);
   if (e13 != hipSuccess) return e13;
   // w2: (row block, token) workgroups; the row-block count a multiple of 8 so
   // that a row block's workgroups share an XCD
