@@ -71,11 +71,10 @@ struct WaveRanking {
     } else {
       e_win = wave_min_u32(bk == m ? (uint32_t)(lane + kWave * bi) : 0xFFFFFFFFu);
     }
-    if ((int)(e_win & (kWave - 1)) == lane) {
+    // clear the taken key: a select in every lane, no branch
+    const uint32_t kill = (int)(e_win & (kWave - 1)) == lane ? 1u << (e_win >> 6) : 0u;
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if (i == (int)(e_win >> 6)) keys[i] = 0u;
-    }
+    for (int i = 0; i < VPL; ++i) keys[i] = (kill >> i) & 1u ? 0u : keys[i];
     return e_win;
   }
 };
