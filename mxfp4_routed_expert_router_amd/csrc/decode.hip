@@ -3,25 +3,31 @@
 // cost of generating one token as reading every active expert weight once
 // (ai-shiz.ru page, section on per-token arithmetic): this path is bound by HBM.
 //
-// One or two tokens (the row-contiguous kernels):
-//   gemv13_dot  one workgroup per (distinct expert, 16 rows of w1/w3); each of
-//               its 8 waves owns two whole rows, so lane l of load j reads
-//               16-byte chunk 64*j + l of those rows: one contiguous 1 KB per
-//               instruction, the scale bytes contiguous too.  A lane decodes its
-//               chunk (one UE8M0 group, 32 inputs) and takes the dot product with
-//               the matching inputs of x from LDS on the VALU (v_dot2c_f32_bf16,
-//               bf16 products exact in fp32); a row's sum is a fixed-order DPP
-//               reduction, and h = bf16(silu(G) * U).  With one token the kernel
-//               also ranks the logits itself (every workgroup, redundantly) and
-//               one workgroup publishes the routing result, so a decode step is
-//               two launches.
-//   gemv2_dot   one workgroup per 16 rows of w2 covering every distinct expert;
-//               each wave owns two rows and sums gate * (w2 row . h row) over the
-//               experts chunk by chunk, then reduces over the wave: the combine
-//               needs no atomics and y is bitwise reproducible.
-// Three to sixteen tokens (the MFMA kernels): the token rows become the 16
-// columns of a 16x16x32 bf16 MFMA whose other operand is 16 weight rows decoded
-// in registers; waves split the inputs (split-K) and meet in LDS.
+// One token (two launches a step):
+//   gemv13_one_kernel  a persistent grid over the (chosen expert, row) units of
+//                      w1/w3, taken in the ranking's order.  Wave 0 of every
+//                      workgroup ranks the logits itself (the routing needs no
+//                      launch of its own) and workgroup 0 publishes the
+//                      result.  Half a wave reads the w1 row and half the w3
+//                      row of a unit; FP4 is decoded in registers
+//                      (v_cvt_scalef32_pk_bf16_fp4) and dotted with x from LDS
+//                      (v_dot2c_f32_bf16, bf16 products exact in fp32); two
+//                      units are in flight per wave; h = bf16(silu(G) * U).
+//                      Optionally the shared expert's w1/w3 rows and the
+//                      layer's RMS pre-norm ride along.
+//   gemv2_one_kernel   one workgroup per CU over rows of y; every (chosen
+//                      expert, 32-input group) pair of a row belongs to one
+//                      lane, which holds its h values and gate in registers;
+//                      rows stream through a 4-deep ring, the wave reduces
+//                      with DPP and the wave partials are added in a fixed
+//                      order: no atomics, y is bitwise reproducible.
+//                      Optionally the shared expert's w2 rows ride along.
+// Two to fifteen tokens: gemv13_few_kernel (the same units for every
+// (token, expert) pair, the token rows in LDS) and gemv2_one_kernel per token.
+// Other small shapes of up to sixteen tokens (the MFMA kernels gemv13_kernel
+// and gemv2_combine_kernel): the token rows become the 16 columns of a
+// 16x16x32 bf16 MFMA whose other operand is 16 weight rows decoded in
+// registers; waves split the inputs (split-K) and meet in LDS.
 #include <algorithm>
 #include <mutex>
 #include <vector>

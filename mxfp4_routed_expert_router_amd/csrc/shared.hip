@@ -9,6 +9,8 @@
 // decoded to bf16 (v_cvt_scalef32_pk_bf16_fp8) and every product is exact in
 // fp32, as on the routed path.
 //
+// One token, where the shapes fit, runs on the one-token decode kernels with no
+// routed expert (launch_shared_one, decode.hip).  Otherwise:
 //   shared_gemv_kernel<M, C>  T <= 4: one wave per output row; lane l takes the
 //                          16-byte chunks l + 64 j of the row (16 codes each,
 //                          whole lines per load), the wave reduces with DPP.
