@@ -168,9 +168,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm13_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  const int ne = a.counts[e];
-  if (ne == 0) return;
-  const int off = a.offsets[e];
+  // both loads in flight at once: the test reads both (off is never negative),
+  // so the compiler cannot sink the second below it
+  const int ne = a.counts[e], off = a.offsets[e];
+  if (ne == 0 || off < 0) return;
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int c16 = lane & 15, kb = lane >> 4;
@@ -226,9 +227,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm2_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  const int ne = a.counts[e];
-  if (ne == 0) return;
-  const int off = a.offsets[e];
+  // both loads in flight at once: the test reads both (off is never negative),
+  // so the compiler cannot sink the second below it
+  const int ne = a.counts[e], off = a.offsets[e];
+  if (ne == 0 || off < 0) return;
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int c16 = lane & 15, kb = lane >> 4;

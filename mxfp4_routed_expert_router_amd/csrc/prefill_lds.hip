@@ -237,9 +237,10 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  const int ne = a.counts[e];
-  if (ne == 0) return;
-  const int off = a.offsets[e];
+  // both loads in flight at once: the test reads both (off is never negative),
+  // so the compiler cannot sink the second below it
+  const int ne = a.counts[e], off = a.offsets[e];
+  if (ne == 0 || off < 0) return;
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -303,9 +304,10 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  const int ne = a.counts[e];
-  if (ne == 0) return;
-  const int off = a.offsets[e];
+  // both loads in flight at once: the test reads both (off is never negative),
+  // so the compiler cannot sink the second below it
+  const int ne = a.counts[e], off = a.offsets[e];
+  if (ne == 0 || off < 0) return;
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
