@@ -133,14 +133,15 @@ __device__ __forceinline__ void issue_first_wblocks(SmemL<C>& sm, const uint8_t*
 // src (row length ld = K): acc[m][rt][nt] = W_m[rows of tile rt] . X^T[tokens of nt].
 // wrow0[m][rt] points at row 0 of the wave's 16-row tile (inside the weights
 // even for a tile past the end, whose results are not stored), srow0 at that
-// row's scales.  Tokens past nc read token 0's row.  The caller has issued
-// weight blocks 0 and 1 (issue_first_wblocks) before the pass's token rows
-// were staged.
+// row's scales.  trow[i]: the source row of the wave's staged token 8 w + i
+// (any valid row past the pass's tokens: their results are not stored).  The
+// caller has issued weight blocks 0 and 1 (issue_first_wblocks).
 template <class C, int M, int kRT, int NT>
 __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
                                               const uint8_t* const (&srow0)[M][kRT], size_t wrow,
-                                              size_t srow, const uint16_t* __restrict__ src, int nc,
-                                              int K, f32x4 (&acc)[M][kRT][NT]) {
+                                              size_t srow, const uint16_t* __restrict__ src,
+                                              const int (&trow)[8], int K,
+                                              f32x4 (&acc)[M][kRT][NT]) {
   static_assert(M * kRT == kTiles, "tile count");
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -158,9 +159,11 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
   const uint8_t* xsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int t = 8 * w + 4 * q + (lane >> 4);
-    xsrc[q] = reinterpret_cast<const uint8_t*>(src + (size_t)sm.row[t < nc ? t : 0] * K) +
-              ((c16 ^ xsw(t)) << 4);
+    const int t = 8 * w + 4 * q + (lane >> 4), li = 4 * q + (lane >> 4);
+    int row = trow[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) row = li == i ? trow[i] : row;  // a select: trow stays uniform
+    xsrc[q] = reinterpret_cast<const uint8_t*>(src + (size_t)row * K) + ((c16 ^ xsw(t)) << 4);
   }
 
   auto issue_w = [&](int b) { issue_wblock<C, M, kRT>(sm, wrow0, srow0, wrow, srow, b, NB); };
@@ -230,6 +233,45 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
   __syncthreads();  // the LDS is free for the caller (and its row table may change)
 }
 
+// An expert's token count and offset by scalar loads issued and waited for in
+// one asm block: they follow the weight DMA loads of the kernel's entry,
+// behind which the compiler would otherwise place vector loads and a wait for
+// every load (it cannot see what the DMA loads write).  Scalar loads count
+// apart from them (lgkmcnt), so the weights stay in flight.
+__device__ __forceinline__ void scalar_count_offset(const int32_t* cnt, const int32_t* offp, int& ne,
+                                                    int& off) {
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(ne), "=&s"(off)
+      : "s"(cnt), "s"(offp)
+      : "memory");
+}
+// The wave's 8 token rows of the first pass the same way: trow[i] =
+// slot_tok[first + min(8 w + i, nc - 1)].
+__device__ __forceinline__ void scalar_token_rows(const int32_t* slot_tok, int first, int nc,
+                                                  int (&trow)[8]) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int32_t* p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = slot_tok + first + min(8 * w + i, nc - 1);
+  asm volatile(
+      "s_load_dword %0, %8, 0x0\n\t"
+      "s_load_dword %1, %9, 0x0\n\t"
+      "s_load_dword %2, %10, 0x0\n\t"
+      "s_load_dword %3, %11, 0x0\n\t"
+      "s_load_dword %4, %12, 0x0\n\t"
+      "s_load_dword %5, %13, 0x0\n\t"
+      "s_load_dword %6, %14, 0x0\n\t"
+      "s_load_dword %7, %15, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(trow[0]), "=&s"(trow[1]), "=&s"(trow[2]), "=&s"(trow[3]), "=&s"(trow[4]),
+        "=&s"(trow[5]), "=&s"(trow[6]), "=&s"(trow[7])
+      : "s"(p[0]), "s"(p[1]), "s"(p[2]), "s"(p[3]), "s"(p[4]), "s"(p[5]), "s"(p[6]), "s"(p[7])
+      : "memory");
+}
+
 template <class C>
 __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   constexpr int kRows13 = C::kRows13, kTok = C::kTok;
@@ -237,10 +279,6 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  // both loads in flight at once: the test reads both (off is never negative),
-  // so the compiler cannot sink the second below it
-  const int ne = a.counts[e], off = a.offsets[e];
-  if (ne == 0 || off < 0) return;
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -254,23 +292,37 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   const uint8_t* const sr[2][1] = {{a.s1 + (size_t)e * a.stride[1] + ro * srow},
                                    {a.s3 + (size_t)e * a.stride[3] + ro * srow}};
   const int NB = a.H / kKB;
+  // Weight blocks 0 and 1 of the first pass need only the expert and the rows:
+  // out at entry, before the expert's token count, offset and token rows.
+  issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
+  int ne, off;
+  scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
+  if (ne == 0) {
+    wait_n<0>();  // the DMA lands before the workgroup's LDS is released
+    return;
+  }
+  int trow[8];
+  scalar_token_rows(a.slot_tok, off, min(kTok, ne), trow);
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
-    // The pass's token rows go to LDS by a DMA load of wave 0 issued before
-    // weight blocks 0 and 1 (which need only the expert and the rows), so the
-    // wait for the rows leaves the weights in flight and the activation loads
-    // can follow while block 0 travels.
-    static_assert(kTok <= kWave, "one row-table load per pass");
-    if (w == 0) lds_load4(lds_addr(&sm.row[0]), a.slot_tok + off + c0 + min(lane, nc - 1));
-    issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
-    if (NB > 1)
-      wait_n<kWLoads + kWLoadsOdd>();
-    else
-      wait_n<kWLoads>();
+    if (c0 > 0) {
+      // A later pass: its token rows go to LDS by a DMA load of wave 0 issued
+      // before weight blocks 0 and 1, so the wait for the rows leaves the
+      // weights in flight.
+      static_assert(kTok <= kWave, "one row-table load per pass");
+      if (w == 0) lds_load4(lds_addr(&sm.row[0]), a.slot_tok + off + c0 + min(lane, nc - 1));
+      issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
+      if (NB > 1)
+        wait_n<kWLoads + kWLoadsOdd>();
+      else
+        wait_n<kWLoads>();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) trow[i] = sm.row[min(8 * w + i, nc - 1)];
+    }
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[2][1][NT];
-      gemm_pass_lds<C, 2, 1, NT>(sm, wr, sr, wrow, srow, a.x, nc, a.H, acc);
+      gemm_pass_lds<C, 2, 1, NT>(sm, wr, sr, wrow, srow, a.x, trow, a.H, acc);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = 16 * nt + c16;
@@ -304,10 +356,6 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
   int logical;
   if (!xcd_tile(a.E * tpe, logical)) return;
   const int e = logical / tpe, rtile = logical - e * tpe;
-  // both loads in flight at once: the test reads both (off is never negative),
-  // so the compiler cannot sink the second below it
-  const int ne = a.counts[e], off = a.offsets[e];
-  if (ne == 0 || off < 0) return;
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -325,15 +373,24 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
     wr[0][rt] = a.w2 + (size_t)e * a.stride[4] + ro * wrow;
     sr[0][rt] = a.s2 + (size_t)e * a.stride[5] + ro * srow;
   }
+  // weight blocks 0 and 1 of the first pass out at entry (as in gemm13_lds_kernel)
+  issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
+  int ne, off;
+  scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
+  if (ne == 0) {
+    wait_n<0>();
+    return;
+  }
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
-    issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
-    if (tid < nc) sm.row[tid] = off + c0 + tid;
-    lds_barrier();
+    if (c0 > 0) issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
+    int trow[8];  // the h rows are the sorted slots
+#pragma unroll
+    for (int i = 0; i < 8; ++i) trow[i] = off + c0 + min(8 * w + i, nc - 1);
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
       f32x4 acc[1][2][NT];
-      gemm_pass_lds<C, 1, 2, NT>(sm, wr, sr, wrow, srow, a.h, nc, a.I, acc);
+      gemm_pass_lds<C, 1, 2, NT>(sm, wr, sr, wrow, srow, a.h, trow, a.I, acc);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
