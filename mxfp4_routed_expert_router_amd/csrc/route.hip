@@ -237,23 +237,43 @@ perm_scan_kernel(int32_t* __restrict__ bcnt, int NB, int P, int E, int32_t* coun
                  int32_t* offsets, int32_t* dinfo, int32_t* meta) {
   __shared__ PermSmem<kPermScanThreads> sm;
   const int e = threadIdx.x;
+  // Up to kScanRegs blocks the column of expert e is read once, all loads in
+  // flight together, and kept in registers until its base is known; past that,
+  // in rounds of eight loads, the prefix stored and the base added after.
+  constexpr int kScanRegs = 64;
+  const bool in_regs = NB <= kScanRegs;
+  int col[kScanRegs];
   int run = 0;
   if (e < E) {
-    int b = 0;
-    for (; b + 8 <= NB; b += 8) {  // eight independent loads in flight
-      int c[8];
+    if (in_regs) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = bcnt[(size_t)(b + j) * E + e];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bcnt[(size_t)(b + j) * E + e] = run;
-        run += c[j];
+      for (int b = 0; b < kScanRegs; ++b) {  // unconditional loads: all in flight at once
+        const int v = bcnt[(size_t)min(b, NB - 1) * E + e];
+        col[b] = b < NB ? v : 0;
       }
-    }
-    for (; b < NB; ++b) {
-      const int c = bcnt[(size_t)b * E + e];
-      bcnt[(size_t)b * E + e] = run;
-      run += c;
+#pragma unroll
+      for (int b = 0; b < kScanRegs; ++b) {
+        const int c = col[b];
+        col[b] = run;
+        run += c;
+      }
+    } else {
+      int b = 0;
+      for (; b + 8 <= NB; b += 8) {  // eight independent loads in flight
+        int c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = bcnt[(size_t)(b + j) * E + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          bcnt[(size_t)(b + j) * E + e] = run;
+          run += c[j];
+        }
+      }
+      for (; b < NB; ++b) {
+        const int c = bcnt[(size_t)b * E + e];
+        bcnt[(size_t)b * E + e] = run;
+        run += c;
+      }
     }
   }
   int c[1] = {run}, f[1] = {run > 0 ? 1 : 0};
@@ -269,7 +289,13 @@ perm_scan_kernel(int32_t* __restrict__ bcnt, int NB, int P, int E, int32_t* coun
       dinfo[4 * f[0] + 2] = run;
       dinfo[4 * f[0] + 3] = 0;
     }
-    for (int b = 0; b < NB; ++b) bcnt[(size_t)b * E + e] += c[0];
+    if (in_regs) {
+#pragma unroll
+      for (int b = 0; b < kScanRegs; ++b)
+        if (b < NB) bcnt[(size_t)b * E + e] = col[b] + c[0];
+    } else {
+      for (int b = 0; b < NB; ++b) bcnt[(size_t)b * E + e] += c[0];
+    }
   }
   if (e == 0) {
     offsets[E] = total;
