@@ -272,6 +272,13 @@ __device__ __forceinline__ void scalar_token_rows(const int32_t* slot_tok, int f
       : "memory");
 }
 
+// Whether a workgroup issues its first two weight blocks before it has read
+// its expert's token count: worth it where nearly every expert has tokens (two
+// or more slots per expert on average).  In small batches most experts have
+// none, and the early loads of their workgroups would only add traffic (at 32
+// tokens, top-6 of 384, about a third more w1/w3 bytes).
+__device__ __forceinline__ bool early_wblocks(const LayerArgs& a) { return a.T * a.k >= 2 * a.E; }
+
 template <class C>
 __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   constexpr int kRows13 = C::kRows13, kTok = C::kTok;
@@ -293,14 +300,17 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
                                    {a.s3 + (size_t)e * a.stride[3] + ro * srow}};
   const int NB = a.H / kKB;
   // Weight blocks 0 and 1 of the first pass need only the expert and the rows:
-  // out at entry, before the expert's token count, offset and token rows.
-  issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
+  // where most experts have tokens they go out at entry, before the expert's
+  // token count, offset and token rows are known (early_wblocks).
+  const bool early = early_wblocks(a);
+  if (early) issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
   int ne, off;
   scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
   if (ne == 0) {
-    wait_n<0>();  // the DMA lands before the workgroup's LDS is released
+    if (early) wait_n<0>();  // the DMA lands before the workgroup's LDS is released
     return;
   }
+  if (!early) issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
   int trow[8];
   scalar_token_rows(a.slot_tok, off, min(kTok, ne), trow);
   for (int c0 = 0; c0 < ne; c0 += kTok) {
@@ -373,17 +383,18 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
     wr[0][rt] = a.w2 + (size_t)e * a.stride[4] + ro * wrow;
     sr[0][rt] = a.s2 + (size_t)e * a.stride[5] + ro * srow;
   }
-  // weight blocks 0 and 1 of the first pass out at entry (as in gemm13_lds_kernel)
-  issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
+  // weight blocks 0 and 1 of the first pass as in gemm13_lds_kernel
+  const bool early = early_wblocks(a);
+  if (early) issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
   int ne, off;
   scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
   if (ne == 0) {
-    wait_n<0>();
+    if (early) wait_n<0>();
     return;
   }
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
-    if (c0 > 0) issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
+    if (c0 > 0 || !early) issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
     int trow[8];  // the h rows are the sorted slots
 #pragma unroll
     for (int i = 0; i < 8; ++i) trow[i] = off + c0 + min(8 * w + i, nc - 1);
