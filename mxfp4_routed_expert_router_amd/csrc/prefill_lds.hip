@@ -23,12 +23,6 @@ namespace {
 constexpr int kKB = 256;                // inputs per weight block
 constexpr int kHB = 128;                // inputs per activation half block
 constexpr int kTiles = 2;               // weight tiles per wave (w1 and w3, or two w2 tiles)
-// Loads a wave issues per weight block.  The scale bytes of two blocks come in
-// one load, issued with the even block (one scale load gathers 8 bytes from
-// each of 16 rows, so a load per block costs as much request traffic as the
-// weight halves).
-constexpr int kWLoads = 3 * kTiles;     // even weight block: two 1 KB halves and the scales per tile
-constexpr int kWLoadsOdd = 2 * kTiles;  // odd weight block: the halves only
 constexpr int kXLoads = 2;              // per half block, waves whose tokens are read: two 1 KB quarters
 
 // Two shapes of the same kernels: 8 waves and 64 tokens per pass (one
@@ -36,24 +30,57 @@ constexpr int kXLoads = 2;              // per half block, waves whose tokens ar
 // (two workgroups per CU, 75 KB) for small batches, where each expert has a
 // few tokens and a second resident workgroup hides the first one's pipeline
 // fill.  Wave w stages tokens 8 w .. 8 w + 7 of a pass in both.
-template <int W, int TOK>
+//
+// The scale bytes of the weight tiles come in one of two ways.  Pair loads
+// (any K): one 4-byte load per tile with every even block, the 8 bytes of two
+// blocks from each of the tile's 16 rows.  Such a load touches 16 cache lines
+// for 256 bytes, as many line requests as the tile's two weight halves.  Quad
+// loads (QS: rows of scales a multiple of 16 bytes, i.e. K a multiple of 512,
+// and 16-byte aligned scale tensors): one 16-byte load per wave with every
+// fourth block, lanes 0-31 the 32 bytes of four blocks of each row of tile 0,
+// lanes 32-63 those of tile 1: a quarter of the instructions and half the line
+// requests.  They need twice the LDS, found by keeping the row table and the
+// saliency buffer in the activation stages, which are free when those are used.
+template <int W, int TOK, bool QS>
 struct LdsCfg {
   static constexpr int kWaves = W, kThreads = W * kWave, kTok = TOK, kMaxNT = TOK / 16;
   static constexpr int kRows13 = 16 * W;  // w1/w3 rows per workgroup (one 16-row tile per wave)
   static constexpr int kRows2 = 32 * W;   // w2 rows per workgroup (two 16-row tiles per wave)
+  static constexpr bool kQuad = QS;
+  // loads a wave issues with weight block b: the two 1 KB halves of each tile,
+  // and the scale loads that come with it (kWLoadsBig when b is a multiple of
+  // kScaleEvery)
+  static constexpr int kScaleEvery = QS ? 4 : 2;
+  static constexpr int kWLoadsBig = QS ? 2 * kTiles + 1 : 3 * kTiles;
+  static constexpr int kWLoadsSmall = 2 * kTiles;
   static_assert(TOK == 8 * W, "each wave stages 8 tokens of a pass");
 };
-using CfgBig = LdsCfg<8, 64>;
-using CfgSmall = LdsCfg<4, 32>;
+template <bool QS>
+using CfgBig = LdsCfg<8, 64, QS>;
+template <bool QS>
+using CfgSmall = LdsCfg<4, 32, QS>;
 
 template <class C>
 struct SmemL {
-  uint8_t w[3][C::kWaves][kTiles][2048];   // 16 rows x 128 bytes (see woff)
-  uint8_t x[3][C::kTok * kHB * 2];         // kTok tokens x 128 bf16 (see xoff_h)
-  uint32_t ws[2][C::kWaves][kTiles][64];   // blocks 2p, 2p+1 in slot p % 2: dword d of row r at 16 d + r
-  int row[C::kTok];                        // source row of each staged token
-  float sal[C::kWaves * 64];               // saliency reduction (saliency.h, 8 waves only)
+  static constexpr int kXStage = C::kTok * kHB * 2;  // kTok tokens x 128 bf16 (see xoff_h)
+  uint8_t w[3][C::kWaves][kTiles][2048];             // 16 rows x 128 bytes (see woff)
+  union {
+    uint8_t x[3][kXStage];
+    // between passes: the row table of a later pass in stage 2 (written after
+    // the previous pass's last barrier; stage 2 is loaded again only after the
+    // first barrier of the pass, when every wave has read the table)
+    struct {
+      uint8_t before[2 * kXStage];
+      int row[C::kTok];  // source row of each staged token
+    } t;
+    float sal[C::kWaves * 64];  // saliency reduction after a pass (saliency.h, 8 waves only)
+  } u;
+  // pair loads: blocks 2p, 2p + 1 in slot p % 2, dword d of row r of tile t at
+  // [t][16 d + r]; quad loads: blocks 4p .. 4p + 3 in slot p % 2, byte g of
+  // block b of row r of tile t at 512 t + 32 r + 8 (b % 4) + g
+  uint32_t ws[2][C::kWaves][kTiles][C::kQuad ? 128 : 64];
 };
+static_assert(sizeof(SmemL<CfgBig<true>>) <= 160 * 1024, "LDS of the quad-scale shape");
 
 // Byte offset in a half-block activation tile of token t's 16-byte chunk c (of
 // 16, 8 inputs each): 256 bytes a token, slot c ^ xsw(t), where xsw swaps the
@@ -71,29 +98,35 @@ __device__ __forceinline__ void wait_n() { wait_then_barrier<N>(); }
 // block, and for hb even the weight block), allowing in flight what was issued
 // after them: one weight block and one half block (see the issue order in
 // gemm_pass_lds).  xw: whether this wave loads activations.
+template <class C>
 __device__ __forceinline__ void wait_step(int hb, int NHB, int NB, bool xw) {
   const int wb = (hb + 1) / 2 + 1;  // the weight block issued after step hb's operands
-  const bool w_after = wb < NB, w_even = (wb & 1) == 0;
+  const bool w_after = wb < NB, w_big = wb % C::kScaleEvery == 0;
   const bool x_after = xw && hb + 1 < NHB;
   if (w_after && x_after)
-    w_even ? wait_n<kWLoads + kXLoads>() : wait_n<kWLoadsOdd + kXLoads>();
+    w_big ? wait_n<C::kWLoadsBig + kXLoads>() : wait_n<C::kWLoadsSmall + kXLoads>();
   else if (w_after)
-    w_even ? wait_n<kWLoads>() : wait_n<kWLoadsOdd>();
+    w_big ? wait_n<C::kWLoadsBig>() : wait_n<C::kWLoadsSmall>();
   else if (x_after)
     wait_n<kXLoads>();
   else
     wait_n<0>();
 }
 
-// Weight block b (256 inputs) of the wave's tiles into stage b % 3, and for b
-// even the scale bytes of blocks b and b + 1 into pair slot (b / 2) % 2.  The
+// Weight block b (256 inputs) of the wave's tiles into stage b % 3, and the
+// scale bytes that come with it (pair loads: for b even, those of blocks b and
+// b + 1 into slot (b / 2) % 2; quad loads: for b a multiple of 4, those of
+// blocks b .. b + 3 into slot (b / 4) % 2).  The
 // weight halves carry the non-temporal hint: each is read once a pass, and
 // the L2 then keeps the gathered activation rows that every row tile of the
 // expert reads again (w1/w3 reads 5.50 -> 5.07 GB, 1.375 -> 1.368 ms; the
 // same hint made the MXFP8 kernels 3% slower, so they go without it).
-// Scale lanes: tile row lane % 16, dword lane / 16 of a block pair's 16 bytes
-// (dwords 2, 3 belong to the odd block; past the last block a lane re-reads
-// the even block's).
+// Pair-load lanes: tile row lane % 16, dword lane / 16 of a block pair's 16
+// bytes (dwords 2, 3 belong to the odd block; past the last block a lane
+// re-reads the even block's).  Quad-load lanes: tile lane / 32, row
+// (lane % 32) / 2, bytes 16 (lane % 2) .. +15 of the quad (blocks 4p + 2
+// (lane % 2) and the next); with K a multiple of 512 the blocks come in pairs,
+// and a lane whose pair lies past the last block re-reads the quad's first.
 template <class C, int M, int kRT>
 __device__ __forceinline__ void issue_wblock(SmemL<C>& sm, const uint8_t* const (&wrow0)[M][kRT],
                                              const uint8_t* const (&srow0)[M][kRT], size_t wrow,
@@ -113,8 +146,19 @@ __device__ __forceinline__ void issue_wblock(SmemL<C>& sm, const uint8_t* const 
       const uint8_t* const g = wrow0[m][rt] + (size_t)b * 128;
       lds_load16_nt(lds_addr(dst), g + wr_r * wrow + 16 * wr_c0);
       lds_load16_nt(lds_addr(dst + 1024), g + (8 + wr_r) * wrow + 16 * wr_c1);
-      if (even)
-        lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
+      if constexpr (!C::kQuad)
+        if (even)
+          lds_load4(lds_addr(&sm.ws[(b >> 1) & 1][w][m * kRT + rt][0]), srow0[m][rt] + c16 * srow + so);
+    }
+  if constexpr (C::kQuad)
+    if ((b & 3) == 0) {
+      static_assert(M * kRT == 2, "quad loads: two tiles a wave");
+      const int t = lane >> 5, r = (lane & 31) >> 1, hp = lane & 1;
+      // tile 1's row 0 as an offset from tile 0's (a select of the two array
+      // elements by lane would become an indexed load from scratch)
+      const uint8_t* const sp = srow0[0][0] + (ptrdiff_t)t * (srow0[M - 1][kRT - 1] - srow0[0][0]);
+      const int qo = b * 8 + (b + 2 * hp < NB ? 16 * hp : 0);
+      lds_load16(lds_addr(&sm.ws[(b >> 2) & 1][w][0][0]), sp + r * srow + qo);
     }
 }
 
@@ -169,13 +213,13 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
   auto issue_w = [&](int b) { issue_wblock<C, M, kRT>(sm, wrow0, srow0, wrow, srow, b, NB); };
   auto issue_x = [&](int hb) {
     if (!xw) return;
-    uint8_t* const dst = &sm.x[hb % 3][0];
+    uint8_t* const dst = &sm.u.x[hb % 3][0];
     lds_load16(lds_addr(dst + (8 * w) * 256), xsrc[0] + (size_t)hb * (kHB * 2));
     lds_load16(lds_addr(dst + (8 * w + 4) * 256), xsrc[1] + (size_t)hb * (kHB * 2));
   };
   auto compute = [&](int hb) {
     const int b = hb >> 1, s = b % 3, hh = hb & 1, ps = (b >> 1) & 1, d = 2 * (b & 1) + hh;
-    const uint8_t* const xt = &sm.x[hb % 3][0];
+    const uint8_t* const xt = &sm.u.x[hb % 3][0];
     u32x4 A4[M][kRT];
     float sc[M][kRT];
 #pragma unroll
@@ -183,7 +227,12 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         A4[m][rt] = ld16(&sm.w[s][w][m * kRT + rt][woff(c16, 4 * hh + kb)]);
-        sc[m][rt] = ue8m0_to_f32((sm.ws[ps][w][m * kRT + rt][16 * d + c16] >> (8 * kb)) & 0xFFu);
+        if constexpr (C::kQuad) {
+          const uint8_t* const q = reinterpret_cast<const uint8_t*>(&sm.ws[(b >> 2) & 1][w][0][0]);
+          sc[m][rt] = ue8m0_to_f32(q[512 * (m * kRT + rt) + 32 * c16 + 8 * (b & 3) + 4 * hh + kb]);
+        } else {
+          sc[m][rt] = ue8m0_to_f32((sm.ws[ps][w][m * kRT + rt][16 * d + c16] >> (8 * kb)) & 0xFFu);
+        }
       }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -217,11 +266,11 @@ __device__ __forceinline__ void gemm_pass_lds(SmemL<C>& sm, const uint8_t* const
       if (xw && NHB > 1)
         wait_n<kXLoads>();
       else if (!xw && NB > 1)
-        wait_n<kWLoadsOdd>();
+        wait_n<C::kWLoadsSmall>();  // block 1 is never one that brings scales
       else
         wait_n<0>();
     } else {
-      wait_step(hb, NHB, NB, xw);
+      wait_step<C>(hb, NHB, NB, xw);
     }
     // every wave is past step hb - 1: its slots (x (hb - 1) % 3, and for hb
     // even the weight slot of block hb/2 - 1, and the scale pair slot of
@@ -320,14 +369,14 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
       // before weight blocks 0 and 1, so the wait for the rows leaves the
       // weights in flight.
       static_assert(kTok <= kWave, "one row-table load per pass");
-      if (w == 0) lds_load4(lds_addr(&sm.row[0]), a.slot_tok + off + c0 + min(lane, nc - 1));
+      if (w == 0) lds_load4(lds_addr(&sm.u.t.row[0]), a.slot_tok + off + c0 + min(lane, nc - 1));
       issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
       if (NB > 1)
-        wait_n<kWLoads + kWLoadsOdd>();
+        wait_n<C::kWLoadsBig + C::kWLoadsSmall>();
       else
-        wait_n<kWLoads>();
+        wait_n<C::kWLoadsBig>();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) trow[i] = sm.row[min(8 * w + i, nc - 1)];
+      for (int i = 0; i < 8; ++i) trow[i] = sm.u.t.row[min(8 * w + i, nc - 1)];
     }
     auto pass = [&](auto nt_const) {
       constexpr int NT = decltype(nt_const)::value;
@@ -416,7 +465,7 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
           }
         }
       if constexpr (C::kWaves == 8)
-        if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.sal, off + c0, nc, rtile);
+        if (a.sal_part) saliency_tile<2, NT>(a, acc, act, sm.u.sal, off + c0, nc, rtile);
     };
     if constexpr (C::kMaxNT == 4) {
       switch ((nc + 15) / 16) {
@@ -431,7 +480,7 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
   }
 }
 
-static_assert(CfgBig::kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
+static_assert(CfgBig<false>::kRows2 == kSalRows, "saliency tiles are the w2 workgroup tiles");
 
 }  // namespace
 
@@ -445,7 +494,17 @@ bool prefill_lds_takes(int K, const uint8_t* const* scales, const int64_t* strid
 namespace {
 // Small batches (at most 32 tokens, so at most 32 per expert: one pass) take
 // the 4-wave shape; saliency needs the 8-wave one's 256-row w2 tiles.
-bool small_batch(const LayerArgs& a) { return a.T <= CfgSmall::kTok && !a.sal_part; }
+bool small_batch(const LayerArgs& a) { return a.T <= CfgSmall<false>::kTok && !a.sal_part; }
+
+// Quad scale loads (see LdsCfg): K a multiple of 512, so that each row's
+// K / 32 scale bytes are whole 16-byte chunks, and 16-byte aligned tensors and
+// expert strides.
+bool quad_scales(int K, const uint8_t* const* scales, const int64_t* strides, int n) {
+  if (K % (2 * kKB)) return false;
+  for (int i = 0; i < n; ++i)
+    if ((uintptr_t)scales[i] % 16 || strides[i] % 16) return false;
+  return true;
+}
 
 template <class C>
 void launch13(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -460,18 +519,32 @@ void launch2(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_
 }  // namespace
 
 hipError_t launch_gemm13_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (small_batch(a))
-    launch13<CfgSmall>(a, stream, start, stop);
+  const uint8_t* const sc[2] = {a.s1, a.s3};
+  const int64_t st[2] = {a.stride[1], a.stride[3]};
+  const bool q = quad_scales(a.H, sc, st, 2), small = small_batch(a);
+  if (small && q)
+    launch13<CfgSmall<true>>(a, stream, start, stop);
+  else if (small)
+    launch13<CfgSmall<false>>(a, stream, start, stop);
+  else if (q)
+    launch13<CfgBig<true>>(a, stream, start, stop);
   else
-    launch13<CfgBig>(a, stream, start, stop);
+    launch13<CfgBig<false>>(a, stream, start, stop);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_lds(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (small_batch(a))
-    launch2<CfgSmall>(a, stream, start, stop);
+  const uint8_t* const sc[1] = {a.s2};
+  const int64_t st[1] = {a.stride[5]};
+  const bool q = quad_scales(a.I, sc, st, 1), small = small_batch(a);
+  if (small && q)
+    launch2<CfgSmall<true>>(a, stream, start, stop);
+  else if (small)
+    launch2<CfgSmall<false>>(a, stream, start, stop);
+  else if (q)
+    launch2<CfgBig<true>>(a, stream, start, stop);
   else
-    launch2<CfgBig>(a, stream, start, stop);
+    launch2<CfgBig<false>>(a, stream, start, stop);
   return hipGetLastError();
 }
 

@@ -216,6 +216,18 @@ def test_forward_prefill_many_pairs_lds(moe, orc):
     _forward_case(moe, orc, 700, 256, 256, 20, 2, seed=7, mode=2)
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (700, 512, 512, 20, 2),     # both GEMMs: K = 512, two blocks (the quad's second half past the end); two passes
+    (300, 1536, 1024, 12, 3),   # K = 1536: six blocks, the last quad half full; w2 four blocks
+    (20, 1536, 512, 10, 3),     # the small-batch shape
+])
+def test_forward_prefill_quad_scales(moe, orc, T, H, I, E, k):
+    """K a multiple of 512: the LDS-fed GEMMs load the scale bytes of four
+    blocks of both tiles in one 16-byte load per wave."""
+    say(f"forward prefill quad scales T={T} H={H} I={I} E={E} k={k}")
+    _forward_case(moe, orc, T, H, I, E, k, seed=T + H + I, mode=2)
+
+
 @pytest.mark.parametrize("mode", [1, 2])
 def test_forward_accumulate(moe, orc, mode):
     say(f"forward accumulate mode={mode}")
