@@ -47,6 +47,9 @@ struct LdsCfg {
   static constexpr int kRows13 = 16 * W;  // w1/w3 rows per workgroup (one 16-row tile per wave)
   static constexpr int kRows2 = 32 * W;   // w2 rows per workgroup (two 16-row tiles per wave)
   static constexpr bool kQuad = QS;
+  // small batches: the grid runs over the routing's distinct-expert records
+  // (expert_slots), not over all E experts
+  static constexpr bool kDistinct = W == 4;
   // loads a wave issues with weight block b: the two 1 KB halves of each tile,
   // and the scale loads that come with it (kWLoadsBig when b is a multiple of
   // kScaleEvery)
@@ -321,6 +324,55 @@ __device__ __forceinline__ void scalar_token_rows(const int32_t* slot_tok, int f
       : "memory");
 }
 
+// The expert slots of a grid: all E experts (each workgroup then reads its
+// expert's token count and offset, and leaves at once if there are none), or
+// for the small-batch shape the distinct-expert records of the routing, at
+// most min(E, T k), those past the last distinct expert marked -1.  At 32
+// tokens, top-6 of 384, that is 192 slots for about 95 distinct experts
+// instead of 384, so about 3,500 instead of 10,400 w1/w3 workgroups find
+// nothing to do.
+template <class C>
+__host__ __device__ inline int expert_slots(const LayerArgs& a) {
+  return C::kDistinct ? (a.E < a.T * a.k ? a.E : a.T * a.k) : a.E;
+}
+
+// A workgroup's expert slot and row tile.  Over all E experts: xcd_tile's
+// ranges, an expert's tiles on one XCD.  Over the distinct-expert records,
+// which are dense at the front: XCD x (blockIdx % 8) takes records x, x + 8,
+// x + 16, ..., so the records that have an expert spread over every XCD
+// (contiguous ranges would give them all to the first few).
+template <class C>
+__device__ __forceinline__ bool expert_tile(const LayerArgs& a, int tpe, int& es, int& rtile) {
+  if constexpr (C::kDistinct) {
+    const int j = blockIdx.x >> 3, r = j / tpe;
+    es = (blockIdx.x & 7) + 8 * r;
+    rtile = j - r * tpe;
+    return es < expert_slots<C>(a);
+  } else {
+    int logical;
+    if (!xcd_tile(a.E * tpe, logical)) return false;
+    es = logical / tpe;
+    rtile = logical - es * tpe;
+    return true;
+  }
+}
+template <class C>
+unsigned expert_grid(const LayerArgs& a, int tpe) {
+  return C::kDistinct ? (unsigned)(8 * ((expert_slots<C>(a) + 7) / 8) * tpe) : xcd_grid(a.E * tpe);
+}
+
+// A distinct-expert record (expert, first sorted slot, pairs) by scalar loads.
+__device__ __forceinline__ void scalar_record(const int32_t* rec, int& e, int& off, int& ne) {
+  asm volatile(
+      "s_load_dword %0, %3, 0x0\n\t"
+      "s_load_dword %1, %3, 0x4\n\t"
+      "s_load_dword %2, %3, 0x8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(e), "=&s"(off), "=&s"(ne)
+      : "s"(rec)
+      : "memory");
+}
+
 // Whether a workgroup issues its first two weight blocks before it has read
 // its expert's token count: worth it where nearly every expert has tokens (two
 // or more slots per expert on average).  In small batches most experts have
@@ -332,9 +384,13 @@ template <class C>
 __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   constexpr int kRows13 = C::kRows13, kTok = C::kTok;
   const int tpe = (a.I + kRows13 - 1) / kRows13;
-  int logical;
-  if (!xcd_tile(a.E * tpe, logical)) return;
-  const int e = logical / tpe, rtile = logical - e * tpe;
+  int es, rtile;
+  if (!expert_tile<C>(a, tpe, es, rtile)) return;
+  int e = es, ne = 0, off = 0;
+  if constexpr (C::kDistinct) {
+    scalar_record(a.dinfo + 4 * es, e, off, ne);
+    if (e < 0) return;
+  }
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -351,13 +407,14 @@ __global__ void __launch_bounds__(C::kThreads) gemm13_lds_kernel(LayerArgs a) {
   // Weight blocks 0 and 1 of the first pass need only the expert and the rows:
   // where most experts have tokens they go out at entry, before the expert's
   // token count, offset and token rows are known (early_wblocks).
-  const bool early = early_wblocks(a);
+  const bool early = !C::kDistinct && early_wblocks(a);
   if (early) issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
-  int ne, off;
-  scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
-  if (ne == 0) {
-    if (early) wait_n<0>();  // the DMA lands before the workgroup's LDS is released
-    return;
+  if constexpr (!C::kDistinct) {
+    scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
+    if (ne == 0) {
+      if (early) wait_n<0>();  // the DMA lands before the workgroup's LDS is released
+      return;
+    }
   }
   if (!early) issue_first_wblocks<C, 2, 1>(sm, wr, sr, wrow, srow, a.H);
   int trow[8];
@@ -412,9 +469,13 @@ template <class C>
 __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
   constexpr int kRows2 = C::kRows2, kTok = C::kTok;
   const int tpe = (a.H + kRows2 - 1) / kRows2;
-  int logical;
-  if (!xcd_tile(a.E * tpe, logical)) return;
-  const int e = logical / tpe, rtile = logical - e * tpe;
+  int es, rtile;
+  if (!expert_tile<C>(a, tpe, es, rtile)) return;
+  int e = es, ne = 0, off = 0;
+  if constexpr (C::kDistinct) {
+    scalar_record(a.dinfo + 4 * es, e, off, ne);
+    if (e < 0) return;
+  }
   __shared__ SmemL<C> sm;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -433,13 +494,14 @@ __global__ void __launch_bounds__(C::kThreads) gemm2_lds_kernel(LayerArgs a) {
     sr[0][rt] = a.s2 + (size_t)e * a.stride[5] + ro * srow;
   }
   // weight blocks 0 and 1 of the first pass as in gemm13_lds_kernel
-  const bool early = early_wblocks(a);
+  const bool early = !C::kDistinct && early_wblocks(a);
   if (early) issue_first_wblocks<C, 1, 2>(sm, wr, sr, wrow, srow, a.I);
-  int ne, off;
-  scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
-  if (ne == 0) {
-    if (early) wait_n<0>();
-    return;
+  if constexpr (!C::kDistinct) {
+    scalar_count_offset(a.counts + e, a.offsets + e, ne, off);
+    if (ne == 0) {
+      if (early) wait_n<0>();
+      return;
+    }
   }
   for (int c0 = 0; c0 < ne; c0 += kTok) {
     const int nc = min(kTok, ne - c0);
@@ -508,13 +570,13 @@ bool quad_scales(int K, const uint8_t* const* scales, const int64_t* strides, in
 
 template <class C>
 void launch13(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const int t13 = a.E * ((a.I + C::kRows13 - 1) / C::kRows13);
-  launch_k(gemm13_lds_kernel<C>, dim3(xcd_grid(t13)), dim3(C::kThreads), 0, stream, start, stop, a);
+  const int tpe = (a.I + C::kRows13 - 1) / C::kRows13;
+  launch_k(gemm13_lds_kernel<C>, dim3(expert_grid<C>(a, tpe)), dim3(C::kThreads), 0, stream, start, stop, a);
 }
 template <class C>
 void launch2(const LayerArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const int t2 = a.E * ((a.H + C::kRows2 - 1) / C::kRows2);
-  launch_k(gemm2_lds_kernel<C>, dim3(xcd_grid(t2)), dim3(C::kThreads), 0, stream, start, stop, a);
+  const int tpe = (a.H + C::kRows2 - 1) / C::kRows2;
+  launch_k(gemm2_lds_kernel<C>, dim3(expert_grid<C>(a, tpe)), dim3(C::kThreads), 0, stream, start, stop, a);
 }
 }  // namespace
 
