@@ -54,7 +54,8 @@ extern "C" {
 #define MOE_FP4_EHIP          5  /* a kernel launch failed (hipGetLastError)        */
 
 /* ---- forward modes */
-#define MOE_FP4_MODE_AUTO     0  /* DECODE where it supports the dims, else PREFILL  */
+#define MOE_FP4_MODE_AUTO     0  /* DECODE up to 8 tokens where it supports the    */
+                                 /* dims, else PREFILL                            */
 #define MOE_FP4_MODE_DECODE   1  /* GEMV path for a few tokens (see below)           */
 #define MOE_FP4_MODE_PREFILL  2  /* grouped-GEMM path; any T                         */
 #define MOE_FP4_MODE_PREFILL_MXFP8 3  /* grouped GEMM on FP4 x FP8 scaled MFMA (below)  */

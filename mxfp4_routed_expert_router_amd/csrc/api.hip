@@ -23,11 +23,18 @@ bool dims_ok(const moe_fp4_dims& d) {
          d.I <= 16384 && d.I % 32 == 0;
 }
 
+// AUTO takes the GEMV path up to this many tokens: at H = 5120, I = 2304,
+// top-6 of 384 the few-token GEMV kernels and the small-batch grouped GEMMs
+// take 148 and 150 us per call at T = 8, but 210 against 189 us at T = 12 and
+// 256 against 215 us at T = 15 (graph replay, one MI355X).
+constexpr int kAutoDecodeMaxT = 8;
+
 // Mode that a call actually runs, or -1 if the dims do not allow it.
 int resolve_mode(const moe_fp4_dims& d, int mode) {
   const bool decode_ok = decode_fits(d.T, d.H, d.I, d.k);
   switch (mode) {
-    case MOE_FP4_MODE_AUTO: return decode_ok ? MOE_FP4_MODE_DECODE : MOE_FP4_MODE_PREFILL;
+    case MOE_FP4_MODE_AUTO:
+      return decode_ok && d.T <= kAutoDecodeMaxT ? MOE_FP4_MODE_DECODE : MOE_FP4_MODE_PREFILL;
     case MOE_FP4_MODE_DECODE: return decode_ok ? MOE_FP4_MODE_DECODE : -1;
     case MOE_FP4_MODE_PREFILL: return MOE_FP4_MODE_PREFILL;
     case MOE_FP4_MODE_PREFILL_MXFP8:  // one scaled MFMA covers 128 inputs

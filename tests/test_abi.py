@@ -206,7 +206,10 @@ def test_plan(lib):
     """The kernel path a forward call takes, by size and mode."""
     assert lib.moe_fp4_plan(1, 5120, 2304, 384, 6) == lib.PATH_DECODE_ONE
     assert lib.moe_fp4_plan(6, 5120, 2304, 384, 6) == lib.PATH_DECODE_FEW
-    assert lib.moe_fp4_plan(15, 5120, 2304, 384, 6) == lib.PATH_DECODE_FEW
+    assert lib.moe_fp4_plan(8, 5120, 2304, 384, 6) == lib.PATH_DECODE_FEW
+    # AUTO: the grouped GEMMs from 9 tokens on; DECODE still takes up to 15
+    assert lib.moe_fp4_plan(9, 5120, 2304, 384, 6) == lib.PATH_PREFILL
+    assert lib.moe_fp4_plan(15, 5120, 2304, 384, 6, lib.MODE_DECODE) == lib.PATH_DECODE_FEW
     assert lib.moe_fp4_plan(16, 5120, 2304, 384, 6) == lib.PATH_PREFILL
     assert lib.moe_fp4_plan(2048, 5120, 2304, 384, 6) == lib.PATH_PREFILL
     assert lib.moe_fp4_plan(1, 5120, 2304, 384, 6, lib.MODE_PREFILL) == lib.PATH_PREFILL
