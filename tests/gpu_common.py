@@ -112,3 +112,38 @@ def check_route(route, idx_ref, g_ref, perm_ref, what: str = ""):
     assert np.array_equal(route.pair_slot.cpu().numpy(), slot), what
     g = route.gates.cpu().numpy()
     assert np.max(np.abs(g.astype(np.float64) - g_ref)) <= 1e-6, (what, np.max(np.abs(g - g_ref)))
+
+
+def mx8_w2_on_h(orc, experts, idx, gates, h_bits, H, I):
+    """The MXFP8 mode's w2 stage applied to the GPU's own h: y[t] = sum_j
+    gate[t][j] * W2_e . MXFP8(h[t*k+j]), h in pair order (bf16 bits), quantised
+    by the oracle's quantiser; the E4M3 and FP4 values are exact in float64 and
+    the products are summed in float64 (experts in parallel threads, added in
+    ascending expert order).  Where the GPU's h sits next to an FP8 code
+    boundary its code may differ from the one the oracle's h takes, so the
+    end-to-end y carries those decisions; against this reference only the w2
+    stage's own accumulation remains."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from pins import bf16_to_f64, read_golden
+    T, k = idx.shape
+    codes, sc = orc.mx8_quant(bf16_to_f64(np.asarray(h_bits, np.uint16)))
+    e4 = np.array([orc.e4m3(c) for c in range(256)])
+    hq = e4[codes] * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=-1)
+    g = read_golden("mx_formats.txt")["e2m1_positive"]
+    t16 = np.array(g + [-v for v in g])
+    lut = np.stack([t16[np.arange(256) & 15], t16[np.arange(256) >> 4]], axis=-1)  # byte -> 2 values
+    flat = idx.ravel()
+    gflat = gates.ravel().astype(np.float64)
+
+    def part(e):
+        p = np.nonzero(flat == e)[0]
+        w2, s2 = experts[int(e)]["w2"], experts[int(e)]["s2"]
+        W2 = lut[w2].reshape(H, I) * np.repeat(np.ldexp(1.0, s2.astype(np.int64) - 127), 32, axis=1)
+        return p, gflat[p][:, None] * (hq[p] @ W2.T)
+
+    y = np.zeros((T, H))
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        for p, c in ex.map(part, np.unique(flat)):
+            y[p // k] += c
+    return y

@@ -7,13 +7,16 @@ instruction sums its 128 products with much less than fp32 precision (the
 probes of test_gpu_accum.py measure up to 2^-11.85 of its terms' absolute
 sum), and the h check takes the accumulation model of that instruction
 (tests/accum.py, family mx8): its intervals are wide because the hardware's
-sums are.  y is held end to end against the oracle's MXFP8 forward to the
-layer's rel-L2 <= 2e-3 and to max |error| <= 5e-2 * RMS: the same scaled
-instruction sums w2's products with about 12 bits, and the FP8 codes of h are
-decisions taken from a bf16 h that may lie a step from the oracle's, so single
-elements of y move by up to about 2e-2 * RMS (measured 2.07e-2 at T=70,
-H=256, I=128, k=4), beyond the bf16 path's 2e-2."""
-MX_MAX_ABS_RMS = 5e-2
+sums are.  The FP8 codes of h are then decisions taken from the GPU's own h,
+which may lie across an E4M3 code boundary from the oracle's.  y is therefore
+held to the layer's full tolerance (rel-L2 <= 2e-3, max |error| <= 2e-2 * RMS)
+against the w2 stage applied to the GPU's own h (gpu_common.mx8_w2_on_h),
+which leaves only the w2 stage's accumulation, and end to end to the layer's
+rel-L2 <= 2e-3 against the oracle's MXFP8 forward.  The end-to-end max |error|
+is printed but not bounded: one flipped code of a large h element moves single
+elements of y by up to one E4M3 step of that term (measured 2.07e-2 * RMS over
+the 10.5M outputs of the 2048-token chunk, 8.1e-2 over the 16.8M outputs of a
+65535-token call at H = 256)."""
 import numpy as np
 import pytest
 
@@ -21,7 +24,8 @@ import accum
 import pins
 import synth
 from synth.configs import PREFILL
-from gpu_common import check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
+from gpu_common import (REL_L2, check_h, check_route, check_y, dev_bits, dev_weights, host_bits,
+                        mx8_w2_on_h, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +70,19 @@ def test_quant_mxfp8_bitexact(moe, orc, rows, K):
     assert bad.size == 0, [(tuple(b), int(c[tuple(b)]), int(ref_c[tuple(b)])) for b in bad[:8]]
 
 
+def check_mx_y(orc, experts, route, h_bits, y, ref, H, I, what):
+    """y against the w2 stage on the GPU's own h (full tolerance), and end to end
+    against the oracle's MXFP8 forward (rel-L2)."""
+    own = mx8_w2_on_h(orc, experts, route.topk_idx.cpu().numpy(), route.gates.cpu().numpy(), h_bits,
+                      H, I)
+    check_y(y, own, what + ", w2 stage on the GPU's h")
+    d = np.asarray(y, np.float64) - ref
+    rel = np.linalg.norm(d) / np.linalg.norm(ref)
+    rms = np.sqrt(np.mean(np.asarray(ref, np.float64) ** 2))
+    say(f"  {what}, end to end: rel_l2={rel:.3e} max_abs/rms={np.max(np.abs(d)) / rms:.3e}")
+    assert np.all(np.isfinite(y)) and rel <= REL_L2, (what, rel)
+
+
 def _forward_mx(moe, orc, T, H, I, E, k, seed):
     import torch
     rng = np.random.default_rng(seed)
@@ -82,7 +99,7 @@ def _forward_mx(moe, orc, T, H, I, E, k, seed):
     check_route(route, ref["idx"], ref["gates"], orc.permute(ref["idx"], E), what)
     hb = host_bits(h)
     check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what)
-    check_y(y.cpu().numpy(), ref["y"], what, MX_MAX_ABS_RMS)
+    check_mx_y(orc, experts, route, hb, y.cpu().numpy(), ref["y"], H, I, what)
     return x, lg, w, y
 
 
@@ -146,4 +163,4 @@ def test_prefill_chunk_mxfp8(moe, orc):
     ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, experts, want_h=True, mx8=True,
                       acc=accum.model("mx8", wl.H))
     check_h(h, ref["h"], ref["hpre"], ref["hbound"], "MXFP8 prefill h, all tokens")
-    check_y(y, ref["y"], "MXFP8 prefill y, all tokens", MX_MAX_ABS_RMS)
+    check_mx_y(orc, experts, route, h, y, ref["y"], wl.H, wl.I, "MXFP8 prefill y, all tokens")
