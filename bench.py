@@ -389,6 +389,8 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the warm (graph replay) decode figures: every decode launch is then cold")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read measurement")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip one GPU's share of the layer on eight (decode TP-8, prefill EP-8)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router, shared-expert, verify and stack figures (profiling runs)")
     ap.add_argument("--eager", action="store_true",
@@ -506,6 +508,38 @@ def main():
         sweep()
         step(i, evc[n])
     torch.cuda.synchronize()
+    # One GPU's share of the layer on eight, decode in tensor parallel: the same
+    # tokens and routing, 288 of the 2304 intermediate rows of every expert
+    # (its y is the partial sum an all-reduce of 20 KB a token would complete),
+    # caches cold as above.
+    tp8 = None
+    if not args.no_shards and not args.eager:
+        from synth.configs import DECODE_TP8 as wt
+        w_tp = moe.ExpertWeights.from_dict(synth.layer_device(wt, layer=0, device=dev))
+        ws_tp = torch.empty(moe.moe_fp4_workspace_size(1, wt.H, wt.I, wt.E, wt.k), dtype=torch.uint8,
+                            device=dev)
+
+        def step_tp(i):
+            j = i % n_gen
+            moe.moe_fp4_forward(x_d[j:j + 1], lg_d[j:j + 1], w_tp, wt.k, y=y_d[j:j + 1], workspace=ws_tp)
+
+        for i in range(args.warmup):
+            sweep()
+            step_tp(i)
+        g_c = graph_of(lambda n: (sweep(), step_tp(args.warmup + n)), args.steps)
+        g_s = graph_of(lambda n: sweep(), args.steps)
+        us_tp = (replay_us(g_c) - replay_us(g_s)) / args.steps
+        del g_c, g_s
+        b_tp = float(np.mean([sum(v for n, v in decode_bytes(wt, idx_all[i][None]).items() if n != "D")
+                              for i in timed_ids]))
+        tp8 = {"workload": "decode T=1, E=384, top-6, H=5120, I=288 (one GPU's 1/8 of every expert's "
+                           "intermediate rows), the decode workload's tokens, L2 and MALL cold",
+               "us_per_token": us_tp, "bytes_per_step": b_tp,
+               "GBps": b_tp / (us_tp * 1e-6) / 1e9, "hbm_frac": b_tp / (us_tp * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+               "note": "one GPU's share only: its y is a partial sum; the all-reduce of T x 5120 fp32 "
+                       "that completes it on eight GPUs is not run (one GPU)"}
+        log(f"decode TP-8 shard (I=288): {us_tp:.2f} us/token cold, {tp8['GBps']:.0f} GB/s")
+        del w_tp, ws_tp
     del fbuf, fsink
     if args.eager:
         ev = [e.events for e in evc]
@@ -639,6 +673,44 @@ def main():
                                  "MXFP8 (x and h quantised; FP4 x FP8 scaled MFMA 16x16x128)",
                                  FP8_PEAK_TFLOPS)
 
+    # One GPU's share of the 2048-token chunk on eight, expert parallel: 48
+    # experts and the 1,536 pairs routed to them (32 an expert, as in the chunk)
+    ep8 = None
+    if args.prefill_reps > 0 and not args.no_shards:
+        from synth.configs import PREFILL_EP8 as we
+        w_ep = moe.ExpertWeights.from_dict(synth.layer_device(we, layer=0, device=dev))
+        xe = torch.from_numpy(synth.gen_x(we, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+        le_np = synth.gen_logits(we, 0)
+        le = torch.from_numpy(le_np).to(dev)
+        ye = torch.empty((we.T, we.H), dtype=torch.float32, device=dev)
+        De = len(np.unique(topk_sets(le_np, we.k)))
+        e_bytes = De * expert_bytes(we.H, we.I) + we.T * we.H * 2 + we.T * we.H * 4
+        ep8 = {"workload": "48 experts (one GPU's 1/8 of 384), 256 tokens top-6 over them: 1,536 pairs, "
+                           "32 an expert, H=5120, I=2304, Zipf(0.3) logit bias",
+               "distinct_experts": De, "bytes": e_bytes}
+        for mode, name in ((moe.MODE_PREFILL, "bf16"), (moe.MODE_PREFILL_MXFP8, "mxfp8")):
+            wse = torch.empty(moe.moe_fp4_workspace_size(we.T, we.H, we.I, we.E, we.k, mode),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                moe.moe_fp4_forward(xe, le, w_ep, we.k, y=ye, mode=mode, workspace=wse)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.prefill_reps)]
+            for e0, e1 in evs:
+                e0.record()
+                moe.moe_fp4_forward(xe, le, w_ep, we.k, y=ye, mode=mode, workspace=wse)
+                e1.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+            full = (prefill if mode == moe.MODE_PREFILL else prefill_mx)["ms_per_chunk"]
+            ep8[name] = {"ms": ms, "GBps": e_bytes / (ms * 1e-3) / 1e9,
+                         "hbm_frac": e_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "full_chunk_ms_over_8": full / 8}
+            log(f"prefill EP-8 shard ({name}): {ms:.3f} ms, {ep8[name]['GBps']:.0f} GB/s "
+                f"(full chunk / 8: {full / 8:.3f} ms)")
+            del wse
+        ep8["note"] = ("one GPU's share only: the all-to-all that brings each GPU its pairs' x rows "
+                       "and the one that returns their outputs are not run (one GPU)")
+        del w_ep
     del w
     torch.cuda.empty_cache()
     stream = None if args.no_stream else run_stream(torch, dev)
@@ -689,6 +761,7 @@ def main():
         "stack": stack,
         "prefill": prefill,
         "prefill_mxfp8": prefill_mx,
+        "shards": {"decode_tp8": tp8, "prefill_ep8": ep8},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))

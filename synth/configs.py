@@ -56,4 +56,17 @@ STACK1 = Workload("stack1", T=1, H=5120, I=2304, E=138, k=6, zipf_s=1.1, layers=
 STACK6 = Workload("stack6", T=6, H=5120, I=2304, E=138, k=6, zipf_s=1.1, layers=40, steps=64,
                   weight_seed=WEIGHT_SEED + 7, input_seed=INPUT_SEED + 7)
 
+# One GPU's share of the layer when eight GPUs hold it.  Decode in tensor
+# parallel: the routing is replicated and each GPU holds 288 of the 2304
+# intermediate rows of every expert (w1/w3 [288, 2560 B] + [288, 160], w2
+# [5120, 144 B] + [5120, 9]); its y is a partial sum that an all-reduce
+# completes.  The inputs are the decode workload's.  Prefill in expert
+# parallel: each GPU holds 48 of the 384 experts and receives the pairs routed
+# to them, about 1,536 of the chunk's 12,288 (32 an expert); here 256 tokens
+# routed top-6 over 48 experts give the same pairs per expert.
+DECODE_TP8 = Workload("decode_tp8", T=1, H=5120, I=288, E=384, k=6, zipf_s=1.1, steps=256,
+                      weight_seed=WEIGHT_SEED + 9, input_seed=INPUT_SEED + 2)
+PREFILL_EP8 = Workload("prefill_ep8", T=256, H=5120, I=2304, E=48, k=6, zipf_s=0.3,
+                       input_seed=INPUT_SEED + 8)
+
 ALL = {w.name: w for w in (TINY, DECODE, VERIFY6, VERIFY32, PREFILL, STACK1, STACK6)}

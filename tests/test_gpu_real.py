@@ -7,7 +7,7 @@ import pytest
 
 import accum
 import synth
-from synth.configs import DECODE, PREFILL, STACK1, STACK6, VERIFY6, VERIFY32
+from synth.configs import DECODE, DECODE_TP8, PREFILL, PREFILL_EP8, STACK1, STACK6, VERIFY6, VERIFY32
 from gpu_common import check_h, check_route, check_y, dev_bits, host_bits, say
 
 pytestmark = pytest.mark.gpu
@@ -94,6 +94,31 @@ def test_prefill_chunk(moe, orc, layer):
                       acc=accum.forward_model(wl.T, wl.H, wl.I, wl.E, wl.k, 0))
     check_h(h, ref["h"], ref["hpre"], ref["hbound"], "prefill h, all tokens")
     check_y(y, ref["y"], "prefill y, all tokens")
+
+
+@pytest.mark.parametrize("wl,steps", [(DECODE_TP8, (0, 1, 2)), (PREFILL_EP8, (0,))],
+                         ids=["decode_tp8_shard", "prefill_ep8_shard"])
+def test_one_gpu_share_of_eight(moe, orc, wl, steps):
+    """One GPU's share of the layer on eight: decode with 288 of the 2304
+    intermediate rows of all 384 experts (its y a partial sum), prefill with 48
+    experts and about 1,536 pairs.  Every token against the oracle."""
+    import torch
+    say(f"{wl.name}: generating {wl.E} experts at I={wl.I}")
+    w = moe.ExpertWeights.from_dict(synth.layer_device(wl, layer=0))
+    torch.cuda.synchronize()
+    try:
+        for step in steps:
+            x, lg, y, h, route = _run(moe, wl, w, step)
+            idx, g = orc.route(lg, wl.k)
+            what = f"{wl.name} step {step}, path {moe.moe_fp4_plan(wl.T, wl.H, wl.I, wl.E, wl.k)}"
+            check_route(route, idx, g, orc.permute(idx, wl.E), what)
+            ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, _experts(wl, 0, idx), want_h=True,
+                              acc=accum.forward_model(wl.T, wl.H, wl.I, wl.E, wl.k, 0))
+            check_h(h, ref["h"], ref["hpre"], ref["hbound"], what)
+            check_y(y, ref["y"], what)
+    finally:
+        del w
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("wl", [STACK1, STACK6], ids=["T1", "T6"])

@@ -178,6 +178,8 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (1, 1568, 96, 7, 3),      # one token, two slots a lane, the second one ragged (49 groups a row)
     (1, 3104, 160, 9, 4),     # one token, four slots, one group in the last
     (1, 8192, 128, 8, 4),     # one token, eight slots a lane (H = 8192)
+    (1, 256, 128, 1024, 16),  # one token, E = 1024: the routing kernel feeds the one-token kernels
+    (1, 512, 256, 600, 6),    # one token, E = 600 (above the 512 the w1/w3 kernel ranks itself)
     (100, 64, 32, 1024, 16),  # E = 1024, k = 16: the largest router tables, 1600 pairs
     (2, 8192, 256, 8, 4),     # few-token GEMV path, 4 groups a lane (H = 8192)
     (6, 1024, 2304, 12, 8),   # few-token path at T = 6, two (pair, group)s a lane in w2
