@@ -752,9 +752,17 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int H = a.H, I = a.I, CPR = I / 32;
-  const int NP = a.k * CPR, PW = (NP + kWaves - 1) / kWaves;
+  const int NP = a.k * CPR;
+  // Where a row's pairs fit one wave (NP <= 64, e.g. one GPU's 288 rows of each
+  // expert: 6 x 9 pairs), each wave takes whole rows m0 + w, m0 + w + 8, ...
+  // with all its pairs and a row's sum is its wave's; otherwise the pairs are
+  // split over the 8 waves, every wave takes every row, and the 8 partials of
+  // a row are added in wave order.
+  const bool rw = NPL == 1 && NP <= kWave;
+  const int PW = rw ? NP : (NP + kWaves - 1) / kWaves, pw0 = rw ? 0 : w * PW;
   const int R = (H + nblk - 1) / nblk, m0 = bid * R;
   const int m1 = min(H, m0 + R);
+  const int r0 = rw ? m0 + w : m0, rs = rw ? kWaves : 1;  // this wave's first row and row step
   if (m0 >= H) return;  // whole workgroup
 
   const uint8_t* wp[NPL];
@@ -767,7 +775,7 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
     u32x4 hr[NPL][4];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int p = w * PW + lane + kWave * j;
+      const int p = pw0 + lane + kWave * j;
       const int pc = (lane + kWave * j < PW && p < NP) ? p : 0;
       const int jj = pc / CPR;
       gg[j] = pc - jj * CPR;
@@ -786,7 +794,7 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
     }
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int p = w * PW + lane + kWave * j;
+      const int p = pw0 + lane + kWave * j;
       const bool ok = lane + kWave * j < PW && p < NP;
       wp[j] = a.w2 + (size_t)ev[j] * a.stride[4] + gg[j] * 16;
       sp[j] = a.s2 + (size_t)ev[j] * a.stride[5] + gg[j];
@@ -844,13 +852,14 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
   if (routed) {
 #pragma unroll
   for (int b = 0; b < kOneDP; ++b) {
-    load(b, m0 + b);
+    load(b, r0 + rs * b);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int m = m0; m < m1; m += kOneDP) {
+  for (int m = r0; m < m1; m += rs * kOneDP) {
 #pragma unroll
     for (int b = 0; b < kOneDP; ++b) {
-      if (m + b < m1) {
+      const int mb = m + rs * b;
+      if (mb < m1) {
         float p = 0.f;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
@@ -861,9 +870,9 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
           p += gt[j] * t;
         }
         p = wave_sum_f32(p);
-        if (lane == 0) part[w][m + b - m0] = p;
+        if (lane == 0) part[rw ? 0 : w][mb - m0] = p;
       }
-      load(b, m + b + kOneDP);
+      load(b, mb + rs * kOneDP);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -893,8 +902,12 @@ __device__ __forceinline__ void gemv2_one_body(const LayerArgs& a, int bid, int 
     float v;
     if (routed) {
       float s = 0.f;
+      if (rw) {
+        s += part[0][tid];
+      } else {
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) s += part[q][tid];
+        for (int q = 0; q < kWaves; ++q) s += part[q][tid];
+      }
       v = a.accumulate ? *yp + s : s;
       if constexpr (SC > 0) v = v + shr[tid];
     } else if constexpr (SC > 0) {
