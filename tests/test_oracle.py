@@ -52,3 +52,23 @@ def test_gate_invariants_large(orc):
     assert np.all(np.diff(g, axis=1) <= 0)
     counts, offsets, sp, slot = orc.permute(idx, 384)
     assert counts.sum() == 2048 * 6
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(50, 256, 128, 8, 2), (9, 384, 256, 7, 3)])
+def test_mx8_w2_reference_matches_oracle(orc, T, H, I, E, k):
+    """The GPU tests' reference for the MXFP8 w2 stage (numpy: the oracle's
+    quantiser on a given h, exact FP4 and E4M3 values, float64 products) gives
+    the oracle's own MXFP8 y when handed the oracle's h: two implementations of
+    the same stage agree to the rounding of y to float32."""
+    from gpu_common import mx8_w2_on_h
+    rng = np.random.default_rng(T + H + I)
+    experts = {e: pins.random_expert(rng, H, I) for e in range(E)}
+    x = pins.rand_bf16(rng, (T, H))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ref = orc.forward(H, I, E, k, x, lg, experts, want_h=True, mx8=True)
+    y = mx8_w2_on_h(orc, experts, ref["idx"], ref["gates"], ref["h"], H, I)
+    yo = ref["y"].astype(np.float64)
+    assert np.max(np.abs(y - yo)) <= 1e-6 * np.sqrt(np.mean(yo ** 2))
+    # and it is not the bf16 path's w2 stage: quantising h moves y
+    yb = orc.forward(H, I, E, k, x, lg, experts)["y"].astype(np.float64)
+    assert np.linalg.norm(y - yb) > 1e-3 * np.linalg.norm(yb)
