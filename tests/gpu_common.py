@@ -71,7 +71,7 @@ def _bf16_rne_stats(v):
 
 
 def check_h(h_gpu: np.ndarray, h_ref: np.ndarray, hpre: np.ndarray, hbound: np.ndarray,
-            what: str = ""):
+            what: str = "", rel_max: float = None):
     """h is rounded to bf16 at the same point on both sides.  The kernel's value
     before rounding lies within the oracle's bound b of the exact value hpre
     (b from the accumulation model of the kernel family that ran: tests/accum.py),
@@ -80,7 +80,9 @@ def check_h(h_gpu: np.ndarray, h_ref: np.ndarray, hpre: np.ndarray, hbound: np.n
     value the GPU must match the oracle exactly, where it holds two, the GPU may
     take the adjacent value.  An exact rule, not a tolerance on a count.
     Prints the mismatch count, the largest distance in bf16 steps and the
-    interval widths."""
+    interval widths.  rel_max, where given, also bounds the relative L2
+    distance of the GPU's h from the oracle's: a statistical guard for paths
+    whose per-element intervals are wide (the MXFP8 mode's)."""
     import oracle
     h_gpu = np.asarray(h_gpu, np.uint16)
     h_ref = np.asarray(h_ref, np.uint16)
@@ -88,9 +90,13 @@ def check_h(h_gpu: np.ndarray, h_ref: np.ndarray, hpre: np.ndarray, hbound: np.n
     n = len(bad[0])
     dist = np.abs(_bf16_order(h_gpu) - _bf16_order(h_ref))
     width = _bf16_order(_bf16_rne_stats(hpre + hbound)) - _bf16_order(_bf16_rne_stats(hpre - hbound)) + 1
+    hg, hr = bf16_value(h_gpu), bf16_value(h_ref)
+    rel = np.linalg.norm(hg - hr) / max(np.linalg.norm(hr), 1e-300)
     say(f"  {what}: h mismatches {n} of {h_ref.size} (largest {int(dist.max()) if dist.size else 0} "
-        f"bf16 steps); interval width median {np.median(width):.0f}, p90 "
+        f"bf16 steps, rel_l2 {rel:.2e}); interval width median {np.median(width):.0f}, p90 "
         f"{np.percentile(width, 90):.0f}, p99 {np.percentile(width, 99):.0f} values")
+    if rel_max is not None:
+        assert rel <= rel_max, (what, rel)
     if n == 0:
         return
     o = oracle.get()

@@ -10,7 +10,7 @@ import pytest
 import accum
 import pins
 from gpu_common import check_h, check_route, check_y, dev_bits, dev_weights, host_bits, say
-from test_gpu_mx8 import check_mx_y
+from test_gpu_mx8 import MX_H_REL_L2, check_mx_y
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_forward_at_token_limit(moe, orc, H, I, E, k, mode):
     what = f"T={T_MAX} H={H} I={I} E={E} k={k} mode={mode}"
     check_route(route, ref["idx"], ref["gates"], orc.permute(ref["idx"], E), what)
     hb = host_bits(h)
-    check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what)
+    check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what, MX_H_REL_L2 if mx else None)
     if mx:
         check_mx_y(orc, experts, route, hb, y.cpu().numpy(), ref["y"], H, I, what)
     else:

@@ -98,10 +98,15 @@ def _forward_mx(moe, orc, T, H, I, E, k, seed):
     what = f"MXFP8 T={T} H={H} I={I} E={E} k={k}"
     check_route(route, ref["idx"], ref["gates"], orc.permute(ref["idx"], E), what)
     hb = host_bits(h)
-    check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what)
+    check_h(hb, ref["h"], ref["hpre"], ref["hbound"], what, MX_H_REL_L2)
     check_mx_y(orc, experts, route, hb, y.cpu().numpy(), ref["y"], H, I, what)
     return x, lg, w, y
 
+
+# The GPU's h against the oracle's, relative L2: measured 2e-6 to 2.4e-4 over
+# these cases, the 2048-token chunk and a 65535-token call; wrong scales, tiles
+# or rows would give O(1).
+MX_H_REL_L2 = 2e-3
 
 MX_CASES = [  # (T, H, I, E, k): H and I multiples of 128
     (8, 256, 128, 16, 2),
@@ -162,5 +167,5 @@ def test_prefill_chunk_mxfp8(moe, orc):
     experts = {int(e): synth.expert_host(wl, 0, int(e)) for e in np.unique(idx)}
     ref = orc.forward(wl.H, wl.I, wl.E, wl.k, x, lg, experts, want_h=True, mx8=True,
                       acc=accum.model("mx8", wl.H))
-    check_h(h, ref["h"], ref["hpre"], ref["hbound"], "MXFP8 prefill h, all tokens")
+    check_h(h, ref["h"], ref["hpre"], ref["hbound"], "MXFP8 prefill h, all tokens", MX_H_REL_L2)
     check_mx_y(orc, experts, route, h, y, ref["y"], wl.H, wl.I, "MXFP8 prefill y, all tokens")
