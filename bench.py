@@ -501,9 +501,14 @@ def main():
     # kernel's dispatch recording its own start and end events
     # (moe_fp4_forward_profiled); warm-up steps are cold too, so every launch of
     # the decode kernels in a --no-warm run is a cold one
+    # (the W warm-up steps run again first, inside the host's head start: the
+    # first launches after the spin are slower while the clocks come back)
     evc = [moe.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(SPIN_CYCLES)
+    for i in range(args.warmup):
+        sweep()
+        step(i)
     for n, i in enumerate(timed_ids):
         sweep()
         step(i, evc[n])
@@ -582,6 +587,8 @@ def main():
         evs = [moe.StageEvents() for _ in range(args.steps)]
         torch.cuda.synchronize()
         torch.cuda._sleep(SPIN_CYCLES)
+        for i in range(args.warmup):
+            step(i)
         for n, i in enumerate(timed_ids):
             step(i, evs[n])
         torch.cuda.synchronize()
