@@ -21,6 +21,7 @@ same units of work.
 from __future__ import annotations
 
 import argparse
+import re
 import json
 import os
 import sys
@@ -97,6 +98,37 @@ def profiled_traffic(kernel):
         return None
     k = rec["kernels"][kernel]
     return float(k["read_bytes"] + k["write_bytes"])
+
+
+TRACE_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                             "moe_layer_decode_T1_prefill_T2048_kernel_trace.md")
+
+
+def library_sources_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mxfp4_routed_expert_router_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traced_mean_us(kernel):
+    """Mean duration of `kernel` (the row whose name starts with it) in the
+    committed rocprofv3 kernel trace, or None when the library's sources differ
+    from the ones the trace was taken with."""
+    try:
+        text = open(TRACE_PROFILE).read()
+    except OSError:
+        return None
+    m = re.search(r"sha256 prefix `([0-9a-f]+)`", text)
+    if not m or m.group(1) != library_sources_hash():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 4 and cells[1].strip("`").startswith(kernel):
+            return float(cells[3])
+    return None
 
 
 def run_extras(args, moe, synth, torch, dev, w, wl, x_d, lg_d, y_d, ws, n_gen, graph_us):
@@ -749,6 +781,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(DECODE_KERNELS[dom]), "traffic_unit": "bytes/launch",
                      "bytes_per_launch": k_bytes[dom], "avg_us": k_us[dom],
+                     "trace_avg_us": traced_mean_us(DECODE_KERNELS[dom]),
                      "note": "cold launches (L2 and MALL flushed before each step)"},
         "kernels_us": {n: (round(v, 3) if v is not None else None) for n, v in k_us.items()},
         "timing": ("value (--eager): mean span from the start of each cold step's first kernel to "
