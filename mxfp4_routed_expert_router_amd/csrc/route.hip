@@ -320,31 +320,29 @@ perm_scatter_kernel(const int32_t* __restrict__ idx, const float* __restrict__ g
                                    slot_tok, sm);
 }
 
-// Few tokens (T <= kFewRouteTokens, at most kFewRoutePairs pairs): the 16 waves
-// rank the tokens (wave w: tokens w, w + 16, ...), and the permutation needs no histogram
-// or scan: pair p's sorted slot is the number of pairs with a lower expert
-// plus the pairs of its expert before p (the same stable order as
-// block_permute), counts and offsets are counts over the P pairs, and a slot
-// whose expert differs from the previous slot's starts a distinct-expert
-// record.
+// Few tokens (T <= kFewRouteTokens <= 64, at most kFewRoutePairs pairs): the 16
+// waves rank the tokens (wave w: tokens w, w + 16, ...) and set bit t of expert
+// e's token mask for each choice; a token's k experts are distinct, so expert
+// e's pairs in pair order are its tokens in token order.  Thread x then counts
+// expert x's pairs (popcount of its mask) and one block scan gives, packed in
+// one int, its first sorted slot and its distinct-expert record index; pair
+// (t, j) lands in slot first(e) + popcount(mask(e) below bit t).  That is the
+// stable (expert, pair id) order of the many-token permutation.
 constexpr int kFewRouteThreads = 1024;
-static_assert(kFewRoutePairs <= kFewRouteThreads, "one pair a thread");
-
-// LDS reads of four consecutive ints (arrays padded to a multiple of 4)
-__device__ __forceinline__ int4 lds4(const int* p) { return *reinterpret_cast<const int4*>(p); }
+static_assert(kFewRouteThreads == kMaxExperts, "one expert a thread");
+static_assert(kFewRouteTokens <= 64, "a 64-bit token mask per expert");
+static_assert(kFewRoutePairs <= kMaxExperts, "slots and records packed in 16 bits each");
 
 template <int VPL>
 __global__ void __launch_bounds__(kFewRouteThreads)
 route_few_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t* idx, float* gates,
                  int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot,
                  int32_t* dinfo, int32_t* meta, float* slot_gate, int32_t* slot_tok) {
-  __shared__ __align__(16) int pe[kFewRoutePairs];  // expert of pair p (padding: INT_MAX)
-  __shared__ __align__(16) int se[kFewRoutePairs];  // expert of sorted slot s (padding: INT_MAX)
-  __shared__ float pg[kFewRoutePairs];              // gate of pair p
-  __shared__ int first[kFewRoutePairs + 1];         // first slot of distinct expert d
-  __shared__ int wstarts[kFewRouteThreads / kWave];
+  __shared__ unsigned long long tmask[kMaxExperts];  // bit t: token t chose expert x
+  __shared__ int first[kMaxExperts];                 // first sorted slot of expert x
+  __shared__ int wsum[2 * kWave + 1];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int P = T * k, P4 = (P + 3) & ~3;
+  const int P = T * k;
   // every logit row of the wave's tokens is loaded before the first is ranked
   constexpr int NW = kFewRouteThreads / kWave, kTPW = (kFewRouteTokens + NW - 1) / NW;
   float lv[kTPW][VPL];
@@ -353,81 +351,60 @@ route_few_kernel(const float* __restrict__ logits, int T, int E, int k, int32_t*
     const int t = w + NW * j;
     wave_load_logits<VPL>(logits + (size_t)(t < T ? t : 0) * E, E, lane, lv[j]);
   }
+  tmask[tid] = 0ull;
+  lds_barrier();
+  int pe[kTPW];  // lane j < k: the expert and gate of rank j of the wave's token j
+  float pg[kTPW];
 #pragma unroll
   for (int j = 0; j < kTPW; ++j) {
     const int t = w + NW * j;
+    pe[j] = 0;
+    pg[j] = 0.f;
     if (t < T) {
-      int e;
-      float g;
-      wave_topk_vals<VPL>(lv[j], E, k, lane, e, g);
+      wave_topk_vals<VPL>(lv[j], E, k, lane, pe[j], pg[j]);
       if (lane < k) {
-        pe[t * k + lane] = e;
-        pg[t * k + lane] = g;
-        idx[t * k + lane] = e;
-        gates[t * k + lane] = g;
+        atomicOr(&tmask[pe[j]], 1ull << t);
+        idx[t * k + lane] = pe[j];
+        gates[t * k + lane] = pg[j];
       }
     }
   }
-  if (tid >= P && tid < P4) {
-    pe[tid] = 0x7FFFFFFF;
-    se[tid] = 0x7FFFFFFF;
-  }
   lds_barrier();
-  if (tid < P) {  // P <= kFewRoutePairs = kFewRouteThreads: one pair a thread
-    const int e = pe[tid];
-    int sl = 0;
-    for (int q = 0; q < P4; q += 4) {
-      const int4 v = lds4(pe + q);
-      sl += (v.x < e || (v.x == e && q + 0 < tid)) ? 1 : 0;
-      sl += (v.y < e || (v.y == e && q + 1 < tid)) ? 1 : 0;
-      sl += (v.z < e || (v.z == e && q + 2 < tid)) ? 1 : 0;
-      sl += (v.w < e || (v.w == e && q + 3 < tid)) ? 1 : 0;
-    }
-    se[sl] = e;
-    pair_slot[tid] = sl;
-    sorted_pairs[sl] = tid;
-    if (slot_tok) slot_tok[sl] = tid / k;
-    if (slot_gate) slot_gate[sl] = pg[tid];
-  }
-  lds_barrier();
-  for (int x = tid; x < E; x += kFewRouteThreads) {
-    int below = 0, cnt = 0;
-    for (int q = 0; q < P4; q += 4) {
-      const int4 v = lds4(se + q);
-      below += (v.x < x ? 1 : 0) + (v.y < x ? 1 : 0) + (v.z < x ? 1 : 0) + (v.w < x ? 1 : 0);
-      cnt += (v.x == x ? 1 : 0) + (v.y == x ? 1 : 0) + (v.z == x ? 1 : 0) + (v.w == x ? 1 : 0);
-    }
-    counts[x] = cnt;
-    offsets[x] = below;
-  }
-  // distinct-expert records: slot s starts one when s == 0 or its expert
-  // differs from slot s - 1; the record index is the number of starts before it
-  const bool start = tid < P && (tid == 0 || se[tid] != se[tid - 1]);
-  const uint64_t bal = __ballot(start);
-  if (lane == 0) wstarts[w] = __popcll(bal);
-  lds_barrier();
-  int d = __popcll(bal & ((1ull << lane) - 1ull)), nd = 0;
-  for (int q = 0; q < kFewRouteThreads / kWave; ++q) {
-    const int c = wstarts[q];
-    d += q < w ? c : 0;
-    nd += c;
-  }
-  if (start) first[d] = tid;
-  if (tid == 0) first[nd] = P;
-  lds_barrier();
-  if (dinfo) {
-    if (start) {
-      dinfo[4 * d + 0] = se[tid];
-      dinfo[4 * d + 1] = tid;
-      dinfo[4 * d + 2] = first[d + 1] - tid;
+  const unsigned long long m = tid < E ? tmask[tid] : 0ull;
+  const int c = __popcll(m);
+  int v[1] = {c | (c ? 1 << 16 : 0)};
+  int tot;
+  block_excl_scan_e<kFewRouteThreads>(v, wsum, &tot);
+  const int f = v[0] & 0xFFFF, d = v[0] >> 16, nd = tot >> 16;
+  first[tid] = f;
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = f;
+    if (dinfo && c) {
+      dinfo[4 * d + 0] = tid;
+      dinfo[4 * d + 1] = f;
+      dinfo[4 * d + 2] = c;
       dinfo[4 * d + 3] = 0;
     }
-    // records past the last distinct expert (up to min(P, E)) say "no expert"
-    for (int x = nd + tid; x < (P < E ? P : E); x += kFewRouteThreads) dinfo[4 * x] = -1;
   }
+  // records past the last distinct expert (up to min(P, E)) say "no expert"
+  if (dinfo && tid >= nd && tid < (P < E ? P : E)) dinfo[4 * tid] = -1;
   if (tid == 0) {
     offsets[E] = P;
     if (meta) meta[0] = nd;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int t = w + NW * j;
+    if (t < T && lane < k) {
+      const int e = pe[j], p = t * k + lane;
+      const int sl = first[e] + __popcll(tmask[e] & ((1ull << t) - 1ull));
+      pair_slot[p] = sl;
+      sorted_pairs[sl] = p;
+      if (slot_tok) slot_tok[sl] = t;
+      if (slot_gate) slot_gate[sl] = pg[j];
+    }
   }
 }
 
