@@ -36,6 +36,9 @@ ROUTE_CASES = [  # (T, E, k, seed)
     (1, 1, 1, 0), (1, 384, 6, 1), (8, 16, 2, 2), (6, 384, 6, 3), (32, 384, 6, 4), (64, 384, 6, 5),
     (65, 384, 6, 6), (2048, 384, 6, 7), (3, 1024, 16, 8), (100, 1024, 16, 9), (5, 16, 16, 10),
     (3000, 7, 7, 11), (200, 138, 6, 12), (171, 64, 1, 13),
+    # the one-launch routing at its limits: 1024 pairs over 1024 experts, and
+    # 1024 pairs over 64 experts (each expert's 64-token mask full or nearly)
+    (64, 1024, 16, 14), (64, 64, 16, 15), (64, 17, 16, 16),
 ]
 
 
@@ -180,6 +183,7 @@ FORWARD_CASES = [  # (T, H, I, E, k)
     (1, 8192, 128, 8, 4),     # one token, eight slots a lane (H = 8192)
     (1, 256, 128, 1024, 16),  # one token, E = 1024: the routing kernel feeds the one-token kernels
     (1, 512, 256, 600, 6),    # one token, E = 600 (above the 512 the w1/w3 kernel ranks itself)
+    (64, 256, 128, 1024, 16), # 1024 pairs over 1024 experts: the one-launch routing's limit
     (100, 64, 32, 1024, 16),  # E = 1024, k = 16: the largest router tables, 1600 pairs
     (2, 8192, 256, 8, 4),     # few-token GEMV path, 4 groups a lane (H = 8192)
     (6, 1024, 2304, 12, 8),   # few-token path at T = 6, two (pair, group)s a lane in w2
